@@ -1,0 +1,339 @@
+"""CPU oracle of the Wan2.1 DiT denoising step -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The product path (the HIP library and
+its Python binding) never calls it and shares no code with it.
+
+What it is: a plain, slow, obviously correct numpy implementation in float64
+of what one denoising step computes, written from the pages' description.
+Every function names the passage it follows.  Page tags used below:
+
+  [Note]  "Wan: Open and Advanced Large-Scale Video Generative Models (Wan 2.1)"
+          (AI Research 技术调研 note).  Sections: 模型架构 / Wan-VAE,
+          模型架构 / Diffusion Transformer, 配置表（来自 HF model card）,
+          I2V 架构扩展, 训练方法, 关键消融.
+  [News]  "超越Sora！阿里正式完全开源最新、最强大的视频生成模型 Wan2.1"
+          (163.com).  Sections: 核心创新一 (3D VAE, feature cache),
+          核心创新二 (视频扩散 DiT), 核心创新四 (Image-to-Video).
+
+Where the pages leave a step open the plainest reading is taken; every such
+reading is listed in the module-level ``READINGS`` table and repeated where it
+is used.  Inputs arrive as float32 arrays (bf16-representable for bf16
+workloads) and are upcast to float64; nothing is rounded in between.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(closed forms, library routines, brute force, invariants).  The numeric value
+of a block or step with random weights has no worked example on the pages;
+it is pinned only through those parts.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+F64 = np.float64
+
+READINGS = {
+    "R1 t-MLP shape": "Linear(256->d), SiLU, Linear(d->6d); one MLP shared by all blocks "
+                      "[Note, Diffusion Transformer; News, 核心创新二]",
+    "R2 sinusoid": "w_k = 10000^(-k/128), k=0..127; e = [cos(t w) | sin(t w)] on raw t "
+                   "(the pages give only the width 256 [Note, 配置表])",
+    "R3 modulation order": "[shift1, scale1, gate1, shift2, scale2, gate2]; block i uses m + beta_i",
+    "R4 biases": "every Linear has a bias",
+    "R5 cross-attention": "pre-LayerNorm without affine and without modulation; ungated residual",
+    "R6 attention": "softmax(q k^T / sqrt(hd)) v; no mask, no positional term, no QK-norm",
+    "R7 GELU": "tanh approximation (FFN and image MLP)",
+    "R8 head": "plain Linear d -> 16*1*2*2, no final norm or modulation",
+    "R9 patch order": "token n = (f*Hp + i)*Wp + j; feature k = c*4 + a*2 + b; "
+                      "value latent[c, f, 2i+a, 2j+b] (Conv3d weight order)",
+    "R10 I2V mask": "frame mask of the video (1+T frames) -> repeat frame 0 four times -> "
+                    "[1+T/4, 4] -> 4 channels x (1+T/4) frames, broadcast over H/8 x W/8",
+    "R11 image MLP": "Linear(1280->d), GELU, Linear(d->d), GELU, Linear(d->d)",
+    "R12 decoupled CA": "two softmaxes (text / image), separate K,V weights, shared Q and "
+                        "out-projection, outputs summed with weight 1",
+    "R13 LayerNorm": "biased variance over d, eps inside the sqrt, no affine",
+}
+
+
+def _f(a) -> np.ndarray:
+    return np.asarray(a, dtype=F64)
+
+
+# ---------------------------------------------------------------------------
+# shapes  -- [Note, 模型架构 (Wan-VAE: latent (1+T/4) x H/8 x W/8, 16 ch) and
+#            Diffusion Transformer: (1,2,2) patchify, L = (1+T/4) * H/16 * W/16]
+
+def latent_shape(frames: int, height: int, width: int):
+    """Video of ``frames`` = 1+T frames at H x W -> latent [16, 1+T/4, H/8, W/8]."""
+    T = frames - 1
+    if T % 4 or height % 8 or width % 8:
+        raise ValueError("video shape not compatible with the 4x8x8 compression")
+    return (16, 1 + T // 4, height // 8, width // 8)
+
+
+def seq_len(frames: int, height: int, width: int) -> int:
+    """L = (1+T/4) * H/16 * W/16 for a video of 1+T frames at H x W."""
+    T = frames - 1
+    if T % 4 or height % 16 or width % 16:
+        raise ValueError("video shape not compatible with 4x8x8 VAE + (1,2,2) patch")
+    return (1 + T // 4) * (height // 16) * (width // 16)
+
+
+# ---------------------------------------------------------------------------
+# elementwise pieces
+
+def silu(z):
+    """SiLU(z) = z * sigmoid(z).  [Note, Diffusion Transformer: Linear+SiLU]"""
+    z = _f(z)
+    return z / (1.0 + np.exp(-z))
+
+
+def gelu_tanh(u):
+    """GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).  (R7)"""
+    u = _f(u)
+    return 0.5 * u * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))
+
+
+def linear(x, w, b):
+    """y = x W^T + b with W stored [out, in].  (R4)"""
+    return _f(x) @ _f(w).T + _f(b)
+
+
+def layer_norm(x, eps: float = 1e-6):
+    """(x - mean) / sqrt(var + eps) over the last axis, biased variance, no affine (R13)."""
+    x = _f(x)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def modulate(xhat, shift, scale):
+    """AdaLN modulation x * (1 + scale) + shift.
+    [Note, Diffusion Transformer: shared AdaLN predicts the modulation]"""
+    return _f(xhat) * (1.0 + _f(scale)) + _f(shift)
+
+
+# ---------------------------------------------------------------------------
+# timestep embedding and the shared AdaLN MLP
+# [Note, Diffusion Transformer; News, 核心创新二: one Linear+SiLU MLP on the time
+#  embedding predicts six modulation parameters, shared by every block, each
+#  block learning its own biases; Note, 配置表: frequency dimension 256]
+
+def sinusoid(t, freq_dim: int = 256):
+    """e(t) = [cos(t w_0..w_{h-1}) | sin(t w_0..w_{h-1})], w_k = 10000^(-k/h), h = freq_dim/2 (R2)."""
+    t = _f(t).reshape(-1)
+    half = freq_dim // 2
+    k = np.arange(half, dtype=F64)
+    w = np.exp(-math.log(10000.0) * k / half)
+    arg = t[:, None] * w[None, :]
+    return np.concatenate([np.cos(arg), np.sin(arg)], axis=1)
+
+
+def tmlp(t, w1, b1, w2, b2, freq_dim: int = 256):
+    """m = W2 SiLU(W1 e(t) + b1) + b2  -> [B, 6d]  (R1)."""
+    e = sinusoid(t, freq_dim)
+    return linear(silu(linear(e, w1, b1)), w2, b2)
+
+
+def block_modulation(m, beta):
+    """m_i = m + beta_i, split into the six [B, d] vectors (R3)."""
+    mi = _f(m) + _f(beta)[None, :]
+    d = mi.shape[1] // 6
+    names = ("shift1", "scale1", "gate1", "shift2", "scale2", "gate2")
+    return {n: mi[:, j * d:(j + 1) * d] for j, n in enumerate(names)}
+
+
+# ---------------------------------------------------------------------------
+# attention  (R6)  [Note, Diffusion Transformer: full spatio-temporal attention;
+#                   text injected through cross-attention in every block]
+
+def attention(q, k, v, chunk: int = 1024):
+    """softmax(q k^T / sqrt(hd)) v for one head.  q [Lq, hd], k/v [Lk, hd].
+    The softmax is materialised one query chunk at a time (rows are
+    independent), with the row maximum subtracted before exp."""
+    q, k, v = _f(q), _f(k), _f(v)
+    hd = q.shape[1]
+    out = np.empty((q.shape[0], v.shape[1]), dtype=F64)
+    scale = 1.0 / math.sqrt(hd)
+    for s in range(0, q.shape[0], chunk):
+        S = (q[s:s + chunk] @ k.T) * scale
+        S -= S.max(axis=1, keepdims=True)
+        P = np.exp(S)
+        P /= P.sum(axis=1, keepdims=True)
+        out[s:s + chunk] = P @ v
+    return out
+
+
+def multihead(q, k, v, heads: int):
+    """Split the feature axis into ``heads`` equal heads (head h = columns
+    h*hd .. (h+1)*hd), attend per head, concatenate."""
+    hd = q.shape[1] // heads
+    return np.concatenate([attention(q[:, h * hd:(h + 1) * hd], k[:, h * hd:(h + 1) * hd],
+                                     v[:, h * hd:(h + 1) * hd]) for h in range(heads)], axis=1)
+
+
+def self_attention(hmod, wqkv, bqkv, wo, bo, heads: int, rows: Optional[np.ndarray] = None):
+    """Self-attention of one sample: qkv = h Wqkv^T + b (q | k | v blocks of d
+    rows in Wqkv), o = MHA(q, k, v), y = o Wo^T + bo.  ``rows`` restricts the
+    query side (and the returned rows) to a subset of tokens; keys and values
+    always cover all tokens."""
+    hmod = _f(hmod)
+    d = hmod.shape[1]
+    wqkv, bqkv = _f(wqkv), _f(bqkv)
+    k = linear(hmod, wqkv[d:2 * d], bqkv[d:2 * d])
+    v = linear(hmod, wqkv[2 * d:], bqkv[2 * d:])
+    hq = hmod if rows is None else hmod[rows]
+    q = linear(hq, wqkv[:d], bqkv[:d])
+    o = multihead(q, k, v, heads)
+    return linear(o, wo, bo)
+
+
+def cross_attention(xq, ctx, wq, bq, wkv, bkv, wo, bo, heads: int, eps: float = 1e-6,
+                    img=None, wkv_img=None, bkv_img=None):
+    """Cross-attention of one sample (R5, R12): q from LayerNorm(x) without
+    modulation, keys/values from the text context; with ``img`` a second,
+    separately normalised attention over the image tokens is added before the
+    shared out-projection.  [News, 核心创新二; Note, I2V 架构扩展: decoupled
+    cross-attention in the manner of IP-Adapter]"""
+    d = ctx.shape[1]
+    q = linear(layer_norm(xq, eps), wq, bq)
+    wkv, bkv = _f(wkv), _f(bkv)
+    kt = linear(ctx, wkv[:d], bkv[:d])
+    vt = linear(ctx, wkv[d:], bkv[d:])
+    o = multihead(q, kt, vt, heads)
+    if img is not None:
+        wkv_img, bkv_img = _f(wkv_img), _f(bkv_img)
+        ki = linear(img, wkv_img[:d], bkv_img[:d])
+        vi = linear(img, wkv_img[d:], bkv_img[d:])
+        o = o + multihead(q, ki, vi, heads)
+    return linear(o, wo, bo)
+
+
+def ffn(hmod, w1, b1, w2, b2):
+    """z = GELU_tanh(h W1^T + b1) W2^T + b2.  [Note, 配置表: FFN dimension]"""
+    return linear(gelu_tanh(linear(hmod, w1, b1)), w2, b2)
+
+
+# ---------------------------------------------------------------------------
+# one DiT block
+
+def block(x, m, wts: Dict[str, np.ndarray], ctx, heads: int, eps: float = 1e-6,
+          img=None, rows: Optional[np.ndarray] = None, return_parts: bool = False):
+    """One block for a batch.  x [B, L, d]; m [B, 6d] (shared t-MLP output);
+    ctx [B, Lc, d]; img [B, Li, d] or None.
+
+      x1 = x  + gate1 * SA(LN(x) (1+scale1) + shift1)
+      x2 = x1 + CA(LN(x1), ctx [, img])
+      x3 = x2 + gate2 * FFN(LN(x2) (1+scale2) + shift2)
+
+    [News, 核心创新二 and Note, Diffusion Transformer: shared AdaLN, full
+    self-attention, text cross-attention in every block; readings R3, R5.]
+    With ``rows`` only those token rows of the output are computed (self-
+    attention still reads all tokens' keys and values)."""
+    x = _f(x)
+    mod = block_modulation(m, wts["mod_bias"])
+    outs, parts = [], []
+    for b in range(x.shape[0]):
+        xb = x[b]
+        h1 = modulate(layer_norm(xb, eps), mod["shift1"][b], mod["scale1"][b])
+        sa = self_attention(h1, wts["sa_wqkv"], wts["sa_bqkv"], wts["sa_wo"], wts["sa_bo"],
+                            heads, rows=rows)
+        xr = xb if rows is None else xb[rows]
+        x1 = xr + mod["gate1"][b] * sa
+        ca = cross_attention(x1, _f(ctx[b]), wts["ca_wq"], wts["ca_bq"], wts["ca_wkv"],
+                             wts["ca_bkv"], wts["ca_wo"], wts["ca_bo"], heads, eps,
+                             img=None if img is None else _f(img[b]),
+                             wkv_img=wts.get("ca_wkv_img"), bkv_img=wts.get("ca_bkv_img"))
+        x2 = x1 + ca
+        h2 = modulate(layer_norm(x2, eps), mod["shift2"][b], mod["scale2"][b])
+        z = ffn(h2, wts["ffn_w1"], wts["ffn_b1"], wts["ffn_w2"], wts["ffn_b2"])
+        x3 = x2 + mod["gate2"][b] * z
+        outs.append(x3)
+        parts.append({"sa": sa, "ca": ca, "ffn": z})
+    out = np.stack(outs)
+    return (out, parts) if return_parts else out
+
+
+# ---------------------------------------------------------------------------
+# patchify / unpatchify  [Note, Diffusion Transformer: (1,2,2) 3D convolution;
+#                         Note, 配置表: in/out latent dimension 16]  (R9)
+
+def patch_gather(latent):
+    """latent [C, F, H8, W8] -> P [L, 4C] with P[(f*Hp+i)*Wp+j, c*4+a*2+b] =
+    latent[c, f, 2i+a, 2j+b]."""
+    lat = _f(latent)
+    C, F, H8, W8 = lat.shape
+    Hp, Wp = H8 // 2, W8 // 2
+    # [C, F, Hp, 2, Wp, 2] -> [F, Hp, Wp, C, 2, 2]
+    r = lat.reshape(C, F, Hp, 2, Wp, 2).transpose(1, 2, 4, 0, 3, 5)
+    return r.reshape(F * Hp * Wp, C * 4)
+
+
+def patchify(latent, w, b):
+    """Conv3d with kernel = stride = (1,2,2) as gather + matmul: x0 = P W^T + b.
+    latent [B, C, F, H8, W8]; w [d, 4C] (Conv3d weight [d, C, 1, 2, 2] flattened)."""
+    return np.stack([linear(patch_gather(latent[s]), w, b) for s in range(latent.shape[0])])
+
+
+def unpatch_scatter(o, F: int, Hp: int, Wp: int, C: int = 16):
+    """Inverse of patch_gather: o [L, 4C] -> [C, F, 2Hp, 2Wp]."""
+    o = _f(o)
+    r = o.reshape(F, Hp, Wp, C, 2, 2).transpose(3, 0, 1, 4, 2, 5)
+    return r.reshape(C, F, 2 * Hp, 2 * Wp)
+
+
+def head_unpatchify(x, w, b, F: int, Hp: int, Wp: int, C: int = 16):
+    """Head Linear d -> 4C (R8) then unpatchify.  x [B, L, d] -> [B, C, F, H8, W8]."""
+    return np.stack([unpatch_scatter(linear(x[i], w, b), F, Hp, Wp, C) for i in range(x.shape[0])])
+
+
+# ---------------------------------------------------------------------------
+# I2V inputs  [News, 核心创新四; Note, I2V 架构扩展]
+
+def i2v_mask(frame_mask: Sequence[int], lat_f: int, H8: int, W8: int):
+    """Binary mask over the 1+T video frames (1 = keep, 0 = generate) -> the 4
+    mask channels [4, 1+T/4, H8, W8] (R10).  Frame 0 is repeated to make 4T/4+4
+    values, grouped by 4 along time (the VAE's temporal stride), and the group
+    member index becomes the channel."""
+    fm = np.asarray(frame_mask, dtype=F64).reshape(-1)
+    T = fm.shape[0] - 1
+    if T % 4 or 1 + T // 4 != lat_f:
+        raise ValueError("frame mask length does not match the latent frames")
+    ext = np.concatenate([np.repeat(fm[:1], 4), fm[1:]])        # 4 + T values
+    grp = ext.reshape(lat_f, 4).T                               # [4, lat_f]
+    return np.broadcast_to(grp[:, :, None, None], (4, lat_f, H8, W8)).copy()
+
+
+def image_context(clip, w1, b1, w2, b2, w3, b3):
+    """Three-layer MLP from CLIP features to the model width (R11)."""
+    return linear(gelu_tanh(linear(gelu_tanh(linear(clip, w1, b1)), w2, b2)), w3, b3)
+
+
+# ---------------------------------------------------------------------------
+# one denoising step
+
+def step(latent, t, ctx, mw: Dict[str, object], heads: int, eps: float = 1e-6,
+         clip=None, blocks: Optional[List[Dict[str, np.ndarray]]] = None,
+         return_hidden: bool = False):
+    """patchify -> shared t-MLP -> N blocks -> head -> unpatchify.
+    latent [B, Cin, F, H8, W8]; t [B]; ctx [B, Lc, d]; clip [B, Li, 1280] or None.
+    Returns the predicted velocity [B, 16, F, H8, W8] (the flow-matching
+    target of [Note, 训练方法]).  ``blocks`` may be an iterable that yields the
+    block weights one at a time (to bound host memory)."""
+    lat = _f(latent)
+    B, Cin, F, H8, W8 = lat.shape
+    Hp, Wp = H8 // 2, W8 // 2
+    x = patchify(lat, mw["patch_w"], mw["patch_b"])
+    tw = mw["tmlp"]
+    m = tmlp(t, tw["w1"], tw["b1"], tw["w2"], tw["b2"])
+    img = None
+    if clip is not None:
+        iw = mw["img"]
+        img = np.stack([image_context(clip[b], iw["w1"], iw["b1"], iw["w2"], iw["b2"],
+                                      iw["w3"], iw["b3"]) for b in range(B)])
+    for wts in (blocks if blocks is not None else mw["blocks"]):
+        x = block(x, m, wts, ctx, heads, eps, img=img)
+    out = head_unpatchify(x, mw["head_w"], mw["head_b"], F, Hp, Wp, 16)
+    return (out, x) if return_hidden else out

@@ -1,0 +1,395 @@
+"""Pins of the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` takes the oracle module ``O`` and raises AssertionError when
+the oracle disagrees with a closed form, a library routine (torch CPU), a
+brute-force loop on tiny inputs, or an invariant the method must satisfy.
+``tests/test_oracle_pins.py`` runs them on the real oracle;
+``tests/test_oracle_mutations.py`` runs them on oracles with planted mistakes
+and requires that at least one pin fails for each mistake.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as TF
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, tol, what):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+def _t(a):
+    return torch.from_numpy(np.asarray(a, np.float64))
+
+
+# ---------------------------------------------------------------- shapes
+def pin_shapes(O):
+    """L and latent shapes of the pages' workloads (tests/golden/shapes.json)."""
+    with open(os.path.join(GOLDEN, "shapes.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        fr, h, w = case["frames"], case["height"], case["width"]
+        assert O.seq_len(fr, h, w) == case["L"], case
+        assert tuple(O.latent_shape(fr, h, w)) == tuple(case["latent"]), case
+    # 5 s at 16 fps is 80 frame intervals: 1 + T = 81 frames
+    assert 1 + 5 * 16 == g["frames_5s_16fps"]
+
+
+# ---------------------------------------------------------------- elementwise
+def pin_silu_gelu(O):
+    z = np.linspace(-8, 8, 97)
+    _close(O.silu(z), TF.silu(_t(z)).numpy(), 1e-13, "silu vs torch")
+    _close(O.gelu_tanh(z), TF.gelu(_t(z), approximate="tanh").numpy(), 1e-13, "gelu vs torch")
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    _close(O.gelu_tanh(np.array([30.0])), [30.0], 1e-12, "gelu large")
+
+
+def pin_layer_norm(O):
+    x = _rng(1).normal(size=(7, 33)) * 3 + 5
+    _close(O.layer_norm(x, 1e-6), TF.layer_norm(_t(x), (33,), eps=1e-6).numpy(), 1e-12,
+           "layer_norm vs torch")
+    _close(O.layer_norm(x + 17.0, 1e-6), O.layer_norm(x, 1e-6), 1e-9, "LN shift invariance")
+    c = np.full((2, 16), 3.25)
+    assert np.all(O.layer_norm(c, 1e-6) == 0.0), "LN of a constant row"
+    # eps enters inside the sqrt: row (-1, 1) has var 1 -> x/sqrt(1+eps)
+    _close(O.layer_norm(np.array([[-1.0, 1.0]]), 0.5), [[-1 / math.sqrt(1.5), 1 / math.sqrt(1.5)]],
+           1e-15, "LN eps placement")
+
+
+def pin_modulate(O):
+    x = _rng(2).normal(size=(5, 8))
+    sh, sc = _rng(3).normal(size=8), _rng(4).normal(size=8)
+    assert np.array_equal(O.modulate(x, np.zeros(8), np.zeros(8)), x)
+    _close(O.modulate(x, sh, np.full(8, -1.0)), np.broadcast_to(sh, x.shape), 0, "scale=-1 -> shift")
+    _close(O.modulate(np.ones((1, 8)), sh, sc), (1 + sc + sh)[None], 1e-15, "x=1")
+
+
+# ---------------------------------------------------------------- timestep
+def pin_sinusoid(O):
+    e0 = O.sinusoid(np.array([0.0]), 256)
+    assert e0.shape == (1, 256)
+    assert np.all(e0[0, :128] == 1.0) and np.all(e0[0, 128:] == 0.0), "t = 0"
+    t = np.array([0.5, 3.0, 999.0])
+    e = O.sinusoid(t, 256)
+    _close(e[:, :128] ** 2 + e[:, 128:] ** 2, np.ones((3, 128)), 1e-12, "cos^2+sin^2")
+    # w_0 = 1, w_64 = 10000^(-1/2) = 0.01, w_127 = 10000^(-127/128)
+    _close(e[:, 0], np.cos(t), 1e-14, "w_0")
+    _close(e[:, 128], np.sin(t), 1e-14, "sin w_0")
+    _close(e[:, 64], np.cos(0.01 * t), 1e-12, "w_64")
+    _close(e[:, 128 + 127], np.sin(t * 10000.0 ** (-127 / 128)), 1e-12, "w_127")
+
+
+def pin_tmlp(O):
+    r = _rng(5)
+    d = 6
+    w1, b1 = r.normal(size=(d, 256)) * 0.1, r.normal(size=d)
+    w2, b2 = r.normal(size=(6 * d, d)), r.normal(size=6 * d)
+    t = np.array([0.0, 412.5])
+    m = O.tmlp(t, w1, b1, np.zeros_like(w2), b2)
+    assert np.array_equal(m, np.broadcast_to(b2, (2, 6 * d))), "W2 = 0 -> m = b2"
+    # W1 = 0 -> hidden = SiLU(b1) for every t; SiLU(b) = b / (1 + e^-b)
+    m0 = O.tmlp(t, np.zeros_like(w1), b1, w2, b2)
+    h = np.array([bb / (1 + math.exp(-bb)) for bb in b1])
+    _close(m0, np.broadcast_to(w2 @ h + b2, (2, 6 * d)), 1e-12, "W1 = 0")
+    # t = 0: the embedding is [1]*128 | [0]*128, so the first layer sums the cos-half columns
+    z = w1[:, :128].sum(axis=1) + b1
+    h = z / (1 + np.exp(-z))
+    _close(O.tmlp(np.array([0.0]), w1, b1, w2, b2)[0], w2 @ h + b2, 1e-12, "t = 0 closed form")
+    # torch composition (library Linear + SiLU)
+    tt = torch.tensor([412.5], dtype=torch.float64)
+    e = _t(O.sinusoid(np.array([412.5])))
+    ref = TF.linear(TF.silu(TF.linear(e, _t(w1), _t(b1))), _t(w2), _t(b2)).numpy()
+    _close(O.tmlp(tt.numpy(), w1, b1, w2, b2), ref, 1e-12, "tmlp vs torch")
+    # block modulation: beta adds, order shift1, scale1, gate1, shift2, scale2, gate2
+    beta = np.arange(6 * d, dtype=np.float64)
+    mm = O.block_modulation(np.zeros((1, 6 * d)), beta)
+    for j, n in enumerate(("shift1", "scale1", "gate1", "shift2", "scale2", "gate2")):
+        assert np.array_equal(mm[n][0], beta[j * d:(j + 1) * d]), n
+
+
+# ---------------------------------------------------------------- attention
+def _brute_attention(q, k, v):
+    """Triple loop, fp64 Python floats."""
+    Lq, hd = q.shape
+    Lk = k.shape[0]
+    out = np.zeros((Lq, v.shape[1]))
+    for i in range(Lq):
+        s = [sum(q[i, c] * k[j, c] for c in range(hd)) / math.sqrt(hd) for j in range(Lk)]
+        mx = max(s)
+        p = [math.exp(x - mx) for x in s]
+        tot = sum(p)
+        for c in range(v.shape[1]):
+            out[i, c] = sum(p[j] * v[j, c] for j in range(Lk)) / tot
+    return out
+
+
+def pin_attention(O):
+    r = _rng(6)
+    for Lq, Lk, hd in ((5, 7, 4), (9, 3, 8), (1, 1, 4), (6, 11, 16)):
+        q, k, v = r.normal(size=(Lq, hd)) * 2, r.normal(size=(Lk, hd)) * 2, r.normal(size=(Lk, hd))
+        _close(O.attention(q, k, v), _brute_attention(q, k, v), 1e-12, f"brute {Lq}x{Lk}x{hd}")
+    q, k, v = r.normal(size=(40, 16)), r.normal(size=(70, 16)), r.normal(size=(70, 16))
+    ref = TF.scaled_dot_product_attention(_t(q)[None], _t(k)[None], _t(v)[None])[0].numpy()
+    _close(O.attention(q, k, v), ref, 1e-12, "attention vs torch sdpa")
+    # rows of the softmax sum to one: V = 1 -> O = 1
+    _close(O.attention(q * 8, k, np.ones((70, 16))), np.ones((40, 16)), 1e-12, "V = 1")
+    # equal keys -> uniform weights -> mean of V
+    kk = np.repeat(r.normal(size=(1, 16)), 70, axis=0)
+    _close(O.attention(q, kk, v), np.broadcast_to(v.mean(axis=0), (40, 16)), 1e-12, "equal keys")
+    # one dominant key -> its value row
+    kd = np.zeros((70, 16)); kd[13] = 200.0
+    qd = np.ones((3, 16))
+    _close(O.attention(qd, kd, v), np.broadcast_to(v[13], (3, 16)), 1e-12, "dominant key")
+    # L = 1 -> O = V
+    _close(O.attention(q[:4], k[:1], v[:1]), np.broadcast_to(v[0], (4, 16)), 1e-14, "Lk = 1")
+    # permutation equivariance of self-attention (no positional term)
+    x = r.normal(size=(30, 16))
+    perm = r.permutation(30)
+    _close(O.attention(x[perm], x[perm], x[perm]), O.attention(x, x, x)[perm], 1e-12,
+           "permutation equivariance")
+    # chunking is invisible
+    _close(O.attention(q, k, v, chunk=7), O.attention(q, k, v, chunk=1024), 1e-13, "chunking")
+
+
+def _torch_mha(x_q, x_kv, w_in, b_in, wo, bo, heads):
+    d = x_q.shape[1]
+    mha = torch.nn.MultiheadAttention(d, heads, bias=True, batch_first=True, dtype=torch.float64)
+    with torch.no_grad():
+        mha.in_proj_weight.copy_(_t(w_in)); mha.in_proj_bias.copy_(_t(b_in))
+        mha.out_proj.weight.copy_(_t(wo)); mha.out_proj.bias.copy_(_t(bo))
+        y, _ = mha(_t(x_q)[None], _t(x_kv)[None], _t(x_kv)[None], need_weights=False)
+    return y[0].numpy()
+
+
+def pin_self_attention(O):
+    r = _rng(7)
+    L, d, H = 12, 16, 2
+    h = r.normal(size=(L, d))
+    wqkv, bqkv = r.normal(size=(3 * d, d)) * 0.5, r.normal(size=3 * d)
+    wo, bo = r.normal(size=(d, d)) * 0.5, r.normal(size=d)
+    ref = _torch_mha(h, h, wqkv, bqkv, wo, bo, H)
+    _close(O.self_attention(h, wqkv, bqkv, wo, bo, H), ref, 1e-11, "SA vs torch MHA")
+    rows = np.array([0, 5, 11])
+    _close(O.self_attention(h, wqkv, bqkv, wo, bo, H, rows=rows), ref[rows], 1e-11, "SA rows")
+
+
+def pin_cross_attention(O):
+    r = _rng(8)
+    L, Lc, Li, d, H = 10, 6, 4, 16, 4
+    x, ctx, img = r.normal(size=(L, d)) * 2 + 1, r.normal(size=(Lc, d)), r.normal(size=(Li, d))
+    wq, bq = r.normal(size=(d, d)) * 0.5, r.normal(size=d)
+    wkv, bkv = r.normal(size=(2 * d, d)) * 0.5, r.normal(size=2 * d)
+    wki, bki = r.normal(size=(2 * d, d)) * 0.5, r.normal(size=2 * d)
+    wo, bo = r.normal(size=(d, d)) * 0.5, r.normal(size=d)
+    xn = TF.layer_norm(_t(x), (d,), eps=1e-6).numpy()
+    ref_t = _torch_mha(xn, ctx, np.concatenate([wq, wkv]), np.concatenate([bq, bkv]), wo, bo, H)
+    _close(O.cross_attention(x, ctx, wq, bq, wkv, bkv, wo, bo, H), ref_t, 1e-11, "CA vs torch MHA")
+    # decoupled: text part + image part share Q and the out-projection; the
+    # out-projection is affine, so CA2 = CA_text + CA_img - bo
+    ref_i = _torch_mha(xn, img, np.concatenate([wq, wki]), np.concatenate([bq, bki]), wo, bo, H)
+    got = O.cross_attention(x, ctx, wq, bq, wkv, bkv, wo, bo, H, img=img, wkv_img=wki, bkv_img=bki)
+    _close(got, ref_t + ref_i - bo, 1e-11, "decoupled CA")
+
+
+def pin_ffn(O):
+    r = _rng(9)
+    h = r.normal(size=(7, 8))
+    w1, b1, w2, b2 = r.normal(size=(20, 8)), r.normal(size=20), r.normal(size=(8, 20)), r.normal(size=8)
+    lin1 = torch.nn.Linear(8, 20, dtype=torch.float64)
+    lin2 = torch.nn.Linear(20, 8, dtype=torch.float64)
+    with torch.no_grad():
+        lin1.weight.copy_(_t(w1)); lin1.bias.copy_(_t(b1)); lin2.weight.copy_(_t(w2)); lin2.bias.copy_(_t(b2))
+        ref = lin2(TF.gelu(lin1(_t(h)), approximate="tanh")).numpy()
+    _close(O.ffn(h, w1, b1, w2, b2), ref, 1e-11, "FFN vs torch")
+
+
+# ---------------------------------------------------------------- block
+def _tiny_block_weights(r, d, F, img=False, scale=0.3):
+    w = {
+        "sa_wqkv": r.normal(size=(3 * d, d)) * scale, "sa_bqkv": r.normal(size=3 * d) * scale,
+        "sa_wo": r.normal(size=(d, d)) * scale, "sa_bo": r.normal(size=d) * scale,
+        "ca_wq": r.normal(size=(d, d)) * scale, "ca_bq": r.normal(size=d) * scale,
+        "ca_wkv": r.normal(size=(2 * d, d)) * scale, "ca_bkv": r.normal(size=2 * d) * scale,
+        "ca_wo": r.normal(size=(d, d)) * scale, "ca_bo": r.normal(size=d) * scale,
+        "ffn_w1": r.normal(size=(F, d)) * scale, "ffn_b1": r.normal(size=F) * scale,
+        "ffn_w2": r.normal(size=(d, F)) * scale, "ffn_b2": r.normal(size=d) * scale,
+        "mod_bias": r.normal(size=6 * d) * scale,
+    }
+    if img:
+        w["ca_wkv_img"] = r.normal(size=(2 * d, d)) * scale
+        w["ca_bkv_img"] = r.normal(size=2 * d) * scale
+    return w
+
+
+def pin_block(O):
+    r = _rng(10)
+    B, L, Lc, d, F, H = 2, 9, 5, 16, 24, 2
+    x = r.normal(size=(B, L, d))
+    ctx = r.normal(size=(B, Lc, d))
+    m = r.normal(size=(B, 6 * d))
+    w = _tiny_block_weights(r, d, F)
+    y = O.block(x, m, w, ctx, H)
+    # gates zero and cross-attention out-projection zero -> identity (bitwise)
+    mz = m.copy()
+    wz = dict(w)
+    mz[:, 2 * d:3 * d] = -w["mod_bias"][2 * d:3 * d]
+    mz[:, 5 * d:6 * d] = -w["mod_bias"][5 * d:6 * d]
+    wz["ca_wo"] = np.zeros_like(w["ca_wo"]); wz["ca_bo"] = np.zeros_like(w["ca_bo"])
+    assert np.array_equal(O.block(x, mz, wz, ctx, H), x), "zero gates + zero CA-out -> identity"
+    # gates zero alone -> x + CA(LN(x), ctx) (ungated cross-attention)
+    yz = O.block(x, mz, w, ctx, H)
+    for b in range(B):
+        ca = O.cross_attention(x[b], ctx[b], w["ca_wq"], w["ca_bq"], w["ca_wkv"], w["ca_bkv"],
+                               w["ca_wo"], w["ca_bo"], H)
+        _close(yz[b], x[b] + ca, 1e-12, "zero gates -> x + CA")
+    # batch independence
+    _close(O.block(x[1:], m[1:], w, ctx[1:], H)[0], y[1], 1e-12, "batch independence")
+    # token permutation equivariance of the whole block
+    perm = r.permutation(L)
+    _close(O.block(x[:, perm], m, w, ctx, H), y[:, perm], 1e-11, "block permutation equivariance")
+    # rows subset
+    rows = np.array([1, 4, 8])
+    _close(O.block(x, m, w, ctx, H, rows=rows), y[:, rows], 1e-12, "block rows")
+    # composition from torch library pieces
+    for b in range(B):
+        mb = _t(m[b] + w["mod_bias"]).reshape(6, d)
+        xb = _t(x[b])
+        lin = lambda a, W, bb: TF.linear(a, _t(W), _t(bb))
+        h1 = TF.layer_norm(xb, (d,), eps=1e-6) * (1 + mb[1]) + mb[0]
+        sa = _t(_torch_mha(h1.numpy(), h1.numpy(), w["sa_wqkv"], w["sa_bqkv"], w["sa_wo"], w["sa_bo"], H))
+        x1 = xb + mb[2] * sa
+        xn = TF.layer_norm(x1, (d,), eps=1e-6).numpy()
+        ca = _t(_torch_mha(xn, ctx[b], np.concatenate([w["ca_wq"], w["ca_wkv"]]),
+                           np.concatenate([w["ca_bq"], w["ca_bkv"]]), w["ca_wo"], w["ca_bo"], H))
+        x2 = x1 + ca
+        h2 = TF.layer_norm(x2, (d,), eps=1e-6) * (1 + mb[4]) + mb[3]
+        z = lin(TF.gelu(lin(h2, w["ffn_w1"], w["ffn_b1"]), approximate="tanh"), w["ffn_w2"], w["ffn_b2"])
+        _close(y[b], (x2 + mb[5] * z).numpy(), 1e-10, "block vs torch composition")
+
+
+# ---------------------------------------------------------------- patchify
+def _brute_conv3d_122(lat, w, b):
+    """Direct loops: Conv3d, kernel = stride = (1,2,2), weight [d, C, 1, 2, 2]."""
+    C, Fr, H8, W8 = lat.shape
+    d = w.shape[0]
+    w5 = w.reshape(d, C, 1, 2, 2)
+    out = np.zeros((d, Fr, H8 // 2, W8 // 2))
+    for o in range(d):
+        for f in range(Fr):
+            for i in range(H8 // 2):
+                for j in range(W8 // 2):
+                    s = b[o]
+                    for c in range(C):
+                        for a in range(2):
+                            for bb in range(2):
+                                s += w5[o, c, 0, a, bb] * lat[c, f, 2 * i + a, 2 * j + bb]
+                    out[o, f, i, j] = s
+    return out
+
+
+def pin_patchify(O):
+    r = _rng(11)
+    C, Fr, H8, W8, d = 3, 2, 4, 6, 5
+    lat = r.normal(size=(1, C, Fr, H8, W8))
+    w, b = r.normal(size=(d, C * 4)), r.normal(size=d)
+    x = O.patchify(lat, w, b)[0]                            # [L, d]
+    ref = _brute_conv3d_122(lat[0], w, b)                    # [d, F, Hp, Wp]
+    _close(x, ref.reshape(d, -1).T, 1e-12, "patchify vs brute conv3d (token order f,i,j)")
+    lib = TF.conv3d(_t(lat), _t(w.reshape(d, C, 1, 2, 2)), _t(b), stride=(1, 2, 2))[0].numpy()
+    _close(x, lib.reshape(d, -1).T, 1e-12, "patchify vs torch conv3d")
+    # unpatchify is the transposed convolution with the same kernel layout
+    o = r.normal(size=(1, x.shape[0], 4 * C))
+    wh, bh = r.normal(size=(4 * C, d)), r.normal(size=4 * C)
+    y = O.head_unpatchify(x[None], wh, bh, Fr, H8 // 2, W8 // 2, C)[0]
+    hx = x @ wh.T + bh                                       # [L, 4C]
+    # conv_transpose3d input [1, 4C -> treat head output channels as C*(1*2*2) groups]
+    inp = _t(hx.T.reshape(1, 4 * C, Fr, H8 // 2, W8 // 2))
+    # a per-channel scatter: weight [in=4C, out=C, 1, 2, 2] with one-hot placement
+    wt = torch.zeros(4 * C, C, 1, 2, 2, dtype=torch.float64)
+    for c in range(C):
+        for a in range(2):
+            for bb in range(2):
+                wt[c * 4 + a * 2 + bb, c, 0, a, bb] = 1.0
+    lib = TF.conv_transpose3d(inp, wt, stride=(1, 2, 2))[0].numpy()
+    _close(y, lib, 0, "unpatchify vs torch conv_transpose3d scatter")
+    # identity weights -> exact round trip of the latent
+    C16 = 16
+    lat16 = r.normal(size=(2, C16, 2, 4, 6)).astype(np.float32).astype(np.float64)
+    dd = 64
+    x16 = O.patchify(lat16, np.eye(dd), np.zeros(dd))
+    back = O.head_unpatchify(x16, np.eye(dd), np.zeros(dd), 2, 2, 3, C16)
+    assert np.array_equal(back, lat16), "identity round trip"
+    # I2V: the 20 extra channels with a zero projection leave the noise channels' tokens
+    w36 = np.zeros((d, 36 * 4)); w36[:, :64] = r.normal(size=(d, 64))
+    lat36 = r.normal(size=(1, 36, 2, 4, 6))
+    assert np.array_equal(O.patchify(lat36, w36, b), O.patchify(lat36[:, :16], w36[:, :64], b)), \
+        "zero extra projection"
+
+
+# ---------------------------------------------------------------- I2V
+def pin_i2v(O):
+    with open(os.path.join(GOLDEN, "i2v_mask.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        fm = np.zeros(case["frames"]); fm[case["ones"]] = 1
+        m = O.i2v_mask(fm, case["lat_f"], 3, 2)
+        assert m.shape == (4, case["lat_f"], 3, 2)
+        nz = sorted({(int(c), int(f)) for c, f, _, _ in zip(*np.nonzero(m))})
+        assert nz == [tuple(p) for p in case["nonzero_channel_frame"]], (case, nz)
+        assert set(np.unique(m)) <= {0.0, 1.0}
+    r = _rng(12)
+    d, H = 8, 2
+    clip = r.normal(size=(5, 12))
+    ws = [r.normal(size=s) for s in ((d, 12), (d,), (d, d), (d,), (d, d), (d,))]
+    seq = torch.nn.Sequential(torch.nn.Linear(12, d), torch.nn.GELU(approximate="tanh"),
+                              torch.nn.Linear(d, d), torch.nn.GELU(approximate="tanh"),
+                              torch.nn.Linear(d, d)).double()
+    with torch.no_grad():
+        for lin, (wi, bi) in zip((seq[0], seq[2], seq[4]), ((ws[0], ws[1]), (ws[2], ws[3]), (ws[4], ws[5]))):
+            lin.weight.copy_(_t(wi)); lin.bias.copy_(_t(bi))
+        ref = seq(_t(clip)).numpy()
+    _close(O.image_context(clip, *ws), ref, 1e-12, "image MLP vs torch")
+
+
+# ---------------------------------------------------------------- step
+def pin_step(O):
+    r = _rng(13)
+    B, d, H, F = 2, 64, 2, 32
+    Fr, H8, W8, Lc = 2, 4, 6, 3
+    lat = r.normal(size=(B, 16, Fr, H8, W8))
+    t = np.array([10.0, 700.0])
+    ctx = r.normal(size=(B, Lc, d))
+    mw = {"patch_w": np.eye(d), "patch_b": np.zeros(d), "head_w": np.eye(d), "head_b": np.zeros(d),
+          "tmlp": {"w1": r.normal(size=(d, 256)) * 0.1, "b1": r.normal(size=d),
+                   "w2": np.zeros((6 * d, d)), "b2": np.zeros(6 * d)}}
+    # every block an identity: gate biases 0 (m = 0 because W2 = 0, b2 = 0), CA out zero
+    blocks = []
+    for _ in range(3):
+        w = _tiny_block_weights(r, d, F)
+        w["mod_bias"][2 * d:3 * d] = 0; w["mod_bias"][5 * d:6 * d] = 0
+        w["ca_wo"] = np.zeros((d, d)); w["ca_bo"] = np.zeros(d)
+        blocks.append(w)
+    mw["blocks"] = blocks
+    assert np.array_equal(O.step(lat, t, ctx, mw, H), lat), "identity step"
+    # with real blocks: step == head(blocks(patchify)) composed by hand, and
+    # the batch entries are independent
+    for w in blocks:
+        w["mod_bias"] = r.normal(size=6 * d) * 0.3
+        w["ca_wo"] = r.normal(size=(d, d)) * 0.3
+    mw["tmlp"]["w2"] = r.normal(size=(6 * d, d)) * 0.1
+    out = O.step(lat, t, ctx, mw, H)
+    out1 = O.step(lat[1:], t[1:], ctx[1:], mw, H)
+    _close(out1[0], out[1], 1e-9, "step batch independence")

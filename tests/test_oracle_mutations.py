@@ -1,0 +1,65 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require
+that at least one pin catches each of them."""
+import importlib.util
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "wan_oracle.py")
+
+MUTATIONS = {
+    "no attention scale": ("scale = 1.0 / math.sqrt(hd)", "scale = 1.0"),
+    "k/v weights swapped": ("k = linear(hmod, wqkv[d:2 * d], bqkv[d:2 * d])",
+                            "k = linear(hmod, wqkv[2 * d:], bqkv[2 * d:])"),
+    "modulate sign": ("_f(xhat) * (1.0 + _f(scale))", "_f(xhat) * (1.0 - _f(scale))"),
+    "sin/cos order": ("[np.cos(arg), np.sin(arg)]", "[np.sin(arg), np.cos(arg)]"),
+    "unbiased variance": ("var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)",
+                          "var = ((x - mu) ** 2).sum(axis=-1, keepdims=True) / (x.shape[-1] - 1)"),
+    "eps outside sqrt": ("np.sqrt(var + eps)", "(np.sqrt(var) + eps)"),
+    "gelu constant": ("0.044715", "0.0447"),
+    "gated cross-attention": ("x2 = x1 + ca", "x2 = x1 + mod[\"gate1\"][b] * ca"),
+    "modulation order": ('names = ("shift1", "scale1"', 'names = ("scale1", "shift1"'),
+    "patch a/b swapped": ("transpose(1, 2, 4, 0, 3, 5)", "transpose(1, 2, 4, 0, 5, 3)"),
+    "unpatch a/b swapped": ("transpose(3, 0, 1, 4, 2, 5)", "transpose(3, 0, 1, 5, 2, 4)"),
+    "mask zero-pad reading": ("np.repeat(fm[:1], 4)", "np.concatenate([fm[:1], np.zeros(3)])"),
+    "softmax wrong axis": ("P /= P.sum(axis=1, keepdims=True)", "P /= P.sum(axis=0, keepdims=True)"),
+    "ungated FFN": ('x3 = x2 + mod["gate2"][b] * z', "x3 = x2 + z"),
+    "silu slope": ("z / (1.0 + np.exp(-z))", "z / (1.0 + np.exp(-2 * z))"),
+    "image V from K": ("o = o + multihead(q, ki, vi, heads)", "o = o + multihead(q, ki, ki, heads)"),
+    "image MLP missing GELU": ("linear(gelu_tanh(linear(gelu_tanh(linear(clip, w1, b1)), w2, b2)), w3, b3)",
+                               "linear(linear(gelu_tanh(linear(clip, w1, b1)), w2, b2), w3, b3)"),
+    "t-MLP without SiLU": ("linear(silu(linear(e, w1, b1)), w2, b2)", "linear(linear(e, w1, b1), w2, b2)"),
+    "block bias sign": ("_f(m) + _f(beta)[None, :]", "_f(m) - _f(beta)[None, :]"),
+    "sinusoid base": ("math.log(10000.0)", "math.log(1000.0)"),
+    "LN on modulated input for CA": ("q = linear(layer_norm(xq, eps), wq, bq)", "q = linear(xq, wq, bq)"),
+    "seq_len off by one": ("return (1 + T // 4) * (height // 16)", "return (T // 4) * (height // 16)"),
+    "head split strided": ("k[:, h * hd:(h + 1) * hd],\n                                     v[:, h * hd:(h + 1) * hd])",
+                           "k[:, h::heads],\n                                     v[:, h::heads])"),
+}
+
+
+def _mutant(name, old, new):
+    src = open(SRC, encoding="utf-8").read()
+    assert src.count(old) >= 1, f"mutation site not found: {name}"
+    src = src.replace(old, new)
+    mod = types.ModuleType("wan_oracle_mutant")
+    exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name):
+    old, new = MUTATIONS[name]
+    M = _mutant(name, old, new)
+    caught = []
+    for pname in dir(P):
+        if not pname.startswith("pin_"):
+            continue
+        try:
+            getattr(P, pname)(M)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append(f"{pname}: {type(e).__name__}")
+    assert caught, f"no pin caught the planted mistake '{name}'"
