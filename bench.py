@@ -1,0 +1,203 @@
+"""Benchmark of the Wan2.1 DiT hot path on one MI355X.
+
+Workload: the 1.3B-shaped DiT block at 480P (latent 21x60x104, L = 32760
+tokens, dim 1536, 12 heads of 128, FFN 8960, 512 text tokens), bf16 operands
+with fp32 accumulation, seeded synthetic weights N(0, 0.02) and activations
+N(0, 1).  One timed "step" is one pass of the hot path over that input: the
+shared timestep MLP (wan_tmlp_fwd) followed by one full block
+(wan_dit_block_fwd: LayerNorm+modulate, QKV GEMMs, flash self-attention,
+out-projection with gated residual, cross-attention, FFN with gated residual).
+Inputs are resident in HBM before timing starts; the block updates the
+residual stream in place, so successive timed steps chain blocks.
+
+Prints one JSON line (tokens/s of the block, attention roofline, CPU oracle
+baseline on a bounded sample).  ``--gpus`` above 1 is refused: this build
+runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+
+def block_flops(B, L, d, H, F, Lc, Li=0):
+    hd = d // H
+    M = B * L
+    gemm = 2 * M * d * (3 * d) + 2 * M * d * d + 2 * M * d * d + 2 * B * Lc * d * 2 * d \
+        + 2 * M * d * d + 2 * 2 * M * F * d
+    if Li:
+        gemm += 2 * B * Li * d * 2 * d
+    sa = 4 * B * H * L * L * hd
+    ca = 4 * B * H * L * (Lc + Li) * hd
+    return gemm, sa, ca
+
+
+def cpu_baseline(work, inp, tw, bw, budget_s: float = 25.0):
+    """The CPU oracle, as it stands, on a bounded sample of the same block:
+    oracle.block(..., rows=r) for two sample sizes r1 < r2 (every sampled run
+    still projects K/V for all L tokens); the full block's time is
+    extrapolated linearly in r to r = L and turned into tokens/s."""
+    import numpy as np
+    import oracle.wan_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    m = work.model
+    L = work.L
+    m_vec = O.tmlp(inp["t"], tw["w1"], tw["b1"], tw["w2"], tw["b2"])
+    rng = np.random.default_rng(0)
+    times = {}
+    for r in (128, 640):
+        rows = np.sort(rng.choice(L, size=r, replace=False))
+        t0 = time.perf_counter()
+        O.block(inp["x"], m_vec, bw, inp["ctx"], m.heads, m.eps, rows=rows)
+        times[r] = time.perf_counter() - t0
+    (r1, t1), (r2, t2) = sorted(times.items())
+    per_row = max((t2 - t1) / (r2 - r1), 1e-9)
+    fixed = max(t1 - per_row * r1, 0.0)
+    full = fixed + per_row * L
+    return {"value": work.batch * L / full, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"oracle.block on {r1} and {r2} sampled query rows of the same input "
+                      f"(K/V for all {L} tokens each time; {t1:.1f}s and {t2:.1f}s); full-block time "
+                      f"{full:.1f}s extrapolated linearly in the row count"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", type=int, default=2, help="block workload id (2: 1.3B, 4: 14B)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import video_diffusion_transformer_block_amd as W
+
+    work = synth.CONFIGS[args.config]
+    assert work.kind == "block"
+    m = work.model
+    B, L, d, H, F = work.batch, work.L, m.dim, m.heads, m.ffn
+    dev = "cuda"
+    cfg = W.make_cfg(dim=d, heads=H, ffn=F, n_blocks=1, text_len=m.text_len, eps=m.eps,
+                     dtype=m.dtype)
+
+    inp = synth.workload_inputs(work)
+    tw = synth.tmlp_weights(work)
+    bw = synth.block_weights(work, 0)
+
+    def up(a, dt):
+        t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+        return (t.to(torch.bfloat16) if dt == "bf16" else t).to(dev)
+
+    twd = {k: up(v, m.dtype) for k, v in tw.items()}
+    bwd = {k: up(v, "f32" if k == "mod_bias" else m.dtype) for k, v in bw.items()}
+    x = up(inp["x"], "f32")
+    t = up(inp["t"], "f32")
+    ctx = up(inp["ctx"], m.dtype)
+    mod = torch.empty((B, 6 * d), dtype=torch.float32, device=dev)
+    ws = torch.empty(W.workspace_bytes(cfg, B, work.lat_f, work.lat_h, work.lat_w),
+                     dtype=torch.uint8, device=dev)
+    tws = torch.empty(B * (d + m.freq_dim) * 4, dtype=torch.uint8, device=dev)
+    tws_c, bws_c = W.tmlp_weights(twd), W.block_weights(bwd)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        W.tmlp_fwd(cfg, t, tws_c, mod, tws, stream)
+        W.dit_block_fwd(cfg, x, B, work.lat_f, work.Hp, work.Wp, mod, bws_c, ctx, None, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    t_wall = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    if not all(math.isfinite(v) for v in x[0, :4, :4].flatten().tolist()):
+        raise RuntimeError("non-finite block output")
+
+    # ---- the dominant kernel (self-attention), timed on its own stream with HIP events
+    hd = d // H
+    g = torch.Generator(device="cpu").manual_seed(7)
+    qk = (torch.randn((B * L, 2 * d), generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    Lp = (L + 63) // 64 * 64
+    vt = torch.randn((d, B * Lp), generator=g).to(torch.bfloat16).to(dev)
+    o = torch.empty((B * L, d), dtype=torch.bfloat16, device=dev)
+
+    def attn():
+        W.attention_fwd(qk, 2 * d, qk[:, d:], 2 * d, vt, B * Lp, Lp, o, d, B, H, L, L, stream)
+
+    for _ in range(2):
+        attn()
+    n_att = max(3, args.steps // 2)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n_att):
+        attn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = e0.elapsed_time(e1) / n_att
+
+    gemm_f, sa_f, ca_f = block_flops(B, L, d, H, F, m.text_len)
+    attn_tf = sa_f / (attn_ms * 1e-3) / 1e12
+    block_tf = (gemm_f + sa_f + ca_f) / (ms * 1e-3) / 1e12
+    tokens_s = B * L / (ms * 1e-3)
+
+    out = {
+        "metric": "DiT block tokens/s + attn TFLOP/s (% bf16 MFMA peak), 1.3B @ 480P L=32760",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations)",
+        "config": {"workload": work.name, "batch": B, "latent": [16, work.lat_f, work.lat_h, work.lat_w],
+                   "tokens": L, "dim": d, "heads": H, "ffn": F, "text_tokens": m.text_len},
+        "attn_tflops": round(attn_tf, 1),
+        "attn_frac_of_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+        "block_tflops": round(block_tf, 1),
+        "block_frac_of_peak": round(block_tf / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "k_attn_bf16", "achieved": round(attn_tf, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "launch_ms": round(attn_ms, 4),
+                     "flop_per_launch": sa_f},
+        "wall_s_timed": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(work, inp, tw, bw)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

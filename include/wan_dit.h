@@ -1,0 +1,178 @@
+/*
+ * wan_dit.h -- C ABI of libwandit, the gfx950 (MI355X) implementation of one
+ * Wan2.1 Diffusion-Transformer denoising step.
+ *
+ * Sources the operations follow (page title, section):
+ *   [Note] "Wan: Open and Advanced Large-Scale Video Generative Models
+ *          (Wan 2.1)", sections 模型架构 (Wan-VAE, Diffusion Transformer),
+ *          配置表, I2V 架构扩展, 训练方法.
+ *   [News] "超越Sora！阿里正式完全开源最新、最强大的视频生成模型 Wan2.1",
+ *          sections 核心创新二 (视频扩散 DiT) and 核心创新四 (Image-to-Video).
+ *
+ * Conventions shared by every entry point
+ *   - Row-major.  Linear weights are [out, in] (y = x W^T + b), so both GEMM
+ *     operands are contiguous along the reduction axis.
+ *   - Weight / bias / context dtype is cfg->dtype (WAN_BF16 or WAN_F32).
+ *     The residual stream x, the modulation, the timestep, the latent and the
+ *     step output are always float32.  The per-block modulation bias is float32.
+ *   - Every pointer named "device" is device memory owned by the caller; the
+ *     library never allocates or frees memory.  Temporaries live in the
+ *     caller's workspace (ws, ws_bytes), sized by wan_workspace_bytes().
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without waiting.  Calls are stateless;
+ *     concurrent calls need distinct workspaces and outputs.
+ *   - Errors: every argument is validated on the host before anything is
+ *     enqueued, so a call that returns an error has enqueued nothing.  The
+ *     one exception is WAN_ERR_HIP, returned when a kernel launch fails
+ *     (hipGetLastError); kernels enqueued before the failing one may run.
+ */
+#ifndef WAN_DIT_H
+#define WAN_DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define WAN_OK             0
+#define WAN_ERR_NULL      -1  /* a required pointer is NULL                         */
+#define WAN_ERR_SHAPE     -2  /* sizes inconsistent: odd H/8 or W/8, dim != heads*head_dim,
+                                 unsupported head_dim, empty sequence, ...          */
+#define WAN_ERR_DTYPE     -3  /* cfg->dtype is neither WAN_F32 nor WAN_BF16          */
+#define WAN_ERR_WORKSPACE -4  /* ws_bytes smaller than wan_workspace_bytes()         */
+#define WAN_ERR_CONFIG    -5  /* I2V pointers inconsistent with in_ch / img_len      */
+#define WAN_ERR_HIP       -6  /* a HIP launch failed                                 */
+
+/* operand dtypes */
+#define WAN_F32  0
+#define WAN_BF16 1
+
+/* Model configuration ([Note] 配置表: 1.3B = 1536/8960/12 heads/30 layers,
+ * 14B = 5120/13824/40/40; latent in/out 16 channels; frequency dim 256).   */
+typedef struct {
+    int dim;        /* model width d                                         */
+    int heads;      /* attention heads H                                     */
+    int head_dim;   /* d / H. WAN_BF16: 128.  WAN_F32: 64 or 128              */
+    int ffn;        /* FFN width F                                           */
+    int n_blocks;   /* blocks in a step                                      */
+    int in_ch;      /* latent channels fed to patchify: 16 (T2V) or 36 (I2V) */
+    int out_ch;     /* predicted latent channels: 16                         */
+    int freq_dim;   /* timestep embedding width: 256                          */
+    int text_len;   /* text tokens Lc (512)                                   */
+    int img_len;    /* image tokens Li: 0 (T2V) or 257 (I2V)                  */
+    int img_feat;   /* CLIP feature width (1280), I2V only                    */
+    float eps;      /* LayerNorm epsilon (1e-6)                               */
+    int dtype;      /* WAN_F32 or WAN_BF16                                    */
+} wan_cfg_t;
+
+/* Shared timestep MLP ([Note] Diffusion Transformer; [News] 核心创新二):
+ * w1 [d, freq_dim], b1 [d], w2 [6d, d], b2 [6d]; dtype cfg->dtype; device.   */
+typedef struct {
+    const void *w1, *b1, *w2, *b2;
+} wan_tmlp_weights_t;
+
+/* One block.  All device, dtype cfg->dtype unless noted.
+ *   sa_wqkv [3d, d] (rows: q | k | v), sa_bqkv [3d], sa_wo [d, d], sa_bo [d]
+ *   ca_wq [d, d], ca_bq [d], ca_wkv [2d, d] (rows: k | v), ca_bkv [2d]
+ *   ca_wkv_img [2d, d], ca_bkv_img [2d]  (image tokens; NULL unless img_len)
+ *   ca_wo [d, d], ca_bo [d]
+ *   ffn_w1 [F, d], ffn_b1 [F], ffn_w2 [d, F], ffn_b2 [d]
+ *   mod_bias [6d] float32: this block's own modulation bias, added to the
+ *            shared MLP output (order shift1, scale1, gate1, shift2, scale2, gate2). */
+typedef struct {
+    const void *sa_wqkv, *sa_bqkv, *sa_wo, *sa_bo;
+    const void *ca_wq, *ca_bq, *ca_wkv, *ca_bkv, *ca_wkv_img, *ca_bkv_img, *ca_wo, *ca_bo;
+    const void *ffn_w1, *ffn_b1, *ffn_w2, *ffn_b2;
+    const float *mod_bias;
+} wan_block_weights_t;
+
+/* Whole model.  patch_w [d, in_ch*4] is the Conv3d weight [d, in_ch, 1, 2, 2]
+ * flattened (feature k = c*4 + a*2 + b); for I2V the columns of channels
+ * 16..35 carry the zero-initialised extra projection ([News] 核心创新四).
+ * head_w [out_ch*4, d], head_b [out_ch*4].  img_w1 [d, img_feat], img_w2/w3
+ * [d, d] (+ biases [d]): the 3-layer image MLP, NULL unless img_len.
+ * `blocks` is a HOST array of n_blocks descriptors (device pointers inside). */
+typedef struct {
+    const void *patch_w, *patch_b;
+    wan_tmlp_weights_t tmlp;
+    const wan_block_weights_t *blocks;
+    const void *head_w, *head_b;
+    const void *img_w1, *img_b1, *img_w2, *img_b2, *img_w3, *img_b3;
+} wan_model_weights_t;
+
+/* Workspace bytes needed by any entry point for batch B and a latent of
+ * lat_f x H8 x W8 (H8 = H/8, W8 = W/8).  Returns 0 for an invalid cfg/shape. */
+size_t wan_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, int W8);
+
+/* Human-readable text of a status code (static storage). */
+const char *wan_status_str(int status);
+
+/* Shared AdaLN MLP ([Note] Diffusion Transformer; [News] 核心创新二;
+ * frequency dim 256 from [Note] 配置表):
+ *   e = [cos(t w_k) | sin(t w_k)], w_k = 10000^(-k/(freq_dim/2)), t raw;
+ *   mod = W2 SiLU(W1 e + b1) + b2.
+ * t [B] float32 device; mod [B, 6d] float32 device (written). */
+int wan_tmlp_fwd(const wan_cfg_t *cfg, const float *t, int B, const wan_tmlp_weights_t *w,
+                 float *mod, void *ws, size_t ws_bytes, void *stream);
+
+/* One DiT block, in place on the residual stream ([Note] Diffusion
+ * Transformer: full spatio-temporal self-attention; text cross-attention in
+ * every block; shared AdaLN with per-block biases):
+ *   x += gate1 * SA(LN(x)(1+scale1)+shift1)
+ *   x += CA(LN(x), ctx [, img_ctx])          (ungated, unmodulated)
+ *   x += gate2 * FFN(LN(x)(1+scale2)+shift2)
+ * x [B, L, d] float32 device (read and written), L = lat_f*Hp*Wp tokens in
+ * (frame, row, column) order; mod [B, 6d] float32 device (wan_tmlp_fwd);
+ * ctx [B, text_len, d] device; img_ctx [B, img_len, d] device when
+ * cfg->img_len > 0 (the output of the image MLP), else NULL. */
+int wan_dit_block_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, int Wp,
+                      const float *mod, const wan_block_weights_t *w, const void *ctx,
+                      const void *img_ctx, void *ws, size_t ws_bytes, void *stream);
+
+/* One denoising step ([Note] Diffusion Transformer: patchify with a (1,2,2)
+ * 3D convolution, N blocks, unpatchify; [Note] I2V 架构扩展 for the I2V
+ * inputs): latent [B, in_ch, lat_f, H8, W8] float32 device (for I2V: noise
+ * 16 | condition 16 | mask 4 channels); t [B] float32 device; ctx
+ * [B, text_len, d] device; clip_feat [B, img_len, img_feat] device or NULL
+ * (T2V); out [B, out_ch, lat_f, H8, W8] float32 device: the predicted
+ * flow-matching velocity ([Note] 训练方法). */
+int wan_dit_step_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, int B,
+                     int lat_f, int H8, int W8, const void *ctx, const void *clip_feat,
+                     const wan_model_weights_t *w, float *out, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Host helper ([News] 核心创新四; [Note] I2V 架构扩展): binary frame mask of
+ * the video (n_frames = 1+T bytes, 1 = keep, 0 = generate) -> 4 mask
+ * channels [4, lat_f, H8, W8] float32 HOST buffer.  Frame 0 is repeated four
+ * times, then every 4 consecutive frames form one latent frame (the VAE's
+ * temporal stride) and the position within the group is the channel.
+ * Requires n_frames = 4*(lat_f-1)+1.  Touches no device. */
+int wan_i2v_mask(const uint8_t *frame_mask, int n_frames, int lat_f, int H8, int W8, float *out);
+
+/* ---- component entry points (the kernels the block is made of) ---------- */
+
+/* Multi-head attention O = softmax(Q K^T / sqrt(hd)) V per (batch, head)
+ * ([Note] Diffusion Transformer).  bf16 only, hd = 128, device pointers:
+ *   q  [B, Lq, *] row stride ldq elements, head h at column h*128
+ *   k  [B, Lk, *] row stride ldk, head h at column h*128
+ *   vt [H*128, *] row stride ldv: V transposed; batch b's key j sits at
+ *      column b*vt_bstride + j.  ldv and vt_bstride are multiples of 8 and
+ *      every row holds at least B*vt_bstride columns, vt_bstride >= round_up(Lk, 8)
+ *      (columns past Lk are read but their values are ignored)
+ *   o  [B, Lq, H*128] bf16, row stride ldo.
+ * No mask.  Returns WAN_ERR_SHAPE for unsupported strides or sizes. */
+int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv, int vt_bstride,
+                      void *o, int ldo, int B, int H, int Lq, int Lk, void *stream);
+
+/* y = x W^T + b for a bf16 x [M, K], W [N, K], b [N] (device), K % 64 == 0.
+ * mode 0: y bf16 [M, N];  mode 1: y float32 [M, N];  mode 2: y bf16 = GELU_tanh(.) */
+int wan_linear_fwd(const void *x, const void *w, const void *b, void *y, int M, int N, int K,
+                   int mode, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WAN_DIT_H */

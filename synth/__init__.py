@@ -276,3 +276,25 @@ def workload_inputs(w: Workload) -> Dict[str, np.ndarray]:
         out["clip"] = np.stack([draw(c, "clip", (m.img_len, m.img_feat), sample=b, dtype=dt)
                                 for b in range(B)])
     return out
+
+
+def attention_inputs(seed: int, B: int, H: int, Lq: int, Lk: int, hd: int = 128,
+                     qk_std: float = 2.0, v_std: float = 1.0):
+    """Q, K, V for kernel-level attention stress tests, bf16-rounded float32.
+
+    With q, k ~ N(0, qk_std^2) the logits q.k/sqrt(hd) have std qk_std^2 (4
+    by default): a peaked softmax that exercises the running-max rescaling."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2025, 99, seed, B, H, Lq, Lk])))
+    q = bf16_round(g.standard_normal((B, Lq, H * hd), dtype=np.float32) * np.float32(qk_std))
+    k = bf16_round(g.standard_normal((B, Lk, H * hd), dtype=np.float32) * np.float32(qk_std))
+    v = bf16_round(g.standard_normal((B, Lk, H * hd), dtype=np.float32) * np.float32(v_std))
+    return q, k, v
+
+
+def linear_inputs(seed: int, M: int, N: int, K: int):
+    """x ~ N(0,1), W ~ N(0, 1/K), b ~ N(0, 1), all bf16-rounded float32."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2025, 98, seed, M, N, K])))
+    x = bf16_round(g.standard_normal((M, K), dtype=np.float32))
+    w = bf16_round(g.standard_normal((N, K), dtype=np.float32) / np.float32(np.sqrt(K)))
+    b = bf16_round(g.standard_normal((N,), dtype=np.float32))
+    return x, w, b

@@ -1,0 +1,11 @@
+"""MI355X (gfx950) implementation of the Wan2.1 DiT denoising step.
+
+The computation lives in ``libwandit.so`` (hand-written HIP kernels behind the
+C ABI of ``include/wan_dit.h``); :mod:`.binding` marshals torch device tensors
+into that ABI.  Build the library with ``python -m
+video_diffusion_transformer_block_amd.build`` (or ``__graft_entry__.build()``).
+"""
+from . import binding  # noqa: F401
+from .binding import (Cfg, WanError, attention_fwd, block_weights, dit_block_fwd,  # noqa: F401
+                      dit_step_fwd, i2v_mask, lib, linear_fwd, make_cfg, model_weights,
+                      status_str, tmlp_fwd, tmlp_weights, workspace_bytes)

@@ -1,0 +1,180 @@
+"""ctypes binding of libwandit (include/wan_dit.h): argument marshalling only.
+
+Every computation runs in the HIP library; this module converts torch device
+tensors into the plain pointers and sizes of the C ABI and turns a non-zero
+status into an exception.  It never computes anything itself and raises if
+the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwandit.so")
+
+WAN_F32, WAN_BF16 = 0, 1
+
+EXPORTS = ("wan_workspace_bytes", "wan_status_str", "wan_tmlp_fwd", "wan_dit_block_fwd",
+           "wan_dit_step_fwd", "wan_i2v_mask", "wan_attention_fwd", "wan_linear_fwd")
+
+
+class WanError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: status {status} ({text})")
+        self.status = status
+
+
+class Cfg(C.Structure):
+    _fields_ = [(n, C.c_int) for n in ("dim", "heads", "head_dim", "ffn", "n_blocks", "in_ch",
+                                         "out_ch", "freq_dim", "text_len", "img_len", "img_feat")] \
+        + [("eps", C.c_float), ("dtype", C.c_int)]
+
+
+class TmlpW(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("w1", "b1", "w2", "b2")]
+
+
+_BLOCK_FIELDS = ("sa_wqkv", "sa_bqkv", "sa_wo", "sa_bo", "ca_wq", "ca_bq", "ca_wkv", "ca_bkv",
+                 "ca_wkv_img", "ca_bkv_img", "ca_wo", "ca_bo", "ffn_w1", "ffn_b1", "ffn_w2",
+                 "ffn_b2", "mod_bias")
+
+
+class BlockW(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in _BLOCK_FIELDS]
+
+
+class ModelW(C.Structure):
+    _fields_ = [("patch_w", C.c_void_p), ("patch_b", C.c_void_p), ("tmlp", TmlpW),
+                ("blocks", C.POINTER(BlockW)), ("head_w", C.c_void_p), ("head_b", C.c_void_p)] \
+        + [(n, C.c_void_p) for n in ("img_w1", "img_b1", "img_w2", "img_b2", "img_w3", "img_b3")]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libwandit.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python video_diffusion_transformer_block_amd/build.py`")
+        L = C.CDLL(LIB_PATH)
+        vp, i, sz = C.c_void_p, C.c_int, C.c_size_t
+        L.wan_workspace_bytes.argtypes = [C.POINTER(Cfg), i, i, i, i]
+        L.wan_workspace_bytes.restype = sz
+        L.wan_status_str.argtypes = [i]
+        L.wan_status_str.restype = C.c_char_p
+        L.wan_tmlp_fwd.argtypes = [C.POINTER(Cfg), vp, i, C.POINTER(TmlpW), vp, vp, sz, vp]
+        L.wan_dit_block_fwd.argtypes = [C.POINTER(Cfg), vp, i, i, i, i, vp, C.POINTER(BlockW), vp,
+                                        vp, vp, sz, vp]
+        L.wan_dit_step_fwd.argtypes = [C.POINTER(Cfg), vp, vp, i, i, i, i, vp, vp, C.POINTER(ModelW),
+                                       vp, vp, sz, vp]
+        L.wan_i2v_mask.argtypes = [vp, i, i, i, i, vp]
+        L.wan_attention_fwd.argtypes = [vp, i, vp, i, vp, i, i, vp, i, i, i, i, i, vp]
+        L.wan_linear_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+        for n in EXPORTS[2:]:
+            getattr(L, n).restype = i
+        _lib = L
+    return _lib
+
+
+def status_str(st: int) -> str:
+    return lib().wan_status_str(st).decode()
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise WanError(fn, st, status_str(st))
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def make_cfg(*, dim, heads, ffn, n_blocks=1, in_ch=16, out_ch=16, freq_dim=256, text_len=512,
+             img_len=0, img_feat=1280, eps=1e-6, dtype="bf16") -> Cfg:
+    return Cfg(dim, heads, dim // heads, ffn, n_blocks, in_ch, out_ch, freq_dim, text_len,
+               img_len, img_feat, eps, WAN_BF16 if dtype == "bf16" else WAN_F32)
+
+
+def workspace_bytes(cfg: Cfg, B: int, lat_f: int, H8: int, W8: int) -> int:
+    return int(lib().wan_workspace_bytes(C.byref(cfg), B, lat_f, H8, W8))
+
+
+def tmlp_weights(d: Dict[str, torch.Tensor]) -> TmlpW:
+    return TmlpW(_p(d["w1"]), _p(d["b1"]), _p(d["w2"]), _p(d["b2"]))
+
+
+def block_weights(d: Dict[str, torch.Tensor]) -> BlockW:
+    return BlockW(*[_p(d.get(n)) for n in _BLOCK_FIELDS])
+
+
+def model_weights(d: Dict[str, object], blocks: Sequence[BlockW]):
+    """Returns (ModelW, keep-alive array of block descriptors)."""
+    arr = (BlockW * max(1, len(blocks)))(*blocks)
+    img = d.get("img") or {}
+    mw = ModelW(_p(d["patch_w"]), _p(d["patch_b"]), tmlp_weights(d["tmlp"]),
+                C.cast(arr, C.POINTER(BlockW)), _p(d["head_w"]), _p(d["head_b"]),
+                *[_p(img.get(n)) for n in ("w1", "b1", "w2", "b2", "w3", "b3")])
+    return mw, arr
+
+
+def tmlp_fwd(cfg: Cfg, t: torch.Tensor, tw: TmlpW, mod: torch.Tensor, ws: torch.Tensor,
+             stream=None):
+    _check("wan_tmlp_fwd", lib().wan_tmlp_fwd(C.byref(cfg), _p(t), t.numel(), C.byref(tw), _p(mod),
+                                              _p(ws), ws.numel() * ws.element_size(),
+                                              _stream(stream)))
+
+
+def dit_block_fwd(cfg: Cfg, x: torch.Tensor, B: int, lat_f: int, Hp: int, Wp: int,
+                  mod: torch.Tensor, bw: BlockW, ctx: torch.Tensor, img_ctx: Optional[torch.Tensor],
+                  ws: torch.Tensor, stream=None):
+    _check("wan_dit_block_fwd",
+           lib().wan_dit_block_fwd(C.byref(cfg), _p(x), B, lat_f, Hp, Wp, _p(mod), C.byref(bw),
+                                   _p(ctx), _p(img_ctx), _p(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
+
+
+def dit_step_fwd(cfg: Cfg, latent: torch.Tensor, t: torch.Tensor, ctx: torch.Tensor,
+                 clip: Optional[torch.Tensor], mw: ModelW, out: torch.Tensor, ws: torch.Tensor,
+                 stream=None):
+    B, _, F, H8, W8 = latent.shape
+    _check("wan_dit_step_fwd",
+           lib().wan_dit_step_fwd(C.byref(cfg), _p(latent), _p(t), B, F, H8, W8, _p(ctx), _p(clip),
+                                  C.byref(mw), _p(out), _p(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)))
+
+
+def attention_fwd(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk, stream=None):
+    _check("wan_attention_fwd",
+           lib().wan_attention_fwd(_p(q), ldq, _p(k), ldk, _p(vt), ldv, vt_bstride, _p(o), ldo,
+                                   B, H, Lq, Lk, _stream(stream)))
+
+
+def linear_fwd(x, w, b, y, M, N, K, mode, stream=None):
+    _check("wan_linear_fwd", lib().wan_linear_fwd(_p(x), _p(w), _p(b), _p(y), M, N, K, mode,
+                                                  _stream(stream)))
+
+
+def i2v_mask(frame_mask: Sequence[int], lat_f: int, H8: int, W8: int):
+    """Host helper: the 4 I2V mask channels [4, lat_f, H8, W8] as a float32 CPU tensor."""
+    fm = (C.c_uint8 * len(frame_mask))(*[1 if v else 0 for v in frame_mask])
+    out = torch.empty((4, lat_f, H8, W8), dtype=torch.float32)
+    _check("wan_i2v_mask", lib().wan_i2v_mask(C.cast(fm, C.c_void_p), len(frame_mask), lat_f, H8, W8,
+                                              _p(out)))
+    return out

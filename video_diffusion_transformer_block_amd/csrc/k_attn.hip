@@ -1,0 +1,317 @@
+// Attention O = softmax(Q K^T / sqrt(hd)) V per (batch, head), no mask and no
+// positional term: the full spatio-temporal self-attention and the text /
+// image cross-attention of a DiT block ("Wan: Open and Advanced Large-Scale
+// Video Generative Models (Wan 2.1)", section Diffusion Transformer; section
+// I2V 架构扩展 for the decoupled image attention).
+//
+// bf16 path (hd = 128), flash style with an online softmax:
+//  * a 256-thread workgroup owns 256 queries of one (batch, head); each
+//    wavefront owns 64 of them as two 32-query groups that share every K / V
+//    operand fragment read from LDS (halves the LDS traffic per MFMA);
+//  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//    a lane then holds 16 keys of ONE query, so the row max / row sum are
+//    per-lane reductions plus one exchange between lanes l and l^32;
+//  * O^T = V^T P^T: the probabilities are already in the B-operand layout,
+//    and V arrives transposed ([hd][key], written so by the projection GEMM),
+//    so the A operand is two 8-byte LDS reads per fragment;
+//  * K and V^T tiles of 64 keys are double-buffered in LDS; the next tile's
+//    global loads are in flight while the current one is processed;
+//  * the running max is only raised (and the accumulators rescaled) when a
+//    tile's max exceeds it by more than 2^8, so most tiles skip the rescale;
+//    probabilities stay <= 256, exact in the bf16 mantissa's relative sense.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace wan {
+
+constexpr int AQ = 256;   // queries per workgroup
+constexpr int AK = 64;    // keys per tile
+constexpr int HD = 128;   // head dim
+constexpr float TAU = 8.0f;
+
+WAN_DEV int vswz(int row) { return (row & 15) ^ ((row >> 4) & 1); }
+
+WAN_DEV float other_half(float v) { return __shfl_xor(v, 32); }
+
+__global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnDesc a) {
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][AK * HD];   // [key][hd], 16B chunks ^ (key&15)
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][HD * AK];   // [hd][key], 8B units ^ vswz(hd)
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int nqt = (a.Lq + AQ - 1) / AQ;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = bid % nqt, bh = bid / nqt;
+  const int h = bh % a.H, b = bh / a.H;
+  const int Lq = a.Lq, Lk = a.Lk;
+
+  const bf16 *Qg = reinterpret_cast<const bf16 *>(a.q);
+  const bf16 *Kg = reinterpret_cast<const bf16 *>(a.k);
+  const bf16 *Vg = reinterpret_cast<const bf16 *>(a.vt);
+
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[q][st*16 + g*8 .. +8]
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int row = qt * AQ + w * 64 + gi * 32 + l32;
+    const bool ok = row < Lq;
+    const bf16 *qp = Qg + (long)(b * Lq + (ok ? row : 0)) * a.ldq + h * HD + g * 8;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      uint4 v = ok ? ld16(qp + st * 16) : make_uint4(0, 0, 0, 0);
+      qf[gi][st] = *reinterpret_cast<bf16x8 *>(&v);
+    }
+  }
+
+  f32x16 o[2][4];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[gi][t][r] = 0.f;
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  const float c = a.scale * 1.4426950408889634f;   // scores -> log2 units
+
+  // ---- tile loaders: K tile = 64 keys x 16 chunks; V^T tile = 128 rows x 8 chunks
+  uint4 rk[4], rv[4];
+  const int kkey = tid >> 4, kc = tid & 15;
+  const int vrow = tid >> 3, vc = tid & 7;
+  const long vbase = (long)b * a.vt_bstride;
+  auto gload = [&](int j) {
+    const int key0 = j * AK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kg = key0 + kkey + 16 * i;
+      rk[i] = kg < Lk ? ld16(Kg + (long)(b * Lk + kg) * a.ldk + h * HD + kc * 8)
+                      : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = vrow + 32 * i;
+      const int col = key0 + vc * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (col < Lk) {
+        v = ld16(Vg + (long)(h * HD + row) * a.ldv + vbase + col);
+        if (col + 8 > Lk) {   // ragged tail: clear keys >= Lk (their memory is padding)
+          uint32_t *e = reinterpret_cast<uint32_t *>(&v);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int k0 = col + 2 * u;
+            if (k0 >= Lk) e[u] = 0u;
+            else if (k0 + 1 >= Lk) e[u] &= 0xFFFFu;
+          }
+        }
+      }
+      rv[i] = v;
+    }
+  };
+  auto sstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kkey + 16 * i;
+      st16(&sK[st][key * HD + ((kc ^ (key & 15)) * 8)], rk[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = vrow + 32 * i;
+      const int f = vswz(row);
+      uint2 lo = make_uint2(rv[i].x, rv[i].y), hi = make_uint2(rv[i].z, rv[i].w);
+      *reinterpret_cast<uint2 *>(&sV[st][row * AK + (((2 * vc) ^ f) * 4)]) = lo;
+      *reinterpret_cast<uint2 *>(&sV[st][row * AK + (((2 * vc + 1) ^ f) * 4)]) = hi;
+    }
+  };
+
+  const int ntiles = (Lk + AK - 1) / AK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+
+    // ---- S^T = K Q^T for both query groups
+    f32x16 s[2][2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[gi][kb][r] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = kb * 32 + l32;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int ch = st * 2 + g;
+        bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&sK[cur][key * HD + ((ch ^ (key & 15)) * 8)]);
+        s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][st], s[0][kb], 0, 0, 0);
+        s[1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[1][st], s[1][kb], 0, 0, 0);
+      }
+    }
+    // keys past Lk (last tile only)
+    if ((j + 1) * AK > Lk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * AK + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+          if (key >= Lk) { s[0][kb][r] = -INFINITY; s[1][kb][r] = -INFINITY; }
+        }
+    }
+
+    // ---- online softmax, probabilities packed to bf16 in the B-operand layout
+    bf16x8 pb[2][2][2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      float mx = s[gi][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[gi][kb][r]);
+      mx = fmaxf(mx, other_half(mx));
+      const float mz = mx * c;
+      if (__builtin_amdgcn_ballot_w64(mz > m[gi] + TAU) != 0) {
+        const float mn = fmaxf(m[gi], mz);
+        const float alpha = __builtin_amdgcn_exp2f(m[gi] - mn);
+        l[gi] *= alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[gi][t][r] *= alpha;
+        m[gi] = mn;
+      }
+      const float nm = -m[gi];
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[gi][kb][r], c, nm));
+          ls += p;
+          pb[gi][kb][r >> 3][r & 7] = f2bf(p);
+        }
+      l[gi] += ls;
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = t * 32 + l32;
+      const int f = vswz(row);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int ua = (kb * 32 + 16 * hf + g * 4) >> 2;   // 8-byte unit of 4 keys
+          uint2 lo = *reinterpret_cast<const uint2 *>(&sV[cur][row * AK + ((ua ^ f) * 4)]);
+          uint2 hi = *reinterpret_cast<const uint2 *>(&sV[cur][row * AK + (((ua + 2) ^ f) * 4)]);
+          uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          bf16x8 va = *reinterpret_cast<bf16x8 *>(&vv);
+          o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[0][kb][hf], o[0][t], 0, 0, 0);
+          o[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[1][kb][hf], o[1][t], 0, 0, 0);
+        }
+    }
+
+    if (j + 1 < ntiles) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: lane holds O^T[hd = t*32 + (r/4)*8 + g*4 + r%4][q = l32]
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const float lt = l[gi] + other_half(l[gi]);
+    const float inv = 1.0f / lt;
+    const int row = qt * AQ + w * 64 + gi * 32 + l32;
+    if (row >= Lq) continue;
+    const long orow = (long)(b * Lq + row);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int hd0 = t * 32 + rb * 8 + g * 4;
+        float v0 = o[gi][t][rb * 4 + 0] * inv, v1 = o[gi][t][rb * 4 + 1] * inv;
+        float v2 = o[gi][t][rb * 4 + 2] * inv, v3 = o[gi][t][rb * 4 + 3] * inv;
+        if (a.out_mode == 1) {
+          *reinterpret_cast<float4 *>(a.acc32 + orow * (a.H * HD) + h * HD + hd0) =
+              make_float4(v0, v1, v2, v3);
+          continue;
+        }
+        if (a.out_mode == 2) {
+          float4 p = *reinterpret_cast<const float4 *>(a.acc32 + orow * (a.H * HD) + h * HD + hd0);
+          v0 += p.x; v1 += p.y; v2 += p.z; v3 += p.w;
+        }
+        bf16x4 ov;
+        ov[0] = f2bf(v0); ov[1] = f2bf(v1); ov[2] = f2bf(v2); ov[3] = f2bf(v3);
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(a.o) + orow * a.ldo + h * HD + hd0) = ov;
+      }
+  }
+}
+
+// float32 path: one wavefront per (batch, head, query); lanes stride over the
+// keys with a per-lane online softmax, merged across the wavefront at the end.
+// V is read untransposed: rows [B*Lk, ldv], head h at column h*hd.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_f32(AttnDesc a) {
+  const int lane = threadIdx.x & 63;
+  const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long total = (long)a.B * a.H * a.Lq;
+  if (wid >= total) return;
+  const int qi = wid % a.Lq;
+  const int bh = wid / a.Lq;
+  const int h = bh % a.H, b = bh / a.H;
+  const float *Q = reinterpret_cast<const float *>(a.q) + (long)(b * a.Lq + qi) * a.ldq + h * D;
+  const float *K = reinterpret_cast<const float *>(a.k);
+  const float *V = reinterpret_cast<const float *>(a.vt);
+  float qv[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) { qv[d] = Q[d]; acc[d] = 0.f; }
+  float m = -INFINITY, l = 0.f;
+  for (int j = lane; j < a.Lk; j += 64) {
+    const float *kp = K + (long)(b * a.Lk + j) * a.ldk + h * D;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) s = fmaf(qv[d], kp[d], s);
+    s *= a.scale;
+    const float mn = fmaxf(m, s);
+    const float al = expf(m - mn), p = expf(s - mn);
+    l = l * al + p;
+    const float *vp = V + (long)(b * a.Lk + j) * a.ldv + h * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vp[d], acc[d] * al);
+    m = mn;
+  }
+  const float M = wave_max(m);
+  const float f = (m == -INFINITY) ? 0.f : expf(m - M);
+  const float lt = wave_sum(l * f);
+  float *O = reinterpret_cast<float *>(a.o) + (long)(b * a.Lq + qi) * a.ldo + h * D;
+  float *A32 = a.acc32 + (long)(b * a.Lq + qi) * (a.H * D) + h * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const float v = wave_sum(acc[d] * f) / lt;
+    if (lane == (d & 63)) {
+      if (a.out_mode == 1) A32[d] = v;
+      else if (a.out_mode == 2) O[d] = v + A32[d];
+      else O[d] = v;
+    }
+  }
+}
+
+hipError_t launch_attention(const AttnDesc &a, hipStream_t s) {
+  if (a.B <= 0 || a.H <= 0 || a.Lq <= 0 || a.Lk <= 0) return hipSuccess;
+  if (a.f32) {
+    const long waves = (long)a.B * a.H * a.Lq;
+    const int blocks = (int)((waves + 3) / 4);
+    if (a.hd == 64) k_attn_f32<64><<<blocks, 256, 0, s>>>(a);
+    else if (a.hd == 128) k_attn_f32<128><<<blocks, 256, 0, s>>>(a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  if (a.hd != HD) return hipErrorInvalidValue;
+  const int nqt = (a.Lq + AQ - 1) / AQ;
+  k_attn_bf16<<<a.B * a.H * nqt, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace wan

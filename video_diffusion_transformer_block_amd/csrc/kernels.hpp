@@ -1,0 +1,56 @@
+// Host-side launch interface of the libwandit kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wan {
+
+enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_GELU = 2, OUT_RESID = 3 };
+
+// C[M,N] = A[M,K] . B[N,K]^T (+ bias) with an epilogue.
+struct GemmDesc {
+  const void *A; long lda;     // [M, K]
+  const void *B; long ldb;     // [N, K]
+  int M, N, K;
+  const void *bias;            // [N] (or [M] when bias_rows), may be NULL
+  int bias_rows;
+  int kind;                    // OutKind
+  void *C; long ldc;           // OUT_BF16 / OUT_F32 / OUT_GELU destination
+  // OUT_RESID: x[m, n] += gate[b(m), n] * (acc + bias[n]); gate may be NULL (=1)
+  float *X; long ldx;
+  const float *gate; long gate_bstride; int rows_per_batch;
+  int f32;                     // operands / bias / C are float32 instead of bf16
+};
+
+// Attention O = softmax(Q K^T * scale) V for every (batch, head); hd = 128, bf16.
+struct AttnDesc {
+  const void *q; long ldq;     // [B*Lq, ldq], head h at column h*hd
+  const void *k; long ldk;     // [B*Lk, ldk]
+  const void *vt; long ldv; long vt_bstride;  // [H*hd, ldv], batch b at column b*vt_bstride
+  void *o; long ldo;           // [B*Lq, ldo]
+  int B, H, Lq, Lk, hd;
+  float scale;                 // 1/sqrt(hd)
+  int out_mode;                // 0: o = O (bf16); 1: acc32 = O; 2: o = acc32 + O
+  float *acc32;                // [B*Lq, H*hd] float32 partial (modes 1, 2)
+  int f32;                     // float32 path (generic kernel): v given untransposed in `vt`
+};
+
+hipError_t launch_mod_combine(const float *mod, const float *bias, float *out, int B, int n,
+                              hipStream_t s);
+hipError_t launch_ln_mod(const float *x, int M, int L, int d, const float *modb, long modb_bstride,
+                         int shift_off, int scale_off, int has_mod, float eps, void *out,
+                         int out_f32, hipStream_t s);
+hipError_t launch_gemm(const GemmDesc &g, hipStream_t s);
+hipError_t launch_attention(const AttnDesc &a, hipStream_t s);
+hipError_t launch_tmlp(const float *t, int B, int freq_dim, int d, const void *w1, const void *b1,
+                       const void *w2, const void *b2, float *hidden, float *mod, int f32,
+                       hipStream_t s);
+hipError_t launch_patch_gather(const float *latent, int B, int C, int F, int H8, int W8, int Kp,
+                               void *P, int f32, hipStream_t s);
+hipError_t launch_head_unpatchify(const float *x, int B, int F, int Hp, int Wp, int d,
+                                  const void *w, const void *b, int out_ch, float *out, int f32,
+                                  hipStream_t s);
+hipError_t launch_pad_rows(const void *src, int R, int K, int Kp, void *dst, int f32, hipStream_t s);
+
+}  // namespace wan

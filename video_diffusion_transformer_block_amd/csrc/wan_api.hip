@@ -1,0 +1,392 @@
+// libwandit host side: argument validation, workspace carving and the launch
+// sequence of the block and the step.  Every entry point validates all of its
+// arguments before it enqueues anything.  See include/wan_dit.h for the ABI.
+//
+// Block sequence ("Wan: Open and Advanced Large-Scale Video Generative Models
+// (Wan 2.1)", section Diffusion Transformer; "超越Sora！…Wan2.1", section 核心创新二):
+//   modb = mod + bias_i
+//   h  = LN(x)(1+scale1)+shift1                       [k_ln_mod]
+//   q|k = h Wqk^T + b ;  V^T = Wv h^T + b               [GEMM, GEMM with swapped operands]
+//   o  = softmax(q k^T/sqrt(hd)) v                      [flash attention]
+//   x += gate1 * (o Wo^T + bo)                          [GEMM, residual epilogue]
+//   hc = LN(x) ; qc = hc Wq^T + b ; kc, V^T_c from ctx   [k_ln_mod, GEMMs]
+//   o  = Attn(qc, kc, vc) (+ Attn(qc, ki, vi) for I2V)   [attention]
+//   x += o Wo_c^T + bo_c                                 [GEMM, residual epilogue]
+//   h  = LN(x)(1+scale2)+shift2 ; u = GELU(h W1^T + b1)  [k_ln_mod, GEMM+GELU]
+//   x += gate2 * (u W2^T + b2)                           [GEMM, residual epilogue]
+#include <math.h>
+#include <string.h>
+
+#include "../../include/wan_dit.h"
+#include "kernels.hpp"
+
+using namespace wan;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+long rup(long v, long a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+  size_t modb, hid, h, qk, vt, o, qc, kc, vtc, ki, vti, acc32, u;   // block
+  size_t mod, x, P, pw, img1, img2, imgc;                           // step
+  size_t total;
+  long Lp, Lcp, Lip;
+  int Kp;
+};
+
+Layout make_layout(const wan_cfg_t &c, int B, long L, bool step) {
+  Layout y;
+  memset(&y, 0, sizeof(y));
+  const bool f32 = c.dtype == WAN_F32;
+  const size_t es = f32 ? 4 : 2;
+  const long d = c.dim, F = c.ffn, Lc = c.text_len, Li = c.img_len;
+  y.Lp = rup(L, 64);
+  y.Lcp = rup(Lc, 64);
+  y.Lip = rup(Li > 0 ? Li : 1, 64);
+  y.Kp = (int)rup(4L * c.in_ch, 64);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up(bytes, ALIGN); return o; };
+  y.modb = take(B * 6 * d * 4);
+  y.hid = take(B * (d + c.freq_dim) * 4);
+  y.h = take(B * L * d * es);
+  y.qk = take(B * L * (f32 ? 3 : 2) * d * es);
+  y.vt = take(f32 ? 0 : d * B * y.Lp * es);
+  y.o = take(B * L * d * es);
+  y.qc = take(B * L * d * es);
+  y.kc = take(B * Lc * (f32 ? 2 : 1) * d * es);
+  y.vtc = take(f32 ? 0 : d * B * y.Lcp * es);
+  y.ki = take(Li ? B * Li * (f32 ? 2 : 1) * d * es : 0);
+  y.vti = take(Li && !f32 ? d * B * y.Lip * es : 0);
+  y.acc32 = take(Li ? B * L * d * 4 : 0);
+  y.u = take(B * L * F * es);
+  if (step) {
+    y.mod = take(B * 6 * d * 4);
+    y.x = take(B * L * d * 4);
+    y.P = take(B * L * y.Kp * es);
+    y.pw = take(d * y.Kp * es);
+    y.img1 = take(Li ? B * Li * d * es : 0);
+    y.img2 = take(Li ? B * Li * d * es : 0);
+    y.imgc = take(Li ? B * Li * d * es : 0);
+  }
+  y.total = off;
+  return y;
+}
+
+int check_cfg(const wan_cfg_t *c) {
+  if (!c) return WAN_ERR_NULL;
+  if (c->dtype != WAN_F32 && c->dtype != WAN_BF16) return WAN_ERR_DTYPE;
+  if (c->dim <= 0 || c->heads <= 0 || c->head_dim <= 0 || c->ffn <= 0 || c->n_blocks < 0 ||
+      c->in_ch <= 0 || c->out_ch <= 0 || c->freq_dim <= 0 || c->text_len <= 0 || c->img_len < 0)
+    return WAN_ERR_SHAPE;
+  if (c->heads * c->head_dim != c->dim) return WAN_ERR_SHAPE;
+  if (c->freq_dim % 2) return WAN_ERR_SHAPE;
+  if (!(c->eps > 0.f) || !isfinite(c->eps)) return WAN_ERR_SHAPE;
+  if (c->dtype == WAN_BF16) {
+    // MFMA tiles: K of every GEMM a multiple of 64; attention head dim 128
+    if (c->head_dim != 128 || c->ffn % 64 || c->freq_dim % 8) return WAN_ERR_SHAPE;
+    if (c->img_len > 0 && (c->img_feat <= 0 || c->img_feat % 64)) return WAN_ERR_SHAPE;
+  } else {
+    if (c->head_dim != 64 && c->head_dim != 128) return WAN_ERR_SHAPE;
+    if (c->dim % 4 || c->freq_dim % 4) return WAN_ERR_SHAPE;
+    if (c->img_len > 0 && (c->img_feat <= 0 || c->img_feat % 4)) return WAN_ERR_SHAPE;
+  }
+  return WAN_OK;
+}
+
+int check_dims(int B, int lat_f, int Hp, int Wp) {
+  if (B <= 0 || B > 8 || lat_f <= 0 || Hp <= 0 || Wp <= 0) return WAN_ERR_SHAPE;
+  const long L = (long)lat_f * Hp * Wp;
+  if ((long)B * L > (1L << 30)) return WAN_ERR_SHAPE;
+  return WAN_OK;
+}
+
+hipStream_t S(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+#define WAN_TRY(expr)                              \
+  do {                                             \
+    if ((expr) != hipSuccess) return WAN_ERR_HIP;  \
+  } while (0)
+
+const char *off(const void *p, long elems, size_t es) {
+  return reinterpret_cast<const char *>(p) + elems * (long)es;
+}
+
+GemmDesc gemm(const void *A, long lda, const void *B, long ldb, int M, int N, int K,
+              const void *bias, int kind, void *C, long ldc, int f32) {
+  GemmDesc g;
+  memset(&g, 0, sizeof(g));
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.M = M; g.N = N; g.K = K;
+  g.bias = bias; g.kind = kind; g.C = C; g.ldc = ldc; g.f32 = f32;
+  return g;
+}
+
+GemmDesc resid(const void *A, long lda, const void *W, int M, int N, int K, const void *bias,
+               float *X, const float *gate, long gate_bs, int rows_per_batch, int f32) {
+  GemmDesc g = gemm(A, lda, W, K, M, N, K, bias, OUT_RESID, nullptr, 0, f32);
+  g.X = X; g.ldx = N; g.gate = gate; g.gate_bstride = gate_bs; g.rows_per_batch = rows_per_batch;
+  return g;
+}
+
+// y[B*Lk, d] = src W^T + b ; V^T[d, b*ldvb + j] = (src_b Wv^T + bv)^T for a K/V source.
+int kv_project(const wan_cfg_t &c, int B, int Lk, const void *src, const void *wkv,
+               const void *bkv, char *kbuf, char *vtbuf, long ldvb, hipStream_t s) {
+  const int d = c.dim;
+  const int f32 = c.dtype == WAN_F32;
+  const size_t es = f32 ? 4 : 2;
+  if (f32) {   // one GEMM, keys and values side by side: [B*Lk, 2d]
+    WAN_TRY(launch_gemm(gemm(src, d, wkv, d, B * Lk, 2 * d, d, bkv, OUT_BF16, kbuf, 2 * d, 1), s));
+    return WAN_OK;
+  }
+  WAN_TRY(launch_gemm(gemm(src, d, wkv, d, B * Lk, d, d, bkv, OUT_BF16, kbuf, d, 0), s));
+  for (int b = 0; b < B; ++b) {
+    GemmDesc g = gemm(off(wkv, (long)d * d, es), d, off(src, (long)b * Lk * d, es), d, d, Lk, d,
+                      off(bkv, d, es), OUT_BF16, vtbuf + (long)b * ldvb * es, (long)B * ldvb, 0);
+    g.bias_rows = 1;
+    WAN_TRY(launch_gemm(g, s));
+  }
+  return WAN_OK;
+}
+
+AttnDesc attn(const void *q, long ldq, const void *k, long ldk, const void *v, long ldv,
+              long vbs, void *o, long ldo, int B, int H, int Lq, int Lk, int hd, int f32) {
+  AttnDesc a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.vt = v; a.ldv = ldv; a.vt_bstride = vbs;
+  a.o = o; a.ldo = ldo; a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk; a.hd = hd;
+  a.scale = 1.0f / sqrtf((float)hd); a.f32 = f32;
+  return a;
+}
+
+int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
+              const wan_block_weights_t &w, const void *ctx, const void *img, char *ws,
+              const Layout &y, hipStream_t s) {
+  const int d = c.dim, F = c.ffn, H = c.heads, hd = c.head_dim, Lc = c.text_len, Li = c.img_len;
+  const int f32 = c.dtype == WAN_F32;
+  const size_t es = f32 ? 4 : 2;
+  const int M = (int)(B * L);
+  float *modb = reinterpret_cast<float *>(ws + y.modb);
+  char *h = ws + y.h, *qk = ws + y.qk, *vt = ws + y.vt, *o = ws + y.o, *qc = ws + y.qc;
+  char *kc = ws + y.kc, *vtc = ws + y.vtc, *ki = ws + y.ki, *vti = ws + y.vti, *u = ws + y.u;
+  float *acc32 = reinterpret_cast<float *>(ws + y.acc32);
+
+  WAN_TRY(launch_mod_combine(mod, w.mod_bias, modb, B, 6 * d, s));
+  // ---- self-attention branch
+  WAN_TRY(launch_ln_mod(x, M, (int)L, d, modb, 6 * d, 0, d, 1, c.eps, h, f32, s));
+  if (f32) {
+    WAN_TRY(launch_gemm(gemm(h, d, w.sa_wqkv, d, M, 3 * d, d, w.sa_bqkv, OUT_BF16, qk, 3 * d, 1), s));
+    WAN_TRY(launch_attention(attn(qk, 3 * d, off(qk, d, es), 3 * d, off(qk, 2 * d, es), 3 * d, 0,
+                                  o, d, B, H, (int)L, (int)L, hd, 1), s));
+  } else {
+    WAN_TRY(launch_gemm(gemm(h, d, w.sa_wqkv, d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0), s));
+    for (int b = 0; b < B; ++b) {
+      GemmDesc g = gemm(off(w.sa_wqkv, 2L * d * d, es), d, off(h, (long)b * L * d, es), d, d,
+                        (int)L, d, off(w.sa_bqkv, 2 * d, es), OUT_BF16, vt + b * y.Lp * es,
+                        (long)B * y.Lp, 0);
+      g.bias_rows = 1;
+      WAN_TRY(launch_gemm(g, s));
+    }
+    WAN_TRY(launch_attention(attn(qk, 2 * d, off(qk, d, es), 2 * d, vt, (long)B * y.Lp, y.Lp, o,
+                                  d, B, H, (int)L, (int)L, hd, 0), s));
+  }
+  WAN_TRY(launch_gemm(resid(o, d, w.sa_wo, M, d, d, w.sa_bo, x, modb + 2 * d, 6 * d, (int)L, f32), s));
+
+  // ---- cross-attention branch (pre-LN without modulation, ungated)
+  WAN_TRY(launch_ln_mod(x, M, (int)L, d, modb, 6 * d, 0, 0, 0, c.eps, h, f32, s));
+  WAN_TRY(launch_gemm(gemm(h, d, w.ca_wq, d, M, d, d, w.ca_bq, OUT_BF16, qc, d, f32), s));
+  int st = kv_project(c, B, Lc, ctx, w.ca_wkv, w.ca_bkv, kc, vtc, y.Lcp, s);
+  if (st) return st;
+  const long kld = f32 ? 2 * d : d;
+  AttnDesc at = f32 ? attn(qc, d, kc, kld, off(kc, d, es), kld, 0, o, d, B, H, (int)L, Lc, hd, 1)
+                    : attn(qc, d, kc, kld, vtc, (long)B * y.Lcp, y.Lcp, o, d, B, H, (int)L, Lc, hd, 0);
+  if (Li > 0) {
+    st = kv_project(c, B, Li, img, w.ca_wkv_img, w.ca_bkv_img, ki, vti, y.Lip, s);
+    if (st) return st;
+    at.out_mode = 1;
+    at.acc32 = acc32;
+    WAN_TRY(launch_attention(at, s));
+    AttnDesc ai = f32 ? attn(qc, d, ki, kld, off(ki, d, es), kld, 0, o, d, B, H, (int)L, Li, hd, 1)
+                      : attn(qc, d, ki, kld, vti, (long)B * y.Lip, y.Lip, o, d, B, H, (int)L, Li, hd, 0);
+    ai.out_mode = 2;
+    ai.acc32 = acc32;
+    WAN_TRY(launch_attention(ai, s));
+  } else {
+    WAN_TRY(launch_attention(at, s));
+  }
+  WAN_TRY(launch_gemm(resid(o, d, w.ca_wo, M, d, d, w.ca_bo, x, nullptr, 0, (int)L, f32), s));
+
+  // ---- FFN branch
+  WAN_TRY(launch_ln_mod(x, M, (int)L, d, modb, 6 * d, 3 * d, 4 * d, 1, c.eps, h, f32, s));
+  WAN_TRY(launch_gemm(gemm(h, d, w.ffn_w1, d, M, F, d, w.ffn_b1, OUT_GELU, u, F, f32), s));
+  WAN_TRY(launch_gemm(resid(u, F, w.ffn_w2, M, d, F, w.ffn_b2, x, modb + 5 * d, 6 * d, (int)L, f32), s));
+  return WAN_OK;
+}
+
+int check_block_weights(const wan_cfg_t &c, const wan_block_weights_t *w) {
+  if (!w) return WAN_ERR_NULL;
+  const void *req[] = {w->sa_wqkv, w->sa_bqkv, w->sa_wo, w->sa_bo, w->ca_wq, w->ca_bq, w->ca_wkv,
+                       w->ca_bkv, w->ca_wo, w->ca_bo, w->ffn_w1, w->ffn_b1, w->ffn_w2, w->ffn_b2,
+                       w->mod_bias};
+  for (const void *p : req)
+    if (!p) return WAN_ERR_NULL;
+  if (c.img_len > 0 && (!w->ca_wkv_img || !w->ca_bkv_img)) return WAN_ERR_CONFIG;
+  return WAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *wan_status_str(int st) {
+  switch (st) {
+    case WAN_OK: return "ok";
+    case WAN_ERR_NULL: return "a required pointer is NULL";
+    case WAN_ERR_SHAPE: return "inconsistent or unsupported sizes";
+    case WAN_ERR_DTYPE: return "unsupported dtype";
+    case WAN_ERR_WORKSPACE: return "workspace too small";
+    case WAN_ERR_CONFIG: return "I2V inputs inconsistent with the configuration";
+    case WAN_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t wan_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, int W8) {
+  if (check_cfg(cfg) != WAN_OK) return 0;
+  if (H8 <= 0 || W8 <= 0 || H8 % 2 || W8 % 2) return 0;
+  if (check_dims(B, lat_f, H8 / 2, W8 / 2) != WAN_OK) return 0;
+  const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
+  return make_layout(*cfg, B, L, true).total;
+}
+
+int wan_tmlp_fwd(const wan_cfg_t *cfg, const float *t, int B, const wan_tmlp_weights_t *w,
+                 float *mod, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (!t || !w || !mod || !ws || !w->w1 || !w->b1 || !w->w2 || !w->b2) return WAN_ERR_NULL;
+  if (B <= 0 || B > 8) return WAN_ERR_SHAPE;
+  const size_t need = (size_t)B * (cfg->dim + cfg->freq_dim) * 4;
+  if (ws_bytes < need) return WAN_ERR_WORKSPACE;
+  WAN_TRY(launch_tmlp(t, B, cfg->freq_dim, cfg->dim, w->w1, w->b1, w->w2, w->b2, (float *)ws, mod,
+                      cfg->dtype == WAN_F32, S(stream)));
+  return WAN_OK;
+}
+
+int wan_dit_block_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, int Wp,
+                      const float *mod, const wan_block_weights_t *w, const void *ctx,
+                      const void *img_ctx, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (!x || !mod || !ctx || !ws) return WAN_ERR_NULL;
+  if ((st = check_dims(B, lat_f, Hp, Wp))) return st;
+  if ((st = check_block_weights(*cfg, w))) return st;
+  if ((cfg->img_len > 0) != (img_ctx != nullptr)) return WAN_ERR_CONFIG;
+  const long L = (long)lat_f * Hp * Wp;
+  Layout y = make_layout(*cfg, B, L, false);
+  if (ws_bytes < y.total) return WAN_ERR_WORKSPACE;
+  return block_run(*cfg, x, B, L, mod, *w, ctx, img_ctx, (char *)ws, y, S(stream));
+}
+
+int wan_dit_step_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, int B, int lat_f,
+                     int H8, int W8, const void *ctx, const void *clip_feat,
+                     const wan_model_weights_t *w, float *out, void *ws, size_t ws_bytes,
+                     void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (!latent || !t || !ctx || !w || !out || !ws) return WAN_ERR_NULL;
+  if (H8 <= 0 || W8 <= 0 || H8 % 2 || W8 % 2) return WAN_ERR_SHAPE;
+  if ((st = check_dims(B, lat_f, H8 / 2, W8 / 2))) return st;
+  if (!w->patch_w || !w->patch_b || !w->head_w || !w->head_b || !w->tmlp.w1 || !w->tmlp.b1 ||
+      !w->tmlp.w2 || !w->tmlp.b2)
+    return WAN_ERR_NULL;
+  if (cfg->n_blocks > 0 && !w->blocks) return WAN_ERR_NULL;
+  for (int i = 0; i < cfg->n_blocks; ++i)
+    if ((st = check_block_weights(*cfg, &w->blocks[i]))) return st;
+  const bool i2v = cfg->img_len > 0;
+  if (i2v != (clip_feat != nullptr)) return WAN_ERR_CONFIG;
+  if (i2v && (!w->img_w1 || !w->img_b1 || !w->img_w2 || !w->img_b2 || !w->img_w3 || !w->img_b3))
+    return WAN_ERR_CONFIG;
+  const int Hp = H8 / 2, Wp = W8 / 2;
+  const long L = (long)lat_f * Hp * Wp;
+  Layout y = make_layout(*cfg, B, L, true);
+  if (ws_bytes < y.total) return WAN_ERR_WORKSPACE;
+
+  hipStream_t s = S(stream);
+  const int d = cfg->dim, f32 = cfg->dtype == WAN_F32;
+  const size_t es = f32 ? 4 : 2;
+  char *wsb = (char *)ws;
+  float *x = reinterpret_cast<float *>(wsb + y.x);
+  float *mod = reinterpret_cast<float *>(wsb + y.mod);
+  const int M = (int)(B * L);
+  // patchify: gather the (1,2,2) patches, then one GEMM against the padded Conv3d weight
+  WAN_TRY(launch_patch_gather(latent, B, cfg->in_ch, lat_f, H8, W8, y.Kp, wsb + y.P, f32, s));
+  WAN_TRY(launch_pad_rows(w->patch_w, d, 4 * cfg->in_ch, y.Kp, wsb + y.pw, f32, s));
+  WAN_TRY(launch_gemm(gemm(wsb + y.P, y.Kp, wsb + y.pw, y.Kp, M, d, y.Kp, w->patch_b, OUT_F32, x, d,
+                           f32), s));
+  // shared timestep MLP
+  WAN_TRY(launch_tmlp(t, B, cfg->freq_dim, d, w->tmlp.w1, w->tmlp.b1, w->tmlp.w2, w->tmlp.b2,
+                      reinterpret_cast<float *>(wsb + y.hid), mod, f32, s));
+  // I2V image context: three Linear layers with GELU between them
+  const void *img = nullptr;
+  if (i2v) {
+    const int Mi = B * cfg->img_len;
+    WAN_TRY(launch_gemm(gemm(clip_feat, cfg->img_feat, w->img_w1, cfg->img_feat, Mi, d,
+                             cfg->img_feat, w->img_b1, OUT_GELU, wsb + y.img1, d, f32), s));
+    WAN_TRY(launch_gemm(gemm(wsb + y.img1, d, w->img_w2, d, Mi, d, d, w->img_b2, OUT_GELU,
+                             wsb + y.img2, d, f32), s));
+    WAN_TRY(launch_gemm(gemm(wsb + y.img2, d, w->img_w3, d, Mi, d, d, w->img_b3, OUT_BF16,
+                             wsb + y.imgc, d, f32), s));
+    img = wsb + y.imgc;
+  }
+  (void)es;
+  for (int i = 0; i < cfg->n_blocks; ++i) {
+    st = block_run(*cfg, x, B, L, mod, w->blocks[i], ctx, img, wsb, y, s);
+    if (st) return st;
+  }
+  WAN_TRY(launch_head_unpatchify(x, B, lat_f, Hp, Wp, d, w->head_w, w->head_b, cfg->out_ch, out,
+                                 f32, s));
+  return WAN_OK;
+}
+
+int wan_i2v_mask(const uint8_t *frame_mask, int n_frames, int lat_f, int H8, int W8, float *out) {
+  if (!frame_mask || !out) return WAN_ERR_NULL;
+  if (n_frames <= 0 || lat_f <= 0 || H8 <= 0 || W8 <= 0) return WAN_ERR_SHAPE;
+  if ((n_frames - 1) % 4 || (n_frames - 1) / 4 + 1 != lat_f) return WAN_ERR_SHAPE;
+  const long plane = (long)H8 * W8;
+  for (int ch = 0; ch < 4; ++ch)
+    for (int f = 0; f < lat_f; ++f) {
+      // extended sequence: frame 0 four times, then frames 1..n-1; group f, member ch
+      const int e = f * 4 + ch;
+      const int src = e < 4 ? 0 : e - 3;
+      const float v = frame_mask[src] ? 1.0f : 0.0f;
+      float *p = out + ((long)ch * lat_f + f) * plane;
+      for (long i = 0; i < plane; ++i) p[i] = v;
+    }
+  return WAN_OK;
+}
+
+int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv,
+                      int vt_bstride, void *o, int ldo, int B, int H, int Lq, int Lk,
+                      void *stream) {
+  if (!q || !k || !vt || !o) return WAN_ERR_NULL;
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return WAN_ERR_SHAPE;
+  if (ldq < H * 128 || ldk < H * 128 || ldo < H * 128 || ldq % 8 || ldk % 8 || ldo % 4)
+    return WAN_ERR_SHAPE;
+  if (ldv % 8 || vt_bstride % 8 || vt_bstride < rup(Lk, 8) || (long)ldv < (long)B * vt_bstride)
+    return WAN_ERR_SHAPE;
+  AttnDesc a = attn(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk, 128, 0);
+  WAN_TRY(launch_attention(a, S(stream)));
+  return WAN_OK;
+}
+
+int wan_linear_fwd(const void *x, const void *w, const void *b, void *y, int M, int N, int K,
+                   int mode, void *stream) {
+  if (!x || !w || !y) return WAN_ERR_NULL;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 64) return WAN_ERR_SHAPE;
+  int kind = mode == 0 ? OUT_BF16 : mode == 1 ? OUT_F32 : mode == 2 ? OUT_GELU : -1;
+  if (kind < 0) return WAN_ERR_CONFIG;
+  WAN_TRY(launch_gemm(gemm(x, K, w, K, M, N, K, b, kind, y, N, 0), S(stream)));
+  return WAN_OK;
+}
+
+}  // extern "C"
