@@ -5,37 +5,47 @@
 // I2V 架构扩展 for the decoupled image attention).
 //
 // bf16 path (hd = 128), flash style with an online softmax:
-//  * a 256-thread workgroup owns 256 queries of one (batch, head); each
-//    wavefront owns 64 of them as two 32-query groups that share every K / V
-//    operand fragment read from LDS (halves the LDS traffic per MFMA);
+//  * a 512-thread workgroup owns 256 queries of one (batch, head): eight
+//    wavefronts of 32 queries, two per SIMD, so one wavefront's softmax
+//    (VALU) overlaps the other's matrix instructions;
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    a lane then holds 16 keys of ONE query, so the row max / row sum are
 //    per-lane reductions plus one exchange between lanes l and l^32;
-//  * O^T = V^T P^T: the probabilities are already in the B-operand layout,
-//    and V arrives transposed ([hd][key], written so by the projection GEMM),
-//    so the A operand is two 8-byte LDS reads per fragment;
-//  * K and V^T tiles of 64 keys are double-buffered in LDS; the next tile's
-//    global loads are in flight while the current one is processed;
+//  * O^T = V^T P^T: the probabilities are already in the B-operand layout.
+//    V arrives transposed ([hd][key], written so by the projection GEMM) and
+//    the LDS copy of a V^T tile stores its keys permuted so that the 8 keys
+//    one lane feeds to an MFMA are 16 contiguous bytes (one ds_read_b128);
+//  * K and V^T tiles of 64 keys are double-buffered in LDS with XOR
+//    swizzles that keep every 16-lane group of a 16-byte read on distinct
+//    banks; the next tile's global loads are in flight during the math;
 //  * the running max is only raised (and the accumulators rescaled) when a
 //    tile's max exceeds it by more than 2^8, so most tiles skip the rescale;
-//    probabilities stay <= 256, exact in the bf16 mantissa's relative sense.
+//    probabilities stay <= 256.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace wan {
 
 constexpr int AQ = 256;   // queries per workgroup
+constexpr int AW = 8;     // wavefronts per workgroup (32 queries each)
 constexpr int AK = 64;    // keys per tile
 constexpr int HD = 128;   // head dim
 constexpr float TAU = 8.0f;
 
-WAN_DEV int vswz(int row) { return (row & 15) ^ ((row >> 4) & 1); }
-
 WAN_DEV float other_half(float v) { return __shfl_xor(v, 32); }
 
-__global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnDesc a) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][AK * HD];   // [key][hd], 16B chunks ^ (key&15)
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][HD * AK];   // [hd][key], 8B units ^ vswz(hd)
+// V^T tile: row = hd (128 B = 64 keys). A lane group g of MFMA (j = 0..3,
+// 16 keys each) reads keys {16j + 4g .. +3} and {16j + 8 + 4g .. +3}; those two
+// 8-byte units are stored side by side in 16-byte chunk 2j + g.
+WAN_DEV int vunit_pos(int u) {           // 8-byte unit u = key/4 -> 8-byte slot
+  const int j = u >> 2, r = u & 3;
+  return 2 * (2 * j + (r & 1)) + (r >> 1);
+}
+WAN_DEV int vswz(int row) { return (row >> 1) & 7; }   // 16-byte chunk XOR for 128-byte rows
+
+__global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][AK * HD];   // [key][hd], chunk ^ (key & 15)
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][HD * AK];   // [hd][key perm], chunk ^ vswz(hd)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -50,45 +60,43 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnDesc a) {
   const bf16 *Vg = reinterpret_cast<const bf16 *>(a.vt);
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[q][st*16 + g*8 .. +8]
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const int row = qt * AQ + w * 64 + gi * 32 + l32;
-    const bool ok = row < Lq;
-    const bf16 *qp = Qg + (long)(b * Lq + (ok ? row : 0)) * a.ldq + h * HD + g * 8;
+  const int qrow = qt * AQ + w * 32 + l32;
+  bf16x8 qf[8];
+  {
+    const bool ok = qrow < Lq;
+    const bf16 *qp = Qg + (long)(b * Lq + (ok ? qrow : 0)) * a.ldq + h * HD + g * 8;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       uint4 v = ok ? ld16(qp + st * 16) : make_uint4(0, 0, 0, 0);
-      qf[gi][st] = *reinterpret_cast<bf16x8 *>(&v);
+      qf[st] = *reinterpret_cast<bf16x8 *>(&v);
     }
   }
 
-  f32x16 o[2][4];
+  f32x16 o[4];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[gi][t][r] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
   const float c = a.scale * 1.4426950408889634f;   // scores -> log2 units
 
-  // ---- tile loaders: K tile = 64 keys x 16 chunks; V^T tile = 128 rows x 8 chunks
-  uint4 rk[4], rv[4];
-  const int kkey = tid >> 4, kc = tid & 15;
-  const int vrow = tid >> 3, vc = tid & 7;
+  // ---- tile loaders: K tile = 64 keys x 16 chunks; V^T tile = 128 rows x 8 chunks;
+  // 512 threads, two chunks of each per thread
+  uint4 rk[2], rv[2];
+  const int kkey = tid >> 4, kc = tid & 15;        // key 0..31 (+32), chunk 0..15
+  const int vrow = tid >> 3, vc = tid & 7;         // row 0..63 (+64), chunk 0..7
   const long vbase = (long)b * a.vt_bstride;
   auto gload = [&](int j) {
     const int key0 = j * AK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kg = key0 + kkey + 16 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int kg = key0 + kkey + 32 * i;
       rk[i] = kg < Lk ? ld16(Kg + (long)(b * Lk + kg) * a.ldk + h * HD + kc * 8)
                       : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = vrow + 32 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int row = vrow + 64 * i;
       const int col = key0 + vc * 8;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (col < Lk) {
@@ -108,19 +116,30 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnDesc a) {
   };
   auto sstore = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kkey + 16 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int key = kkey + 32 * i;
       st16(&sK[st][key * HD + ((kc ^ (key & 15)) * 8)], rk[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = vrow + 32 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int row = vrow + 64 * i;
       const int f = vswz(row);
-      uint2 lo = make_uint2(rv[i].x, rv[i].y), hi = make_uint2(rv[i].z, rv[i].w);
-      *reinterpret_cast<uint2 *>(&sV[st][row * AK + (((2 * vc) ^ f) * 4)]) = lo;
-      *reinterpret_cast<uint2 *>(&sV[st][row * AK + (((2 * vc + 1) ^ f) * 4)]) = hi;
+      const int p0 = vunit_pos(2 * vc), p1 = vunit_pos(2 * vc + 1);   // 8-byte slots
+      bf16 *rp = &sV[st][row * AK];
+      *reinterpret_cast<uint2 *>(rp + ((((p0 >> 1) ^ f) << 3) | ((p0 & 1) << 2))) =
+          make_uint2(rv[i].x, rv[i].y);
+      *reinterpret_cast<uint2 *>(rp + ((((p1 >> 1) ^ f) << 3) | ((p1 & 1) << 2))) =
+          make_uint2(rv[i].z, rv[i].w);
     }
   };
+
+  // per-lane LDS read offsets (elements); tile / buffer offsets are added as constants
+  int koff[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) koff[st] = l32 * HD + (((st * 2 + g) ^ (l32 & 15)) * 8);
+  int voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) voff[j] = l32 * AK + (((2 * j + g) ^ vswz(l32)) * 8);
 
   const int ntiles = (Lk + AK - 1) / AK;
   gload(0);
@@ -130,24 +149,19 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnDesc a) {
   for (int j = 0; j < ntiles; ++j) {
     const int cur = j & 1;
     if (j + 1 < ntiles) gload(j + 1);
+    const bf16 *sk = sK[cur];
+    const bf16 *sv = sV[cur];
 
-    // ---- S^T = K Q^T for both query groups
-    f32x16 s[2][2];
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[gi][kb][r] = 0.f;
+    // ---- S^T = K Q^T: two 32-key blocks
+    f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = kb * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const int ch = st * 2 + g;
-        bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&sK[cur][key * HD + ((ch ^ (key & 15)) * 8)]);
-        s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][st], s[0][kb], 0, 0, 0);
-        s[1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[1][st], s[1][kb], 0, 0, 0);
+        bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sk + kb * 32 * HD + koff[st]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[kb], 0, 0, 0);
       }
     }
     // keys past Lk (last tile only)
@@ -157,82 +171,68 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnDesc a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j * AK + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          if (key >= Lk) { s[0][kb][r] = -INFINITY; s[1][kb][r] = -INFINITY; }
+          if (key >= Lk) s[kb][r] = -INFINITY;
         }
     }
 
-    // ---- online softmax, probabilities packed to bf16 in the B-operand layout
-    bf16x8 pb[2][2][2];
+    // ---- online softmax; probabilities packed to bf16 in the B-operand layout
+    float mx = s[0][0];
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      float mx = s[gi][0][0];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, other_half(mx));
+    const float mz = mx * c;
+    if (__builtin_amdgcn_ballot_w64(mz > m + TAU) != 0) {
+      const float mn = fmaxf(m, mz);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[gi][kb][r]);
-      mx = fmaxf(mx, other_half(mx));
-      const float mz = mx * c;
-      if (__builtin_amdgcn_ballot_w64(mz > m[gi] + TAU) != 0) {
-        const float mn = fmaxf(m[gi], mz);
-        const float alpha = __builtin_amdgcn_exp2f(m[gi] - mn);
-        l[gi] *= alpha;
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[gi][t][r] *= alpha;
-        m[gi] = mn;
-      }
-      const float nm = -m[gi];
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[gi][kb][r], c, nm));
-          ls += p;
-          pb[gi][kb][r >> 3][r & 7] = f2bf(p);
-        }
-      l[gi] += ls;
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      m = mn;
     }
+    const float nm = -m;
+    bf16x8 pb[2][2];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, nm));
+        ls += p;
+        pb[kb][r >> 3][r & 7] = f2bf(p);
+      }
+    l += ls;
 
     // ---- O^T += V^T P^T
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = t * 32 + l32;
-      const int f = vswz(row);
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const int ua = (kb * 32 + 16 * hf + g * 4) >> 2;   // 8-byte unit of 4 keys
-          uint2 lo = *reinterpret_cast<const uint2 *>(&sV[cur][row * AK + ((ua ^ f) * 4)]);
-          uint2 hi = *reinterpret_cast<const uint2 *>(&sV[cur][row * AK + (((ua + 2) ^ f) * 4)]);
-          uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          bf16x8 va = *reinterpret_cast<bf16x8 *>(&vv);
-          o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[0][kb][hf], o[0][t], 0, 0, 0);
-          o[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[1][kb][hf], o[1][t], 0, 0, 0);
+          bf16x8 va = *reinterpret_cast<const bf16x8 *>(sv + t * 32 * AK + voff[2 * kb + hf]);
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][hf], o[t], 0, 0, 0);
         }
-    }
 
     if (j + 1 < ntiles) sstore(cur ^ 1);
     __syncthreads();
   }
 
   // ---- normalise and store: lane holds O^T[hd = t*32 + (r/4)*8 + g*4 + r%4][q = l32]
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const float lt = l[gi] + other_half(l[gi]);
-    const float inv = 1.0f / lt;
-    const int row = qt * AQ + w * 64 + gi * 32 + l32;
-    if (row >= Lq) continue;
-    const long orow = (long)(b * Lq + row);
+  const float lt = l + other_half(l);
+  const float inv = 1.0f / lt;
+  if (qrow < Lq) {
+    const long orow = (long)(b * Lq + qrow);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int hd0 = t * 32 + rb * 8 + g * 4;
-        float v0 = o[gi][t][rb * 4 + 0] * inv, v1 = o[gi][t][rb * 4 + 1] * inv;
-        float v2 = o[gi][t][rb * 4 + 2] * inv, v3 = o[gi][t][rb * 4 + 3] * inv;
+        float v0 = o[t][rb * 4 + 0] * inv, v1 = o[t][rb * 4 + 1] * inv;
+        float v2 = o[t][rb * 4 + 2] * inv, v3 = o[t][rb * 4 + 3] * inv;
         if (a.out_mode == 1) {
           *reinterpret_cast<float4 *>(a.acc32 + orow * (a.H * HD) + h * HD + hd0) =
               make_float4(v0, v1, v2, v3);
@@ -310,7 +310,7 @@ hipError_t launch_attention(const AttnDesc &a, hipStream_t s) {
   }
   if (a.hd != HD) return hipErrorInvalidValue;
   const int nqt = (a.Lq + AQ - 1) / AQ;
-  k_attn_bf16<<<a.B * a.H * nqt, 256, 0, s>>>(a);
+  k_attn_bf16<<<a.B * a.H * nqt, AW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
