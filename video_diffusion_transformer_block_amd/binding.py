@@ -14,7 +14,8 @@ from typing import Dict, Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwandit.so")
+# WANDIT_LIB may point at another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("WANDIT_LIB") or os.path.join(_HERE, "libwandit.so")
 
 WAN_F32, WAN_BF16 = 0, 1
 

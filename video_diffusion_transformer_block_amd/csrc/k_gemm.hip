@@ -5,21 +5,298 @@
 // ("Wan: Open and Advanced Large-Scale Video Generative Models (Wan 2.1)",
 // table 配置表 for the widths), patchify as a GEMM over gathered patches.
 //
-// bf16 path: 256x256x64 block tile, 4 wavefronts in a 2x2 grid, each owning a
-// 128x128 tile of 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per
-// lane).  A and B tiles are staged through LDS with a 16-byte-chunk XOR
-// swizzle so that the 32 rows an MFMA operand read touches land in distinct
-// banks; global loads for the next K tile are in flight while the current
-// one is multiplied (two LDS stages, one barrier per K tile).
+// bf16 path: 256x256x64 block tile, 8 wavefronts (two per SIMD) in a 2x4
+// grid, each owning a 128x64 tile of 4x2 v_mfma_f32_32x32x16_bf16
+// accumulators.  A and B tiles go global -> LDS directly
+// (buffer_load_dwordx4 ... lds) into a 16-byte-chunk XOR swizzle that keeps the
+// 16 lanes one ds_read_b128 cycle serves on distinct banks.  The K loop is
+// software-pipelined: the LDS reads of the next k-substep are interleaved
+// with the MFMAs of the current one, and the last substep's MFMAs run across
+// the stage switch while the next stage's first fragments and the loads two
+// K tiles ahead are issued (two LDS stages, one barrier per K tile).  Tail rows / columns
+// load a clamped (in-bounds) row and are never stored.  Tiles are visited in
+// groups of 8 M-tiles so that the 32 workgroups an XCD runs at once share A
+// and B slices in that XCD's L2.  The epilogue goes through LDS so every
+// lane stores 16 contiguous bytes of one output row.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace wan {
 
-constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GBM = 256, GBN = 256;
+constexpr int GBK = 64, NSTAGE = 2;     // K tile 64 (four MFMA k-substeps), two LDS stages
+constexpr int GW = 8;            // wavefronts per workgroup (two per SIMD)
+constexpr int GROUP_M = 8;       // M-tiles per L2 group
 
-WAN_DEV int swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// 16-byte chunk XOR swizzle of a tile row of CH chunks: the 16 rows one
+// ds_read_b128 cycle touches land on distinct (256-byte-period) bank groups
+template <int CH> WAN_DEV int swz_row(int row);
+template <> WAN_DEV int swz_row<8>(int row) { return (row >> 1) & 7; }   // 128-byte rows
+template <> WAN_DEV int swz_row<4>(int row) { return (row >> 2) & 3; }   // 64-byte rows
 
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), N <= 15: direct loads older than the last N
+// have landed and every LDS read of this wavefront has returned
+template <int N> WAN_DEV void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0070 | N); }
+
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+  static WAN_DEV void load(const bf16 *p, float *v) {
+    uint4 u = ld16(p);
+    const bf16 *e = reinterpret_cast<const bf16 *>(&u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)e[i];
+  }
+  static WAN_DEV void store(bf16 *p, const float *v) {
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = f2bf(v[i]);
+    *reinterpret_cast<bf16x8 *>(p) = o;
+  }
+};
+
+// Epilogue on 8 consecutive columns n..n+7 of row m (n + 8 <= N and 16-byte
+// aligned rows), or element-wise for a ragged column tail.
+template <int KIND, bool BROWS>
+WAN_DEV void epi8(const GemmDesc &g, int m, int n, float *v) {
+  const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
+  const bool full = n + 8 <= g.N;
+  if (bias) {
+    if (BROWS) {
+      const float bb = (float)bias[m];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += bb;
+    } else if (full) {
+      float bv[8];
+      Vec8<bf16>::load(bias + n, bv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += bv[i];
+    } else {
+      for (int i = 0; i < 8 && n + i < g.N; ++i) v[i] += (float)bias[n + i];
+    }
+  }
+  if (KIND == OUT_GELU) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = gelu_tanh(v[i]);
+  }
+  if (KIND == OUT_BF16 || KIND == OUT_GELU) {
+    bf16 *c = reinterpret_cast<bf16 *>(g.C) + (long)m * g.ldc + n;
+    if (full) Vec8<bf16>::store(c, v);
+    else for (int i = 0; i < 8 && n + i < g.N; ++i) c[i] = f2bf(v[i]);
+  } else if (KIND == OUT_F32) {
+    float *c = reinterpret_cast<float *>(g.C) + (long)m * g.ldc + n;
+    if (full) {
+      *reinterpret_cast<float4 *>(c) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4 *>(c + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      for (int i = 0; i < 8 && n + i < g.N; ++i) c[i] = v[i];
+    }
+  } else {  // OUT_RESID: x += gate * v
+    float *xp = g.X + (long)m * g.ldx + n;
+    const float *gp = g.gate ? g.gate + (long)(m / g.rows_per_batch) * g.gate_bstride + n : nullptr;
+    if (full) {
+      float4 x0 = *reinterpret_cast<float4 *>(xp), x1 = *reinterpret_cast<float4 *>(xp + 4);
+      if (gp) {
+        float4 g0 = *reinterpret_cast<const float4 *>(gp), g1 = *reinterpret_cast<const float4 *>(gp + 4);
+        x0.x += g0.x * v[0]; x0.y += g0.y * v[1]; x0.z += g0.z * v[2]; x0.w += g0.w * v[3];
+        x1.x += g1.x * v[4]; x1.y += g1.y * v[5]; x1.z += g1.z * v[6]; x1.w += g1.w * v[7];
+      } else {
+        x0.x += v[0]; x0.y += v[1]; x0.z += v[2]; x0.w += v[3];
+        x1.x += v[4]; x1.y += v[5]; x1.z += v[6]; x1.w += v[7];
+      }
+      *reinterpret_cast<float4 *>(xp) = x0;
+      *reinterpret_cast<float4 *>(xp + 4) = x1;
+    } else {
+      for (int i = 0; i < 8 && n + i < g.N; ++i) xp[i] += (gp ? gp[i] : 1.0f) * v[i];
+    }
+  }
+}
+
+template <int KIND, bool BROWS>
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
+  constexpr int CH = GBK / 8;                 // 16-byte chunks per tile row
+  constexpr int RPB = 1024 / (GBK * 2);       // rows per 1-KB direct-load block
+  constexpr int BPW = GBM / RPB / GW;         // blocks per wavefront per operand tile
+  constexpr int KS = GBK / 16;                // MFMA k-substeps per K tile
+  constexpr int LPT = 2 * BPW;                // direct loads per wavefront per K tile
+  __shared__ __attribute__((aligned(16))) bf16 smem[NSTAGE * (GBM + GBN) * GBK];
+  bf16 *sA = smem;                            // [stage][256][GBK]
+  bf16 *sB = smem + NSTAGE * GBM * GBK;       // [stage][256][GBK]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 2, wn = w & 3;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int tiles_m = (g.M + GBM - 1) / GBM;
+  const int tiles_n = (g.N + GBN - 1) / GBN;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int group = GROUP_M * tiles_n;
+  const int first_m = (bid / group) * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (bid % group) % gm;
+  const int tn = (bid % group) / gm;
+  const int m0 = tm * GBM, n0 = tn * GBN;
+  const bf16 *A = reinterpret_cast<const bf16 *>(g.A);
+  const bf16 *Bm = reinterpret_cast<const bf16 *>(g.B);
+
+  // global -> LDS, direct (buffer_load_dwordx4 ... lds): wavefront w fills the
+  // 1-KB blocks w*BPW .. of each tile; lane i lands at block base + 16 i =
+  // row blk*RPB + i/CH, physical chunk i%CH, so it fetches the logical chunk
+  // (i%CH) ^ swz(row) of that row.
+  // buffer descriptors over A and B (byte sizes < 4 GiB, checked on the host);
+  // per-lane byte offsets of the (clamped, so always in-range) rows
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)A, 0, (int)((unsigned)g.M * (unsigned)g.lda * 2u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)Bm, 0, (int)((unsigned)g.N * (unsigned)g.ldb * 2u), 0x00020000);
+  int oa[BPW], ob[BPW];
+#pragma unroll
+  for (int r = 0; r < BPW; ++r) {
+    const int row = (w * BPW + r) * RPB + lane / CH;
+    const int c = (lane % CH) ^ swz_row<CH>(row);
+    oa[r] = (int)(((unsigned)min(m0 + row, g.M - 1) * (unsigned)g.lda + c * 8) * 2u);
+    ob[r] = (int)(((unsigned)min(n0 + row, g.N - 1) * (unsigned)g.ldb + c * 8) * 2u);
+  }
+  auto gload = [&](int kt, int st) {
+    const int k0b = kt * GBK * 2;      // byte offset of the K tile (scalar)
+    bf16 *da = sA + st * GBM * GBK + w * BPW * 512;
+    bf16 *db = sB + st * GBN * GBK + w * BPW * 512;
+#pragma unroll
+    for (int r = 0; r < BPW; ++r) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(da + r * 512), 16, oa[r], k0b, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(db + r * 512), 16, ob[r], k0b, 0, 0);
+    }
+  };
+
+  // fragment offsets (elements) for k-substep ks: chunk ks*2 + half; the
+  // row swizzle only depends on l32 (row offsets are multiples of 32)
+  int aoff[KS], boff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    aoff[ks] = (wm * 128 + l32) * GBK + (((ks * 2 + half) ^ swz_row<CH>(l32)) * 8);
+    boff[ks] = (wn * 64 + l32) * GBK + (((ks * 2 + half) ^ swz_row<CH>(l32)) * 8);
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fragment registers: three slots, so the LDS reads of substep u+2 are in
+  // flight while substep u is multiplied (slot of substep u = u mod 3)
+  bf16x8 fa[3][4], fb[3][2];
+  auto frags = [&](int st, int ks, int slot) {
+    const bf16 *a_s = sA + st * GBM * GBK;
+    const bf16 *b_s = sB + st * GBN * GBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8 *>(a_s + aoff[ks] + i * 32 * GBK);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8 *>(b_s + boff[ks] + j * 32 * GBK);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+  };
+  // scheduling hint: one MFMA, one LDS read, alternately (6 reads), then 2 MFMAs
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+
+  const int KT = g.K / GBK;
+  // prologue: tiles 0 .. NSTAGE-1 in flight (one per stage); wait for tile 0
+#pragma unroll
+  for (int p = 0; p < NSTAGE; ++p)
+    if (p < KT) gload(p, p);
+  if (KT >= NSTAGE) wait_vm<(NSTAGE - 1) * LPT>();
+  else wait_vm<0>();
+  __syncthreads();
+  frags(0, 0, 0);
+  frags(0, 1, 1);
+
+  // One K tile (KS == 4 substeps); `sb` = slot of its substep 0 (= kt mod 3).
+  // Substeps 0, 1 read the stage's substeps 2, 3; then, once every read of
+  // this stage is issued, the barrier; substeps 2, 3 read the next stage's
+  // substeps 0, 1 and the freed stage receives tile kt + NSTAGE.
+  auto tile = [&](int kt, int sb) {
+    const int st = kt % NSTAGE, nst = (kt + 1) % NSTAGE;
+    frags(st, 2, (sb + 2) % 3);
+    mfmas(sb);
+    interleave();
+    frags(st, 3, sb);          // slot of substep 3 == slot of substep 0 (its MFMAs are issued)
+    mfmas((sb + 1) % 3);
+    interleave();
+    if (kt + NSTAGE - 1 <= KT - 1) wait_vm<(NSTAGE - 2) * LPT>();
+    else wait_vm<0>();
+    __syncthreads();
+    if (kt + NSTAGE < KT) gload(kt + NSTAGE, st);
+    // next stage's substeps 0, 1 (on the last tile a harmless, unused read)
+    frags(nst, 0, (sb + 1) % 3);
+    mfmas((sb + 2) % 3);
+    interleave();
+    frags(nst, 1, (sb + 2) % 3);
+    mfmas(sb);
+    interleave();
+  };
+  int kt = 0;
+  for (; kt + 3 <= KT; kt += 3) {   // three tiles: 12 substeps, slots cycle back to 0
+    tile(kt, 0);
+    tile(kt + 1, 1);
+    tile(kt + 2, 2);
+  }
+  if (kt < KT) tile(kt, 0);
+  if (kt + 1 < KT) tile(kt + 1, 1);
+
+  // ---- epilogue through LDS: per wave 4 slabs of 32 rows x 64 columns (fp32, padded rows)
+  __syncthreads();
+  constexpr int EP = 68;
+  float *ep = reinterpret_cast<float *>(smem) + w * 32 * EP;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    {
+      const int jh = 0;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = (r >> 2) * 8 + half * 4 + (r & 3);
+          ep[row * EP + jj * 32 + l32] = acc[i][jj][r];
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
+      __builtin_amdgcn_wave_barrier();
+      const int row = lane >> 1, cb = (lane & 1) * 32;
+      const int m = m0 + wm * 128 + i * 32 + row;
+      if (m < g.M) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * 64 + jh * 64 + cb + q * 8;
+          if (n < g.N) {
+            float v[8];
+            const float4 u0 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8);
+            const float4 u1 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8 + 4);
+            v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+            v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+            epi8<KIND, BROWS>(g, m, n, v);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+// per-element epilogue (float32 path)
 template <int KIND, bool BROWS, typename T>
 WAN_DEV void epi_one(const GemmDesc &g, int m, int n, float v) {
   if (g.bias) v += to_f<T>(reinterpret_cast<const T *>(g.bias)[BROWS ? m : n]);
@@ -35,103 +312,6 @@ WAN_DEV void epi_one(const GemmDesc &g, int m, int n, float v) {
     float *xp = g.X + (long)m * g.ldx + n;
     *xp = *xp + gt * v;
   }
-}
-
-template <int KIND, bool BROWS>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmDesc g) {
-  __shared__ __attribute__((aligned(16))) bf16 sA[2][GBM * GBK];
-  __shared__ __attribute__((aligned(16))) bf16 sB[2][GBN * GBK];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int tiles_n = (g.N + GBN - 1) / GBN;
-  const int tiles_m = (g.M + GBM - 1) / GBM;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  // consecutive logical tiles walk down M inside one N column strip, so the
-  // tiles resident on one XCD share their B (weight) strip in L2
-  const int tn = bid / tiles_m, tm = bid % tiles_m;
-  (void)tiles_n;
-  const int m0 = tm * GBM, n0 = tn * GBN;
-  const bf16 *A = reinterpret_cast<const bf16 *>(g.A);
-  const bf16 *Bm = reinterpret_cast<const bf16 *>(g.B);
-
-  // global -> register staging: 8 chunks of A and 8 of B per thread
-  const int lrow = tid >> 3, lc = tid & 7;
-  uint4 ra[8], rb[8];
-  auto gload = [&](int kt) {
-    const int k0 = kt * GBK + lc * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int r = lrow + 32 * i;
-      int gm = m0 + r, gn = n0 + r;
-      ra[i] = gm < g.M ? ld16(A + (long)gm * g.lda + k0) : make_uint4(0, 0, 0, 0);
-      rb[i] = gn < g.N ? ld16(Bm + (long)gn * g.ldb + k0) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int r = lrow + 32 * i;
-      int off = r * GBK + ((lc ^ swz8(r)) * 8);
-      st16(&sA[st][off], ra[i]);
-      st16(&sB[st][off], rb[i]);
-    }
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int KT = g.K / GBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  const int arow0 = wm * 128 + (lane & 31);
-  const int brow0 = wn * 128 + (lane & 31);
-  const int half = lane >> 5;
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int c = ks * 2 + half;
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int r = arow0 + i * 32;
-        a[i] = *reinterpret_cast<const bf16x8 *>(&sA[st][r * GBK + ((c ^ swz8(r)) * 8)]);
-        int q = brow0 + i * 32;
-        b[i] = *reinterpret_cast<const bf16x8 *>(&sB[st][q * GBK + ((c ^ swz8(q)) * 8)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) sstore(st ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds C[row = (r/4)*8 + half*4 + r%4][col = lane%32] of each 32x32 tile
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 128 + j * 32 + (lane & 31);
-      if (n >= g.N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        if (m < g.M) epi_one<KIND, BROWS, bf16>(g, m, n, acc[i][j][r]);
-      }
-    }
 }
 
 // float32 path (small fp32 workloads): 64x64 tile, 4x4 outputs per thread.
@@ -183,13 +363,16 @@ static void gemm_go(const GemmDesc &g, hipStream_t s) {
     k_gemm_f32<KIND, BROWS><<<blocks, 256, 0, s>>>(g);
   } else {
     int blocks = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
-    k_gemm_bf16<KIND, BROWS><<<blocks, 256, 0, s>>>(g);
+    k_gemm_bf16<KIND, BROWS><<<blocks, GW * 64, 0, s>>>(g);
   }
 }
 
 hipError_t launch_gemm(const GemmDesc &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (!g.f32 && (g.K % GBK)) return hipErrorInvalidValue;
+  // the bf16 kernel addresses A and B with 32-bit byte offsets
+  if (!g.f32 && ((long)g.M * g.lda * 2 >= (1L << 31) || (long)g.N * g.ldb * 2 >= (1L << 31)))
+    return hipErrorInvalidValue;
   const bool br = g.bias_rows != 0;
   switch (g.kind) {
     case OUT_BF16: br ? gemm_go<OUT_BF16, true>(g, s) : gemm_go<OUT_BF16, false>(g, s); break;
