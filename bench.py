@@ -59,7 +59,7 @@ def cpu_baseline(work, inp, tw, bw, budget_s: float = 25.0):
     m_vec = O.tmlp(inp["t"], tw["w1"], tw["b1"], tw["w2"], tw["b2"])
     rng = np.random.default_rng(0)
     times = {}
-    for r in (128, 640):
+    for r in (1024, 4096):
         rows = np.sort(rng.choice(L, size=r, replace=False))
         t0 = time.perf_counter()
         O.block(inp["x"], m_vec, bw, inp["ctx"], m.heads, m.eps, rows=rows)

@@ -34,6 +34,8 @@ constexpr float TAU = 8.0f;
 
 WAN_DEV float other_half(float v) { return __shfl_xor(v, 32); }
 
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
 // V^T tile: row = hd (128 B = 64 keys). A lane group g of MFMA (j = 0..3,
 // 16 keys each) reads keys {16j + 4g .. +3} and {16j + 8 + 4g .. +3}; those two
 // 8-byte units are stored side by side in 16-byte chunk 2j + g.
@@ -82,26 +84,40 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
 
   // ---- tile loaders: K tile = 64 keys x 16 chunks; V^T tile = 128 rows x 8 chunks;
   // 512 threads, two chunks of each per thread
-  uint4 rk[2], rv[2];
-  const int kkey = tid >> 4, kc = tid & 15;        // key 0..31 (+32), chunk 0..15
+  uint4 rv[2];
   const int vrow = tid >> 3, vc = tid & 7;         // row 0..63 (+64), chunk 0..7
   const long vbase = (long)b * a.vt_bstride;
-  auto gload = [&](int j) {
-    const int key0 = j * AK;
+  // K tile: global -> LDS directly (buffer_load_dwordx4 ... lds).  The tile is
+  // 16 blocks of 1 KB (4 keys each); wavefront w fills blocks 2w, 2w+1; lane i
+  // lands at key blk*4 + i/16, physical chunk i%16 and fetches the logical
+  // chunk (i%16) ^ (key & 15).  The descriptor spans exactly this batch's Lk
+  // key rows, so rows past Lk read as zero.
+  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(Kg + (long)b * Lk * a.ldk), 0, (int)((unsigned)Lk * (unsigned)a.ldk * 2u), 0x00020000);
+  int kvoff[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int kg = key0 + kkey + 32 * i;
-      rk[i] = kg < Lk ? ld16(Kg + (long)(b * Lk + kg) * a.ldk + h * HD + kc * 8)
-                      : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int key = (w * 2 + i) * 4 + (lane >> 4);
+    const int chunk = (lane & 15) ^ (key & 15);
+    kvoff[i] = (key * (int)a.ldk + h * HD + chunk * 8) * 2;
+  }
+  auto gloadK = [&](int j, int st) {
+    const int rowb = j * AK * (int)a.ldk * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr)(&sK[st][(w * 2 + i) * 512]), 16,
+                                               kvoff[i] + rowb, 0, 0, 0);
+  };
+  auto gloadV = [&](int j, bool ragged) {   // ragged: tile j may reach past Lk
+    const int key0 = j * AK;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = vrow + 64 * i;
       const int col = key0 + vc * 8;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (col < Lk) {
+      if (!ragged || col < Lk) {
         v = ld16(Vg + (long)(h * HD + row) * a.ldv + vbase + col);
-        if (col + 8 > Lk) {   // ragged tail: clear keys >= Lk (their memory is padding)
+        if (ragged && col + 8 > Lk) {   // ragged tail: clear keys >= Lk (their memory is padding)
           uint32_t *e = reinterpret_cast<uint32_t *>(&v);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -114,12 +130,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
       rv[i] = v;
     }
   };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int key = kkey + 32 * i;
-      st16(&sK[st][key * HD + ((kc ^ (key & 15)) * 8)], rk[i]);
-    }
+  auto sstoreV = [&](int st) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = vrow + 64 * i;
@@ -142,18 +153,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
   for (int j = 0; j < 4; ++j) voff[j] = l32 * AK + (((2 * j + g) ^ vswz(l32)) * 8);
 
   const int ntiles = (Lk + AK - 1) / AK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
-    const bf16 *sk = sK[cur];
-    const bf16 *sv = sV[cur];
-
-    // ---- S^T = K Q^T: two 32-key blocks
-    f32x16 s[2];
+  // S^T tile j from K buffer kb (two 32-key blocks)
+  auto qk = [&](const bf16 *sk, f32x16 *s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -164,7 +166,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[kb], 0, 0, 0);
       }
     }
-    // keys past Lk (last tile only)
+  };
+  // keys past Lk -> -inf (last tile only)
+  auto mask_tail = [&](f32x16 *s, int j) {
     if ((j + 1) * AK > Lk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -174,14 +178,18 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
           if (key >= Lk) s[kb][r] = -INFINITY;
         }
     }
-
-    // ---- online softmax; probabilities packed to bf16 in the B-operand layout
+  };
+  // row max of a score tile, merged across the two lane halves
+  auto rowmax = [&](const f32x16 *s) -> float {
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, other_half(mx));
+    return fmaxf(mx, other_half(mx));
+  };
+  // raise the running max only when the tile's max exceeds it by more than 2^TAU
+  auto rescale = [&](float mx) {
     const float mz = mx * c;
     if (__builtin_amdgcn_ballot_w64(mz > m + TAU) != 0) {
       const float mn = fmaxf(m, mz);
@@ -193,32 +201,120 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
         for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
       m = mn;
     }
+  };
+  // probabilities of a tile, bf16 in the B-operand layout, and their row sum
+  // (the row sum adds the bf16-rounded probabilities, two per v_dot2 with
+  //  (1, 1): the normaliser then matches exactly the weights the PV MFMA uses)
+  auto probs = [&](const f32x16 *s, bf16x8 (&pb)[2][2]) {
     const float nm = -m;
-    bf16x8 pb[2][2];
-    float ls = 0.f;
+    bf16x2 one;
+    one[0] = (bf16)1.0f; one[1] = (bf16)1.0f;
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, nm));
-        ls += p;
-        pb[kb][r >> 3][r & 7] = f2bf(p);
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pb[kb][hf][e] = f2bf(__builtin_amdgcn_exp2f(fmaf(s[kb][hf * 8 + e], c, nm)));
+        const bf16x2 *pp = reinterpret_cast<const bf16x2 *>(&pb[kb][hf]);
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[0], one, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[1], one, ls1, false);
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[2], one, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[3], one, ls1, false);
       }
-    l += ls;
-
-    // ---- O^T += V^T P^T
+    l += ls0 + ls1;
+  };
+  // O^T += V^T P^T
+  auto pv = [&](const bf16 *sv, const bf16x8 (&pb)[2][2]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        for (int t = 0; t < 4; ++t) {
           bf16x8 va = *reinterpret_cast<const bf16x8 *>(sv + t * 32 * AK + voff[2 * kb + hf]);
           o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][hf], o[t], 0, 0, 0);
         }
+  };
 
-    if (j + 1 < ntiles) sstore(cur ^ 1);
+  // Pipeline: K runs one tile ahead of V.  At the top of iteration j the LDS
+  // holds K(j+1) in sK[(j+1)&1] and V(j) in sV[j&1]; S(j) and its row max are
+  // in registers.  Iteration j: (rare) rescale; the S(j+1) MFMAs interleaved
+  // with the exponentials of tile j; the PV(j) MFMAs interleaved with the row
+  // max of S(j+1); the staged V(j+1) and the directly loaded K(j+2) land in
+  // the buffers freed in iteration j-1; one barrier.
+  gloadK(0, 0);
+  if (ntiles > 1) gloadK(1, 1);
+  gloadV(0, ntiles == 1);
+  sstoreV(0);
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(0), K(1) landed
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  qk(sK[0], sa);
+  mask_tail(sa, 0);
+  const float mxa = rowmax(sa);
+  __syncthreads();   // every wavefront has read K(0): its buffer may be refilled
+
+  // one pipelined iteration; tile j+1 exists
+  // (load_k2: tile j+2 exists; mask_next: tile j+1 is the last, possibly ragged,
+  //  tile; both are constants at every call site, so no branch stays in the loop)
+  auto step = [&](int j, f32x16 *scur, float mxcur, f32x16 *snxt, bool load_k2,
+                  bool mask_next) -> float {
+    if (load_k2) gloadK(j + 2, j & 1);   // buffer of K(j), read in iteration j-1
+    gloadV(j + 1, mask_next);
+    rescale(mxcur);
+    bf16x8 pb[2][2];
+    // matrix unit: next scores; vector unit: this tile's probabilities
+    qk(sK[(j + 1) & 1], snxt);
+    probs(scur, pb);
+    // LDS reads run four MFMAs ahead of their use; VALU fills the MFMA shadow
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      if (q < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
+    }
+    if (mask_next) mask_tail(snxt, j + 1);
+    // matrix unit: PV of this tile; vector unit: row max of the next scores
+    pv(sV[j & 1], pb);
+    const float mxn = rowmax(snxt);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (q < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    sstoreV((j + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(j+2) landed, LDS reads done
     __syncthreads();
+    return mxn;
+  };
+  // the last tile: no next scores
+  auto last = [&](int j, f32x16 *scur, float mxcur) {
+    rescale(mxcur);
+    bf16x8 pb[2][2];
+    probs(scur, pb);
+    pv(sV[j & 1], pb);
+  };
+  int j = 0;
+  float mx = mxa;
+  for (; j + 3 < ntiles; j += 2) {     // unrolled by two (score buffers alternate); never
+    mx = step(j, sa, mx, sb, true, false);       // computes the last tile's scores
+    mx = step(j + 1, sb, mx, sa, true, false);
+  }
+  const int rem = ntiles - j;          // 1, 2 or 3 tiles left; the current scores are in sa
+  if (rem == 3) {
+    mx = step(j, sa, mx, sb, true, false);
+    mx = step(j + 1, sb, mx, sa, false, true);
+    last(j + 2, sa, mx);
+  } else if (rem == 2) {
+    mx = step(j, sa, mx, sb, false, true);
+    last(j + 1, sb, mx);
+  } else {
+    last(j, sa, mx);
   }
 
   // ---- normalise and store: lane holds O^T[hd = t*32 + (r/4)*8 + g*4 + r%4][q = l32]
@@ -309,6 +405,8 @@ hipError_t launch_attention(const AttnDesc &a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.hd != HD) return hipErrorInvalidValue;
+  // K rows are addressed through a buffer descriptor with 32-bit byte offsets
+  if ((long)a.Lk * a.ldk * 2 >= (1L << 31)) return hipErrorInvalidValue;
   const int nqt = (a.Lq + AQ - 1) / AQ;
   k_attn_bf16<<<a.B * a.H * nqt, AW * 64, 0, s>>>(a);
   return hipGetLastError();
