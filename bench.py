@@ -59,7 +59,7 @@ def cpu_baseline(work, inp, tw, bw, budget_s: float = 25.0):
     m_vec = O.tmlp(inp["t"], tw["w1"], tw["b1"], tw["w2"], tw["b2"])
     rng = np.random.default_rng(0)
     times = {}
-    for r in (1024, 4096):
+    for r in (2048, 8192):
         rows = np.sort(rng.choice(L, size=r, replace=False))
         t0 = time.perf_counter()
         O.block(inp["x"], m_vec, bw, inp["ctx"], m.heads, m.eps, rows=rows)
@@ -75,6 +75,25 @@ def cpu_baseline(work, inp, tw, bw, budget_s: float = 25.0):
                       f"{full:.1f}s extrapolated linearly in the row count"}
 
 
+def traffic_pass(W, B, L, d, H, dev):
+    """Kernels for the HBM-traffic counters: the self-attention launch of the
+    workload and, as the calibration reference, a plain copy of 512 MiB
+    (reads 512 MiB, writes 512 MiB)."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(7)
+    qk = (torch.randn((B * L, 2 * d), generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    Lp = (L + 63) // 64 * 64
+    vt = torch.randn((d, B * Lp), generator=g).to(torch.bfloat16).to(dev)
+    o = torch.empty((B * L, d), dtype=torch.bfloat16, device=dev)
+    src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        W.attention_fwd(qk, 2 * d, qk[:, d:], 2 * d, vt, B * Lp, Lp, o, d, B, H, L, L)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_pass": "done", "copy_bytes": 512 << 20}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,7 +101,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", type=int, default=2, help="block workload id (2: 1.3B, 4: 14B)")
+    ap.add_argument("--traffic-pass", action="store_true",
+                    help="only run 3 self-attention launches and 3 plain 512-MiB device copies "
+                         "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and their calibration)")
     args = ap.parse_args()
+    if args.traffic_pass:
+        args.no_cpu_baseline = True
+        args.warmup, args.steps = 1, 1
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
@@ -141,6 +166,9 @@ def main():
     if not all(math.isfinite(v) for v in x[0, :4, :4].flatten().tolist()):
         raise RuntimeError("non-finite block output")
 
+    if args.traffic_pass:
+        traffic_pass(W, B, L, d, H, dev)
+        return
     # ---- the dominant kernel (self-attention), timed on its own stream with HIP events
     hd = d // H
     g = torch.Generator(device="cpu").manual_seed(7)
