@@ -298,3 +298,57 @@ def linear_inputs(seed: int, M: int, N: int, K: int):
     w = bf16_round(g.standard_normal((N, K), dtype=np.float32) / np.float32(np.sqrt(K)))
     b = bf16_round(g.standard_normal((N,), dtype=np.float32))
     return x, w, b
+
+
+# ----------------------------------------------------------------------------
+# On-device seeded weights for the full-size step checks that compare the GPU
+# path with itself (batch independence, zero extra projection, determinism):
+# the 14B model's 16 G parameters would take minutes to draw on the host.
+
+def _dev_gen(device, cid: int, tensor: str, block: int = 0):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([2025, cid, TID[tensor], block, 7]).generate_state(1)[0]))
+    return g
+
+
+def device_model_weights(w: Workload, device="cuda"):
+    """Model weights of workload ``w`` drawn on the device (bf16 values of
+    N(0, 0.02); per-block modulation bias float32), in the layout the C ABI
+    takes.  The I2V patchify weight has its extra input channels zero."""
+    import torch
+    m, c = w.model, w.cid
+    d, F = m.dim, m.ffn
+    dt = torch.bfloat16 if m.dtype == "bf16" else torch.float32
+
+    def rn(tensor, shape, block=0, dtype=dt):
+        g = _dev_gen(device, c, tensor, block)
+        return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * WEIGHT_STD).to(dtype)
+
+    pw = rn("patch_w", (d, 16 * 4))
+    if m.in_ch > 16:
+        pw = torch.cat([pw, torch.zeros((d, (m.in_ch - 16) * 4), dtype=dt, device=device)], dim=1)
+    out = {"patch_w": pw.contiguous(), "patch_b": rn("patch_b", (d,)),
+           "head_w": rn("head_w", (m.out_ch * 4, d)), "head_b": rn("head_b", (m.out_ch * 4,)),
+           "tmlp": {"w1": rn("tmlp_w1", (d, m.freq_dim)), "b1": rn("tmlp_b1", (d,)),
+                    "w2": rn("tmlp_w2", (6 * d, d)), "b2": rn("tmlp_b2", (6 * d,))}}
+    if m.img_len:
+        out["img"] = {"w1": rn("img_w1", (d, m.img_feat)), "b1": rn("img_b1", (d,)),
+                      "w2": rn("img_w2", (d, d)), "b2": rn("img_b2", (d,)),
+                      "w3": rn("img_w3", (d, d)), "b3": rn("img_b3", (d,))}
+    blocks = []
+    for i in range(m.n_blocks):
+        b = {"sa_wqkv": rn("sa_wqkv", (3 * d, d), i), "sa_bqkv": rn("sa_bqkv", (3 * d,), i),
+             "sa_wo": rn("sa_wo", (d, d), i), "sa_bo": rn("sa_bo", (d,), i),
+             "ca_wq": rn("ca_wq", (d, d), i), "ca_bq": rn("ca_bq", (d,), i),
+             "ca_wkv": rn("ca_wkv", (2 * d, d), i), "ca_bkv": rn("ca_bkv", (2 * d,), i),
+             "ca_wo": rn("ca_wo", (d, d), i), "ca_bo": rn("ca_bo", (d,), i),
+             "ffn_w1": rn("ffn_w1", (F, d), i), "ffn_b1": rn("ffn_b1", (F,), i),
+             "ffn_w2": rn("ffn_w2", (d, F), i), "ffn_b2": rn("ffn_b2", (d,), i),
+             "mod_bias": rn("mod_bias", (6 * d,), i, dtype=torch.float32)}
+        if m.img_len:
+            b["ca_wkv_img"] = rn("ca_wkv_img", (2 * d, d), i)
+            b["ca_bkv_img"] = rn("ca_bkv_img", (2 * d,), i)
+        blocks.append(b)
+    out["blocks"] = blocks
+    return out
