@@ -159,9 +159,11 @@ int wan_i2v_mask(const uint8_t *frame_mask, int n_frames, int lat_f, int H8, int
  *   q  [B, Lq, *] row stride ldq elements, head h at column h*128
  *   k  [B, Lk, *] row stride ldk, head h at column h*128
  *   vt [H*128, *] row stride ldv: V transposed; batch b's key j sits at
- *      column b*vt_bstride + j.  ldv and vt_bstride are multiples of 8 and
- *      every row holds at least B*vt_bstride columns, vt_bstride >= round_up(Lk, 8)
- *      (columns past Lk are read but their values are ignored)
+ *      column b*vt_bstride + j.  ldv and vt_bstride are multiples of 8,
+ *      vt_bstride >= round_up(Lk, 64), every row holds at least B*vt_bstride
+ *      columns, and columns Lk .. round_up(Lk, 64)-1 of each batch segment
+ *      hold zeros (whole 64-key tiles are read; finite padding times a zero
+ *      probability must stay zero)
  *   o  [B, Lq, H*128] bf16, row stride ldo.
  * No mask.  Returns WAN_ERR_SHAPE for unsupported strides or sizes. */
 int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv, int vt_bstride,

@@ -12,12 +12,14 @@
 //    a lane then holds 16 keys of ONE query, so the row max / row sum are
 //    per-lane reductions plus one exchange between lanes l and l^32;
 //  * O^T = V^T P^T: the probabilities are already in the B-operand layout.
-//    V arrives transposed ([hd][key], written so by the projection GEMM) and
-//    the LDS copy of a V^T tile stores its keys permuted so that the 8 keys
-//    one lane feeds to an MFMA are 16 contiguous bytes (one ds_read_b128);
-//  * K and V^T tiles of 64 keys are double-buffered in LDS with XOR
-//    swizzles that keep every 16-lane group of a 16-byte read on distinct
-//    banks; the next tile's global loads are in flight during the math;
+//    The K rows of a tile sit in LDS in a permuted order (bits 2 and 3 of
+//    the row index swapped within each 32-key block), which makes the 8
+//    probabilities a lane feeds to one PV MFMA those of 8 consecutive keys;
+//    V arrives transposed ([hd][key], written so by the projection GEMM), so
+//    each V operand is one 16-byte ds_read_b128 of the natural V^T tile;
+//  * K and V^T tiles of 64 keys go global -> LDS directly (buffer_load ...
+//    lds), double-buffered, with XOR swizzles that keep every 16-lane group of
+//    a 16-byte read on distinct banks; K runs one tile ahead of V;
 //  * the running max is only raised (and the accumulators rescaled) when a
 //    tile's max exceeds it by more than 2^8, so most tiles skip the rescale;
 //    probabilities stay <= 256.
@@ -26,28 +28,30 @@
 
 namespace wan {
 
-constexpr int AQ = 256;   // queries per workgroup
-constexpr int AW = 8;     // wavefronts per workgroup (32 queries each)
+#ifndef WAN_ATTN_WAVES
+#define WAN_ATTN_WAVES 8
+#endif
+constexpr int AW = WAN_ATTN_WAVES;   // wavefronts per workgroup (32 queries each)
+constexpr int AQ = AW * 32;          // queries per workgroup
+constexpr int KBW = 16 / AW;         // 1-KB blocks of a K (or V^T) tile each wavefront loads
 constexpr int AK = 64;    // keys per tile
 constexpr int HD = 128;   // head dim
 constexpr float TAU = 8.0f;
+constexpr int NST = 2;    // LDS stages per operand
 
 WAN_DEV float other_half(float v) { return __shfl_xor(v, 32); }
 
 typedef __attribute__((address_space(3))) void *lds_ptr;
 
-// V^T tile: row = hd (128 B = 64 keys). A lane group g of MFMA (j = 0..3,
-// 16 keys each) reads keys {16j + 4g .. +3} and {16j + 8 + 4g .. +3}; those two
-// 8-byte units are stored side by side in 16-byte chunk 2j + g.
-WAN_DEV int vunit_pos(int u) {           // 8-byte unit u = key/4 -> 8-byte slot
-  const int j = u >> 2, r = u & 3;
-  return 2 * (2 * j + (r & 1)) + (r >> 1);
-}
+// Row i of a K tile in LDS holds key ksig(i): bits 2 and 3 of i swapped.  A
+// lane of half g then finds, in S^T registers r = 8 hf .. 8 hf + 7 of 32-key
+// block kb, the keys kb*32 + 16 hf + 8 g + 0..7.
+WAN_DEV int ksig(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 WAN_DEV int vswz(int row) { return (row >> 1) & 7; }   // 16-byte chunk XOR for 128-byte rows
 
-__global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][AK * HD];   // [key][hd], chunk ^ (key & 15)
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][HD * AK];   // [hd][key perm], chunk ^ vswz(hd)
+__global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
+  __shared__ __attribute__((aligned(16))) bf16 sK[NST][AK * HD];   // [row][hd], chunk ^ (row & 15)
+  __shared__ __attribute__((aligned(16))) bf16 sV[NST][HD * AK];   // [hd][key], chunk ^ vswz(hd)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -84,64 +88,48 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
 
   // ---- tile loaders: K tile = 64 keys x 16 chunks; V^T tile = 128 rows x 8 chunks;
   // 512 threads, two chunks of each per thread
-  uint4 rv[2];
-  const int vrow = tid >> 3, vc = tid & 7;         // row 0..63 (+64), chunk 0..7
   const long vbase = (long)b * a.vt_bstride;
   // K tile: global -> LDS directly (buffer_load_dwordx4 ... lds).  The tile is
-  // 16 blocks of 1 KB (4 keys each); wavefront w fills blocks 2w, 2w+1; lane i
-  // lands at key blk*4 + i/16, physical chunk i%16 and fetches the logical
-  // chunk (i%16) ^ (key & 15).  The descriptor spans exactly this batch's Lk
-  // key rows, so rows past Lk read as zero.
+  // 16 blocks of 1 KB (4 rows each); wavefront w fills blocks w*KBW ..; lane i
+  // lands at row blk*4 + i/16, physical chunk i%16; it fetches key ksig(row),
+  // logical chunk (i%16) ^ (row & 15).  The descriptor spans exactly this
+  // batch's Lk key rows, so rows past Lk read as zero.
   const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(Kg + (long)b * Lk * a.ldk), 0, (int)((unsigned)Lk * (unsigned)a.ldk * 2u), 0x00020000);
-  int kvoff[2];
+  int kvoff[KBW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int key = (w * 2 + i) * 4 + (lane >> 4);
-    const int chunk = (lane & 15) ^ (key & 15);
-    kvoff[i] = (key * (int)a.ldk + h * HD + chunk * 8) * 2;
+  for (int i = 0; i < KBW; ++i) {
+    const int row = (w * KBW + i) * 4 + (lane >> 4);    // LDS row of this lane's chunk
+    const int chunk = (lane & 15) ^ (row & 15);
+    kvoff[i] = (ksig(row) * (int)a.ldk + h * HD + chunk * 8) * 2;
   }
   auto gloadK = [&](int j, int st) {
     const int rowb = j * AK * (int)a.ldk * 2;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr)(&sK[st][(w * 2 + i) * 512]), 16,
+    for (int i = 0; i < KBW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr)(&sK[st][(w * KBW + i) * 512]), 16,
                                                kvoff[i] + rowb, 0, 0, 0);
   };
-  auto gloadV = [&](int j, bool ragged) {   // ragged: tile j may reach past Lk
-    const int key0 = j * AK;
+  // V^T tile: global -> LDS directly.  128 rows (hd) x 64 keys = 16 blocks of
+  // 1 KB (8 rows each); wavefront w fills blocks w*KBW ..; lane i lands at row
+  // blk*8 + i/8, physical chunk i%8 and fetches the logical chunk
+  // (i%8) ^ vswz(row), i.e. keys 8*chunk .. +7 of the tile.  Columns past Lk
+  // are read from the caller's zero padding.
+  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)Vg, 0, (int)((unsigned)(a.H * HD) * (unsigned)a.ldv * 2u), 0x00020000);
+  int vvoff[KBW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = vrow + 64 * i;
-      const int col = key0 + vc * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (!ragged || col < Lk) {
-        v = ld16(Vg + (long)(h * HD + row) * a.ldv + vbase + col);
-        if (ragged && col + 8 > Lk) {   // ragged tail: clear keys >= Lk (their memory is padding)
-          uint32_t *e = reinterpret_cast<uint32_t *>(&v);
+  for (int i = 0; i < KBW; ++i) {
+    const int row = (w * KBW + i) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ vswz(row);
+    vvoff[i] = (int)(((h * HD + row) * (long)a.ldv + vbase + chunk * 8) * 2);
+  }
+  auto gloadV = [&](int j, int st) {
+    const int colb = j * AK * 2;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int k0 = col + 2 * u;
-            if (k0 >= Lk) e[u] = 0u;
-            else if (k0 + 1 >= Lk) e[u] &= 0xFFFFu;
-          }
-        }
-      }
-      rv[i] = v;
-    }
-  };
-  auto sstoreV = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = vrow + 64 * i;
-      const int f = vswz(row);
-      const int p0 = vunit_pos(2 * vc), p1 = vunit_pos(2 * vc + 1);   // 8-byte slots
-      bf16 *rp = &sV[st][row * AK];
-      *reinterpret_cast<uint2 *>(rp + ((((p0 >> 1) ^ f) << 3) | ((p0 & 1) << 2))) =
-          make_uint2(rv[i].x, rv[i].y);
-      *reinterpret_cast<uint2 *>(rp + ((((p1 >> 1) ^ f) << 3) | ((p1 & 1) << 2))) =
-          make_uint2(rv[i].z, rv[i].w);
-    }
+    for (int i = 0; i < KBW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr)(&sV[st][(w * KBW + i) * 512]), 16,
+                                               vvoff[i] + colb, 0, 0, 0);
   };
 
   // per-lane LDS read offsets (elements); tile / buffer offsets are added as constants
@@ -174,7 +162,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * AK + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+          const int key = j * AK + kb * 32 + 16 * (r >> 3) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
           if (key >= Lk) s[kb][r] = -INFINITY;
         }
     }
@@ -240,15 +228,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
 
   // Pipeline: K runs one tile ahead of V.  At the top of iteration j the LDS
   // holds K(j+1) in sK[(j+1)&1] and V(j) in sV[j&1]; S(j) and its row max are
-  // in registers.  Iteration j: (rare) rescale; the S(j+1) MFMAs interleaved
-  // with the exponentials of tile j; the PV(j) MFMAs interleaved with the row
-  // max of S(j+1); the staged V(j+1) and the directly loaded K(j+2) land in
-  // the buffers freed in iteration j-1; one barrier.
+  // in registers.  Iteration j: K(j+2) and V(j+1) start loading into the
+  // buffers freed in iteration j-1; (rare) rescale; the S(j+1) MFMAs
+  // interleaved with the exponentials of tile j; the PV(j) MFMAs interleaved
+  // with the row max of S(j+1); wait for the loads; one barrier.
   gloadK(0, 0);
   if (ntiles > 1) gloadK(1, 1);
-  gloadV(0, ntiles == 1);
-  sstoreV(0);
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(0), K(1) landed
+  gloadV(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(0), K(1), V(0) landed
   __syncthreads();
   f32x16 sa[2], sb[2];
   qk(sK[0], sa);
@@ -256,13 +243,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
   const float mxa = rowmax(sa);
   __syncthreads();   // every wavefront has read K(0): its buffer may be refilled
 
-  // one pipelined iteration; tile j+1 exists
-  // (load_k2: tile j+2 exists; mask_next: tile j+1 is the last, possibly ragged,
-  //  tile; both are constants at every call site, so no branch stays in the loop)
+  // one pipelined iteration; tile j+1 exists.  (load_k2: tile j+2 exists;
+  // mask_next: tile j+1 is the last, possibly ragged, tile; both are constants
+  // in the steady-state loop, so no branch stays there.)
   auto step = [&](int j, f32x16 *scur, float mxcur, f32x16 *snxt, bool load_k2,
                   bool mask_next) -> float {
     if (load_k2) gloadK(j + 2, j & 1);   // buffer of K(j), read in iteration j-1
-    gloadV(j + 1, mask_next);
+    gloadV(j + 1, (j + 1) & 1);          // buffer of V(j-1), read in iteration j-1
     rescale(mxcur);
     bf16x8 pb[2][2];
     // matrix unit: next scores; vector unit: this tile's probabilities
@@ -287,8 +274,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
       if (q < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
-    sstoreV((j + 1) & 1);
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(j+2) landed, LDS reads done
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(j+2), V(j+1) landed, LDS reads done
     __syncthreads();
     return mxn;
   };
@@ -407,6 +393,8 @@ hipError_t launch_attention(const AttnDesc &a, hipStream_t s) {
   if (a.hd != HD) return hipErrorInvalidValue;
   // K rows are addressed through a buffer descriptor with 32-bit byte offsets
   if ((long)a.Lk * a.ldk * 2 >= (1L << 31)) return hipErrorInvalidValue;
+  if ((long)a.H * a.hd * a.ldv * 2 >= (1L << 31)) return hipErrorInvalidValue;
+  if (a.vt_bstride < (a.Lk + AK - 1) / AK * AK) return hipErrorInvalidValue;
   const int nqt = (a.Lq + AQ - 1) / AQ;
   k_attn_bf16<<<a.B * a.H * nqt, AW * 64, 0, s>>>(a);
   return hipGetLastError();

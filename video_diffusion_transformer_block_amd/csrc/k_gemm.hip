@@ -82,8 +82,12 @@ WAN_DEV void epi8(const GemmDesc &g, int m, int n, float *v) {
   }
   if (KIND == OUT_BF16 || KIND == OUT_GELU) {
     bf16 *c = reinterpret_cast<bf16 *>(g.C) + (long)m * g.ldc + n;
-    if (full) Vec8<bf16>::store(c, v);
-    else for (int i = 0; i < 8 && n + i < g.N; ++i) c[i] = f2bf(v[i]);
+    if (full) {
+      Vec8<bf16>::store(c, v);
+    } else {
+      const int lim = g.npad > g.N ? g.npad : g.N;
+      for (int i = 0; i < 8 && n + i < lim; ++i) c[i] = n + i < g.N ? f2bf(v[i]) : f2bf(0.f);
+    }
   } else if (KIND == OUT_F32) {
     float *c = reinterpret_cast<float *>(g.C) + (long)m * g.ldc + n;
     if (full) {
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int n = n0 + wn * 64 + jh * 64 + cb + q * 8;
-          if (n < g.N) {
+          if (n < g.N || n < g.npad) {
             float v[8];
             const float4 u0 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8);
             const float4 u1 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8 + 4);

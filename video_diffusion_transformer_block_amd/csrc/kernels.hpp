@@ -21,6 +21,7 @@ struct GemmDesc {
   float *X; long ldx;
   const float *gate; long gate_bstride; int rows_per_batch;
   int f32;                     // operands / bias / C are float32 instead of bf16
+  int npad;                    // OUT_BF16: columns N .. npad-1 of C are written as zeros
 };
 
 // Attention O = softmax(Q K^T * scale) V for every (batch, head); hd = 128, bf16.

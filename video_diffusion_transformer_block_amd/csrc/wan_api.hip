@@ -144,6 +144,7 @@ int kv_project(const wan_cfg_t &c, int B, int Lk, const void *src, const void *w
     GemmDesc g = gemm(off(wkv, (long)d * d, es), d, off(src, (long)b * Lk * d, es), d, d, Lk, d,
                       off(bkv, d, es), OUT_BF16, vtbuf + (long)b * ldvb * es, (long)B * ldvb, 0);
     g.bias_rows = 1;
+    g.npad = (int)ldvb;   // keys Lk .. ldvb-1 of this batch segment are zero
     WAN_TRY(launch_gemm(g, s));
   }
   return WAN_OK;
@@ -185,6 +186,7 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
                         (int)L, d, off(w.sa_bqkv, 2 * d, es), OUT_BF16, vt + b * y.Lp * es,
                         (long)B * y.Lp, 0);
       g.bias_rows = 1;
+      g.npad = (int)y.Lp;   // keys L .. Lp-1 of this batch segment are zero
       WAN_TRY(launch_gemm(g, s));
     }
     WAN_TRY(launch_attention(attn(qk, 2 * d, off(qk, d, es), 2 * d, vt, (long)B * y.Lp, y.Lp, o,
@@ -372,7 +374,7 @@ int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void
   if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return WAN_ERR_SHAPE;
   if (ldq < H * 128 || ldk < H * 128 || ldo < H * 128 || ldq % 8 || ldk % 8 || ldo % 4)
     return WAN_ERR_SHAPE;
-  if (ldv % 8 || vt_bstride % 8 || vt_bstride < rup(Lk, 8) || (long)ldv < (long)B * vt_bstride)
+  if (ldv % 8 || vt_bstride % 8 || vt_bstride < rup(Lk, 64) || (long)ldv < (long)B * vt_bstride)
     return WAN_ERR_SHAPE;
   AttnDesc a = attn(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk, 128, 0);
   WAN_TRY(launch_attention(a, S(stream)));
