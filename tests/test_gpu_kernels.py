@@ -35,6 +35,8 @@ def _attn_oracle(q, k, v, H):
 CASES = [  # B, H, Lq, Lk
     (1, 1, 1, 1), (1, 2, 200, 64), (2, 2, 300, 100), (1, 3, 513, 257), (2, 1, 256, 600),
     (1, 2, 70, 4), (1, 1, 1000, 1000),
+    # key-tile counts 2 .. 5 exercise every tail of the two-tile pipeline
+    (1, 1, 64, 128), (1, 1, 96, 150), (1, 2, 100, 250), (1, 1, 40, 320),
 ]
 
 

@@ -23,6 +23,8 @@
 //  * the running max is only raised (and the accumulators rescaled) when a
 //    tile's max exceeds it by more than 2^8, so most tiles skip the rescale;
 //    probabilities stay <= 256.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,7 +39,6 @@ constexpr int KBW = 16 / AW;         // 1-KB blocks of a K (or V^T) tile each wa
 constexpr int AK = 64;    // keys per tile
 constexpr int HD = 128;   // head dim
 constexpr float TAU = 8.0f;
-constexpr int NST = 2;    // LDS stages per operand
 
 WAN_DEV float other_half(float v) { return __shfl_xor(v, 32); }
 
@@ -50,8 +51,29 @@ WAN_DEV int ksig(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 WAN_DEV int vswz(int row) { return (row >> 1) & 7; }   // 16-byte chunk XOR for 128-byte rows
 
 __global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[NST][AK * HD];   // [row][hd], chunk ^ (row & 15)
-  __shared__ __attribute__((aligned(16))) bf16 sV[NST][HD * AK];   // [hd][key], chunk ^ vswz(hd)
+  // One LDS variable per stage: the compiler gives each its own alias scope,
+  // so LDS reads of one stage need not wait for loads still landing in the
+  // other (it cannot tell two halves of one array apart).  Stages are picked
+  // with compile-time parities.
+  __shared__ __attribute__((aligned(16))) bf16 sK0[AK * HD];   // [row][hd], chunk ^ (row & 15)
+  __shared__ __attribute__((aligned(16))) bf16 sK1[AK * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[HD * AK];   // [hd][key], chunk ^ vswz(hd)
+  __shared__ __attribute__((aligned(16))) bf16 sV1[HD * AK];
+  // a stage is a std::integral_constant (steady state) or an int (the tail)
+  auto kbuf = [&](auto P) -> bf16 * {
+    if constexpr (std::is_integral_v<decltype(P)>) return P ? sK1 : sK0;
+    else if constexpr (decltype(P)::value == 0) return sK0;
+    else return sK1;
+  };
+  auto vbuf = [&](auto P) -> bf16 * {
+    if constexpr (std::is_integral_v<decltype(P)>) return P ? sV1 : sV0;
+    else if constexpr (decltype(P)::value == 0) return sV0;
+    else return sV1;
+  };
+  auto other = [](auto P) {
+    if constexpr (std::is_integral_v<decltype(P)>) return 1 - P;
+    else return std::integral_constant<int, 1 - decltype(P)::value>{};
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -103,11 +125,12 @@ __global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
     const int chunk = (lane & 15) ^ (row & 15);
     kvoff[i] = (ksig(row) * (int)a.ldk + h * HD + chunk * 8) * 2;
   }
-  auto gloadK = [&](int j, int st) {
+  auto gloadK = [&](int j, auto P) {
     const int rowb = j * AK * (int)a.ldk * 2;
+    bf16 *dst = kbuf(P);
 #pragma unroll
     for (int i = 0; i < KBW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr)(&sK[st][(w * KBW + i) * 512]), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr)(dst + (w * KBW + i) * 512), 16,
                                                kvoff[i] + rowb, 0, 0, 0);
   };
   // V^T tile: global -> LDS directly.  128 rows (hd) x 64 keys = 16 blocks of
@@ -124,11 +147,12 @@ __global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
     const int chunk = (lane & 7) ^ vswz(row);
     vvoff[i] = (int)(((h * HD + row) * (long)a.ldv + vbase + chunk * 8) * 2);
   }
-  auto gloadV = [&](int j, int st) {
+  auto gloadV = [&](int j, auto P) {
     const int colb = j * AK * 2;
+    bf16 *dst = vbuf(P);
 #pragma unroll
     for (int i = 0; i < KBW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr)(&sV[st][(w * KBW + i) * 512]), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr)(dst + (w * KBW + i) * 512), 16,
                                                vvoff[i] + colb, 0, 0, 0);
   };
 
@@ -227,33 +251,37 @@ __global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
   };
 
   // Pipeline: K runs one tile ahead of V.  At the top of iteration j the LDS
-  // holds K(j+1) in sK[(j+1)&1] and V(j) in sV[j&1]; S(j) and its row max are
-  // in registers.  Iteration j: K(j+2) and V(j+1) start loading into the
-  // buffers freed in iteration j-1; (rare) rescale; the S(j+1) MFMAs
-  // interleaved with the exponentials of tile j; the PV(j) MFMAs interleaved
-  // with the row max of S(j+1); wait for the loads; one barrier.
-  gloadK(0, 0);
-  if (ntiles > 1) gloadK(1, 1);
-  gloadV(0, 0);
+  // holds K(j+1) in stage (j+1)&1 and V(j) in stage j&1; S(j) and its row max
+  // are in registers.  Iteration j: K(j+2) starts loading into the stage
+  // freed in iteration j-1; (rare) rescale; the S(j+1) MFMAs interleaved with
+  // the exponentials of tile j; V(j+1) starts loading into its freed stage;
+  // the PV(j) MFMAs interleaved with the row max of S(j+1); wait for the
+  // loads; one barrier.
+  constexpr std::integral_constant<int, 0> P0{};
+  constexpr std::integral_constant<int, 1> P1{};
+  gloadK(0, P0);
+  if (ntiles > 1) gloadK(1, P1);
+  gloadV(0, P0);
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(0), K(1), V(0) landed
   __syncthreads();
   f32x16 sa[2], sb[2];
-  qk(sK[0], sa);
+  qk(sK0, sa);
   mask_tail(sa, 0);
   const float mxa = rowmax(sa);
   __syncthreads();   // every wavefront has read K(0): its buffer may be refilled
 
-  // one pipelined iteration; tile j+1 exists.  (load_k2: tile j+2 exists;
-  // mask_next: tile j+1 is the last, possibly ragged, tile; both are constants
-  // in the steady-state loop, so no branch stays there.)
-  auto step = [&](int j, f32x16 *scur, float mxcur, f32x16 *snxt, bool load_k2,
+  // one pipelined iteration; tile j+1 exists; P is the parity of j.
+  // (load_k2: tile j+2 exists; mask_next: tile j+1 is the last, possibly
+  // ragged, tile; both are constants in the steady-state loop, so no branch
+  // stays there.)
+  auto step = [&](auto P, int j, f32x16 *scur, float mxcur, f32x16 *snxt, bool load_k2,
                   bool mask_next) -> float {
-    if (load_k2) gloadK(j + 2, j & 1);   // buffer of K(j), read in iteration j-1
-    gloadV(j + 1, (j + 1) & 1);          // buffer of V(j-1), read in iteration j-1
+    const auto Q = other(P);
+    if (load_k2) gloadK(j + 2, P);   // buffer of K(j), read in iteration j-1
     rescale(mxcur);
     bf16x8 pb[2][2];
     // matrix unit: next scores; vector unit: this tile's probabilities
-    qk(sK[(j + 1) & 1], snxt);
+    qk(kbuf(Q), snxt);
     probs(scur, pb);
     // LDS reads run four MFMAs ahead of their use; VALU fills the MFMA shadow
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -264,8 +292,12 @@ __global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
     }
     if (mask_next) mask_tail(snxt, j + 1);
+    // the V load is issued after the score MFMAs, so that eight wavefronts
+    // leaving the barrier together do not queue all their tile loads at once
+    __builtin_amdgcn_sched_barrier(0);
+    gloadV(j + 1, Q);                // buffer of V(j-1), read in iteration j-1
     // matrix unit: PV of this tile; vector unit: row max of the next scores
-    pv(sV[j & 1], pb);
+    pv(vbuf(P), pb);
     const float mxn = rowmax(snxt);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -279,29 +311,26 @@ __global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
     return mxn;
   };
   // the last tile: no next scores
-  auto last = [&](int j, f32x16 *scur, float mxcur) {
+  auto last = [&](auto P, f32x16 *scur, float mxcur) {
     rescale(mxcur);
     bf16x8 pb[2][2];
     probs(scur, pb);
-    pv(sV[j & 1], pb);
+    pv(vbuf(P), pb);
   };
   int j = 0;
   float mx = mxa;
-  for (; j + 3 < ntiles; j += 2) {     // unrolled by two (score buffers alternate); never
-    mx = step(j, sa, mx, sb, true, false);       // computes the last tile's scores
-    mx = step(j + 1, sb, mx, sa, true, false);
+  for (; j + 3 < ntiles; j += 2) {     // unrolled by two (score buffers and stages alternate);
+    mx = step(P0, j, sa, mx, sb, true, false);   // never computes the last tile's scores
+    mx = step(P1, j + 1, sb, mx, sa, true, false);
   }
-  const int rem = ntiles - j;          // 1, 2 or 3 tiles left; the current scores are in sa
-  if (rem == 3) {
-    mx = step(j, sa, mx, sb, true, false);
-    mx = step(j + 1, sb, mx, sa, false, true);
-    last(j + 2, sa, mx);
-  } else if (rem == 2) {
-    mx = step(j, sa, mx, sb, false, true);
-    last(j + 1, sb, mx);
-  } else {
-    last(j, sa, mx);
+  // the last 1 .. 3 tiles, one at a time with run-time stages; the current
+  // scores are in sa
+  for (; j + 1 < ntiles; ++j) {
+    mx = step(j & 1, j, sa, mx, sb, j + 2 < ntiles, j + 2 == ntiles);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
   }
+  last(j & 1, sa, mx);
 
   // ---- normalise and store: lane holds O^T[hd = t*32 + (r/4)*8 + g*4 + r%4][q = l32]
   const float lt = l + other_half(l);
