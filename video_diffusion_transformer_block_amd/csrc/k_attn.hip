@@ -30,12 +30,10 @@
 
 namespace wan {
 
-#ifndef WAN_ATTN_WAVES
-#define WAN_ATTN_WAVES 8
+#ifndef WAN_ATTN_QB
+#define WAN_ATTN_QB 1
 #endif
-constexpr int AW = WAN_ATTN_WAVES;   // wavefronts per workgroup (32 queries each)
-constexpr int AQ = AW * 32;          // queries per workgroup
-constexpr int KBW = 16 / AW;         // 1-KB blocks of a K (or V^T) tile each wavefront loads
+constexpr int AQ = 256;   // queries per workgroup
 constexpr int AK = 64;    // keys per tile
 constexpr int HD = 128;   // head dim
 constexpr float TAU = 8.0f;
@@ -50,11 +48,19 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 WAN_DEV int ksig(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 WAN_DEV int vswz(int row) { return (row >> 1) & 7; }   // 16-byte chunk XOR for 128-byte rows
 
-__global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
+// QB = 32-query blocks per wavefront (1 or 2).  A workgroup always owns AQ =
+// 256 queries: 8 / QB wavefronts.  With QB = 2 each K / V^T fragment read from
+// LDS feeds two MFMAs (half the LDS traffic per MFMA) and a wavefront has a
+// SIMD to itself (512 registers; the accumulators of O fit in AGPRs).
+constexpr int QB = WAN_ATTN_QB;
+static_assert(QB == 1 || QB == 2, "one or two 32-query blocks per wavefront");
+__global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
+  constexpr int NW = 8 / QB;          // wavefronts per workgroup
+  constexpr int KBW = 16 / NW;        // 1-KB blocks of a K (or V^T) tile each wavefront loads
   // One LDS variable per stage: the compiler gives each its own alias scope,
   // so LDS reads of one stage need not wait for loads still landing in the
-  // other (it cannot tell two halves of one array apart).  Stages are picked
-  // with compile-time parities.
+  // other (it cannot tell two halves of one array apart).  The steady-state
+  // loop picks stages with compile-time parities.
   __shared__ __attribute__((aligned(16))) bf16 sK0[AK * HD];   // [row][hd], chunk ^ (row & 15)
   __shared__ __attribute__((aligned(16))) bf16 sK1[AK * HD];
   __shared__ __attribute__((aligned(16))) bf16 sV0[HD * AK];   // [hd][key], chunk ^ vswz(hd)
@@ -87,29 +93,35 @@ __global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
   const bf16 *Kg = reinterpret_cast<const bf16 *>(a.k);
   const bf16 *Vg = reinterpret_cast<const bf16 *>(a.vt);
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[q][st*16 + g*8 .. +8]
-  const int qrow = qt * AQ + w * 32 + l32;
-  bf16x8 qf[8];
-  {
-    const bool ok = qrow < Lq;
-    const bf16 *qp = Qg + (long)(b * Lq + (ok ? qrow : 0)) * a.ldq + h * HD + g * 8;
+  // ---- Q fragments (B operand of S^T = K Q^T): for query block qb the lane
+  // holds Q[q][st*16 + g*8 .. +8] of query q = qrow[qb]
+  int qrow[QB];
+  bf16x8 qf[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    qrow[qb] = qt * AQ + (w * QB + qb) * 32 + l32;
+    const bool ok = qrow[qb] < Lq;
+    const bf16 *qp = Qg + (long)(b * Lq + (ok ? qrow[qb] : 0)) * a.ldq + h * HD + g * 8;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       uint4 v = ok ? ld16(qp + st * 16) : make_uint4(0, 0, 0, 0);
-      qf[st] = *reinterpret_cast<bf16x8 *>(&v);
+      qf[qb][st] = *reinterpret_cast<bf16x8 *>(&v);
     }
   }
 
-  f32x16 o[4];
+  f32x16 o[4][QB];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][qb][r] = 0.f;
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
   const float c = a.scale * 1.4426950408889634f;   // scores -> log2 units
 
-  // ---- tile loaders: K tile = 64 keys x 16 chunks; V^T tile = 128 rows x 8 chunks;
-  // 512 threads, two chunks of each per thread
+  // ---- tile loaders: K tile = 64 keys x 16 chunks; V^T tile = 128 rows x 8 chunks
   const long vbase = (long)b * a.vt_bstride;
   // K tile: global -> LDS directly (buffer_load_dwordx4 ... lds).  The tile is
   // 16 blocks of 1 KB (4 rows each); wavefront w fills blocks w*KBW ..; lane i
@@ -166,79 +178,97 @@ __global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
 
   const int ntiles = (Lk + AK - 1) / AK;
 
-  // S^T tile j from K buffer kb (two 32-key blocks)
-  auto qk = [&](const bf16 *sk, f32x16 *s) {
+  // S^T of a tile (two 32-key blocks x QB query blocks); each K fragment
+  // feeds the QB query blocks
+  auto qk = [&](const bf16 *sk, f32x16 (&s)[2][QB]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sk + kb * 32 * HD + koff[st]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[kb], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][st], s[kb][qb], 0, 0, 0);
       }
     }
   };
   // keys past Lk -> -inf (last tile only)
-  auto mask_tail = [&](f32x16 *s, int j) {
+  auto mask_tail = [&](f32x16 (&s)[2][QB], int j) {
     if ((j + 1) * AK > Lk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j * AK + kb * 32 + 16 * (r >> 3) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
-          if (key >= Lk) s[kb][r] = -INFINITY;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if (key >= Lk) s[kb][qb][r] = -INFINITY;
         }
     }
   };
-  // row max of a score tile, merged across the two lane halves
-  auto rowmax = [&](const f32x16 *s) -> float {
-    float mx = s[0][0];
+  // row max of a score tile per query block, merged across the two lane halves
+  auto rowmax = [&](const f32x16 (&s)[2][QB], float (&mx)[QB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float v = s[0][qb][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    return fmaxf(mx, other_half(mx));
-  };
-  // raise the running max only when the tile's max exceeds it by more than 2^TAU
-  auto rescale = [&](float mx) {
-    const float mz = mx * c;
-    if (__builtin_amdgcn_ballot_w64(mz > m + TAU) != 0) {
-      const float mn = fmaxf(m, mz);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      l *= alpha;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-      m = mn;
+        for (int r = 0; r < 16; ++r) v = fmaxf(v, s[kb][qb][r]);
+      mx[qb] = fmaxf(v, other_half(v));
     }
   };
-  // probabilities of a tile, bf16 in the B-operand layout, and their row sum
-  // (the row sum adds the bf16-rounded probabilities, two per v_dot2 with
+  // raise the running max only when the tile's max exceeds it by more than 2^TAU
+  auto rescale = [&](const float (&mx)[QB]) {
+    bool up = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) up |= mx[qb] * c > m[qb] + TAU;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mn = fmaxf(m[qb], mx[qb] * c);
+        const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+        l[qb] *= alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[t][qb][r] *= alpha;
+        m[qb] = mn;
+      }
+    }
+  };
+  // probabilities of a tile, bf16 in the B-operand layout, and their row sums
+  // (a row sum adds the bf16-rounded probabilities, two per v_dot2 with
   //  (1, 1): the normaliser then matches exactly the weights the PV MFMA uses)
-  auto probs = [&](const f32x16 *s, bf16x8 (&pb)[2][2]) {
-    const float nm = -m;
+  auto probs = [&](const f32x16 (&s)[2][QB], bf16x8 (&pb)[QB][2][2]) {
     bf16x2 one;
     one[0] = (bf16)1.0f; one[1] = (bf16)1.0f;
-    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      const float nm = -m[qb];
+      float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pb[kb][hf][e] = f2bf(__builtin_amdgcn_exp2f(fmaf(s[kb][hf * 8 + e], c, nm)));
-        const bf16x2 *pp = reinterpret_cast<const bf16x2 *>(&pb[kb][hf]);
-        ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[0], one, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[1], one, ls1, false);
-        ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[2], one, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[3], one, ls1, false);
-      }
-    l += ls0 + ls1;
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pb[qb][kb][hf][e] = f2bf(__builtin_amdgcn_exp2f(fmaf(s[kb][qb][hf * 8 + e], c, nm)));
+          const bf16x2 *pp = reinterpret_cast<const bf16x2 *>(&pb[qb][kb][hf]);
+          ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[0], one, ls0, false);
+          ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[1], one, ls1, false);
+          ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[2], one, ls0, false);
+          ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[3], one, ls1, false);
+        }
+      l[qb] += ls0 + ls1;
+    }
   };
-  // O^T += V^T P^T
-  auto pv = [&](const bf16 *sv, const bf16x8 (&pb)[2][2]) {
+  // O^T += V^T P^T; each V^T fragment feeds the QB query blocks
+  auto pv = [&](const bf16 *sv, const bf16x8 (&pb)[QB][2][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -246,7 +276,9 @@ __global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           bf16x8 va = *reinterpret_cast<const bf16x8 *>(sv + t * 32 * AK + voff[2 * kb + hf]);
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][hf], o[t], 0, 0, 0);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[t][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][kb][hf], o[t][qb], 0, 0, 0);
         }
   };
 
@@ -264,86 +296,94 @@ __global__ __launch_bounds__(AW * 64, 8 / AW) void k_attn_bf16(AttnDesc a) {
   gloadV(0, P0);
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(0), K(1), V(0) landed
   __syncthreads();
-  f32x16 sa[2], sb[2];
+  f32x16 sa[2][QB], sb[2][QB];
+  float mxa[QB];
   qk(sK0, sa);
   mask_tail(sa, 0);
-  const float mxa = rowmax(sa);
+  rowmax(sa, mxa);
   __syncthreads();   // every wavefront has read K(0): its buffer may be refilled
 
+  // MFMAs per section, and the LDS reads / VALU instructions laid between them
+  constexpr int NMF = 16 * QB;
   // one pipelined iteration; tile j+1 exists; P is the parity of j.
   // (load_k2: tile j+2 exists; mask_next: tile j+1 is the last, possibly
   // ragged, tile; both are constants in the steady-state loop, so no branch
   // stays there.)
-  auto step = [&](auto P, int j, f32x16 *scur, float mxcur, f32x16 *snxt, bool load_k2,
-                  bool mask_next) -> float {
+  auto step = [&](auto P, int j, f32x16 (&scur)[2][QB], float (&mx)[QB], f32x16 (&snxt)[2][QB],
+                  bool load_k2, bool mask_next) {
     const auto Q = other(P);
+    rescale(mx);
     if (load_k2) gloadK(j + 2, P);   // buffer of K(j), read in iteration j-1
-    rescale(mxcur);
-    bf16x8 pb[2][2];
+    bf16x8 pb[QB][2][2];
     // matrix unit: next scores; vector unit: this tile's probabilities
     qk(kbuf(Q), snxt);
     probs(scur, pb);
-    // LDS reads run four MFMAs ahead of their use; VALU fills the MFMA shadow
+    // LDS reads run ahead of their use; VALU fills the MFMA shadow
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < NMF; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      if (q < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+      if (q % QB == 0 && q < NMF - 4 * QB)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // 1 LDS read
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
     }
     if (mask_next) mask_tail(snxt, j + 1);
-    // the V load is issued after the score MFMAs, so that eight wavefronts
+    // the V load is issued after the score MFMAs, so that the wavefronts
     // leaving the barrier together do not queue all their tile loads at once
     __builtin_amdgcn_sched_barrier(0);
     gloadV(j + 1, Q);                // buffer of V(j-1), read in iteration j-1
     // matrix unit: PV of this tile; vector unit: row max of the next scores
     pv(vbuf(P), pb);
-    const float mxn = rowmax(snxt);
+    rowmax(snxt, mx);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < NMF; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (q < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q % QB == 0 && q < NMF - 4 * QB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(j+2), V(j+1) landed, LDS reads done
     __syncthreads();
-    return mxn;
   };
   // the last tile: no next scores
-  auto last = [&](auto P, f32x16 *scur, float mxcur) {
-    rescale(mxcur);
-    bf16x8 pb[2][2];
+  auto last = [&](auto P, f32x16 (&scur)[2][QB], const float (&mx)[QB]) {
+    rescale(mx);
+    bf16x8 pb[QB][2][2];
     probs(scur, pb);
     pv(vbuf(P), pb);
   };
   int j = 0;
-  float mx = mxa;
+  float mx[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mx[qb] = mxa[qb];
   for (; j + 3 < ntiles; j += 2) {     // unrolled by two (score buffers and stages alternate);
-    mx = step(P0, j, sa, mx, sb, true, false);   // never computes the last tile's scores
-    mx = step(P1, j + 1, sb, mx, sa, true, false);
+    step(P0, j, sa, mx, sb, true, false);        // never computes the last tile's scores
+    step(P1, j + 1, sb, mx, sa, true, false);
   }
   // the last 1 .. 3 tiles, one at a time with run-time stages; the current
   // scores are in sa
   for (; j + 1 < ntiles; ++j) {
-    mx = step(j & 1, j, sa, mx, sb, j + 2 < ntiles, j + 2 == ntiles);
+    step(j & 1, j, sa, mx, sb, j + 2 < ntiles, j + 2 == ntiles);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sa[kb][qb] = sb[kb][qb];
   }
   last(j & 1, sa, mx);
 
-  // ---- normalise and store: lane holds O^T[hd = t*32 + (r/4)*8 + g*4 + r%4][q = l32]
-  const float lt = l + other_half(l);
-  const float inv = 1.0f / lt;
-  if (qrow < Lq) {
-    const long orow = (long)(b * Lq + qrow);
+  // ---- normalise and store: lane holds O^T[hd = t*32 + (r/4)*8 + g*4 + r%4][q = qrow[qb]]
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float inv = 1.0f / (l[qb] + other_half(l[qb]));
+    if (qrow[qb] >= Lq) continue;
+    const long orow = (long)(b * Lq + qrow[qb]);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int hd0 = t * 32 + rb * 8 + g * 4;
-        float v0 = o[t][rb * 4 + 0] * inv, v1 = o[t][rb * 4 + 1] * inv;
-        float v2 = o[t][rb * 4 + 2] * inv, v3 = o[t][rb * 4 + 3] * inv;
+        float v0 = o[t][qb][rb * 4 + 0] * inv, v1 = o[t][qb][rb * 4 + 1] * inv;
+        float v2 = o[t][qb][rb * 4 + 2] * inv, v3 = o[t][qb][rb * 4 + 3] * inv;
         if (a.out_mode == 1) {
           *reinterpret_cast<float4 *>(a.acc32 + orow * (a.H * HD) + h * HD + hd0) =
               make_float4(v0, v1, v2, v3);
@@ -425,7 +465,7 @@ hipError_t launch_attention(const AttnDesc &a, hipStream_t s) {
   if ((long)a.H * a.hd * a.ldv * 2 >= (1L << 31)) return hipErrorInvalidValue;
   if (a.vt_bstride < (a.Lk + AK - 1) / AK * AK) return hipErrorInvalidValue;
   const int nqt = (a.Lq + AQ - 1) / AQ;
-  k_attn_bf16<<<a.B * a.H * nqt, AW * 64, 0, s>>>(a);
+  k_attn_bf16<<<a.B * a.H * nqt, 512 / QB, 0, s>>>(a);
   return hipGetLastError();
 }
 
