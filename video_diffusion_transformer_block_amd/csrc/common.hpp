@@ -39,16 +39,15 @@ WAN_DEV float wave_max(float v) {
   return v;
 }
 
-// GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).
-// tanh(y) = 1 - 2 / (1 + e^{2y}); exp via the hardware exp2.
+// tanh-approximated GELU, 0.5 u (1 + tanh(y)) with y = sqrt(2/pi)(u + 0.044715 u^3),
+// written as u * sigmoid(2y) = u / (1 + 2^(-2 y log2 e)): one v_exp_f32 and
+// one v_rcp_f32 (each about 1 ulp).  For large |u| the exponential goes to 0
+// or +inf and the reciprocal to 1 or 0, giving u and 0 without a clamp.
 WAN_DEV float gelu_tanh(float u) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  float y = k0 * (u + 0.044715f * u * u * u);
-  // 2y*log2(e); clamp keeps e^{2y} finite (tanh saturates long before)
-  float z = fminf(fmaxf(2.0f * 1.4426950408889634f * y, -60.f), 60.f);
-  float e = __builtin_amdgcn_exp2f(z);
-  float th = 1.0f - 2.0f / (1.0f + e);
-  return 0.5f * u * (1.0f + th);
+  const float a = -2.0f * 1.4426950408889634f * 0.7978845608028654f;   // -2 log2(e) sqrt(2/pi)
+  const float b = a * 0.044715f;
+  const float z = u * fmaf(b, u * u, a);
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
 WAN_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
