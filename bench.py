@@ -29,6 +29,34 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 
+# HBM bytes per self-attention launch of this workload, from two rocprofv3
+# --pmc passes over `bench.py --traffic-pass` (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch), each scaled by what the counter reads for a plain 512 MiB
+# copy (fetch x2.00, write x1.00); see profiles/k_attn_bf16_wan1.3b_block_480p.md.
+# Valid only for the kernel sources they were taken on: reported as null
+# once k_attn.hip, common.hpp or kernels.hpp change.
+ATTN_TRAFFIC = {
+    "sources_sha256": "3133670ae87636397581fe73a772644188c3f2bc49f576991970bc7fd145cebc",
+    "fetch_kib": 442440, "write_kib": 100681, "fetch_scale": 2.00, "write_scale": 1.00,
+}
+
+
+def attn_sources_sha256() -> str:
+    import hashlib
+    csrc = os.path.join(ROOT, "video_diffusion_transformer_block_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("k_attn.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def attn_traffic_bytes():
+    t = ATTN_TRAFFIC
+    if attn_sources_sha256() != t["sources_sha256"]:
+        return None
+    return int(round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])))
+
 
 def block_flops(B, L, d, H, F, Lc, Li=0):
     hd = d // H
@@ -217,7 +245,9 @@ def main():
         "block_frac_of_peak": round(block_tf / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "k_attn_bf16", "achieved": round(attn_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic_bytes(),
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 counters, copy-calibrated)",
+                     "algorithmic_bytes": 4 * B * L * d * 2,
                      "launch_ms": round(attn_ms, 4),
                      "flop_per_launch": sa_f},
         "wall_s_timed": round(t_wall, 3),
