@@ -15,6 +15,9 @@ Every function names the passage it follows.  Page tags used below:
   [News]  "超越Sora！阿里正式完全开源最新、最强大的视频生成模型 Wan2.1"
           (163.com).  Sections: 核心创新一 (3D VAE, feature cache),
           核心创新二 (视频扩散 DiT), 核心创新四 (Image-to-Video).
+  [Guide] "Wan 2.1 AI：下一代开源视频生成技术的突破性实践" (cloud.baidu.com).
+          Section 工作原理 (the sampling knobs: number of inference steps,
+          guidance scale).
 
 Where the pages leave a step open the plainest reading is taken; every such
 reading is listed in the module-level ``READINGS`` table and repeated where it
@@ -54,6 +57,15 @@ READINGS = {
     "R12 decoupled CA": "two softmaxes (text / image), separate K,V weights, shared Q and "
                         "out-projection, outputs summed with weight 1",
     "R13 LayerNorm": "biased variance over d, eps inside the sqrt, no affine",
+    "R19 sampler time": "flow time tau runs from 0 (noise x0) to 1 (data x1), x_tau = tau x1 + "
+                        "(1 - tau) x0 [Note, 训练方法]; explicit Euler on a uniform grid tau_k = k/N "
+                        "(N about 50 [Note, Infra / 推理优化]); the model's timestep input is "
+                        "1000 tau (the range of R2)",
+    "R20 guidance": "v = v_u + s (v_c - v_u) with s the guidance scale [Guide, 工作原理]; in a "
+                    "two-sample guidance batch sample 0 is conditional, sample 1 unconditional, "
+                    "and both carry the same latent",
+    "R21 I2V sampling": "only the 16 noise channels move; the condition latent and the mask "
+                        "channels of the 36-channel input stay as given",
 }
 
 
@@ -337,3 +349,58 @@ def step(latent, t, ctx, mw: Dict[str, object], heads: int, eps: float = 1e-6,
         x = block(x, m, wts, ctx, heads, eps, img=img)
     out = head_unpatchify(x, mw["head_w"], mw["head_b"], F, Hp, Wp, 16)
     return (out, x) if return_hidden else out
+
+
+# ---------------------------------------------------------------------------
+# Sampler around the step (R19 - R21)
+
+
+def cfg_combine(v_cond, v_uncond, scale: float):
+    """Guided velocity v_u + s (v_c - v_u)  [Guide, 工作原理: guidance scale] (R20)."""
+    vc, vu = _f(v_cond), _f(v_uncond)
+    return vu + F64(scale) * (vc - vu)
+
+
+def sampler_times(n_steps: int):
+    """Flow times tau_k = k / N, k = 0..N (0 = noise, 1 = data), and the model's
+    timestep input 1000 tau_k for the N evaluations  [Note, 训练方法; Infra] (R19)."""
+    tau = np.arange(n_steps + 1, dtype=F64) / F64(n_steps)
+    return tau, 1000.0 * tau[:-1]
+
+
+def sample(latent0, n_steps: int, velocity, guidance: Optional[float] = None, out_ch: int = 16):
+    """Explicit Euler along the flow from tau = 0 to tau = 1 (R19).
+
+    latent0 [B, Cin, F, H8, W8]: channels 0..out_ch-1 hold the noise x0, the
+    rest (I2V: condition latent and mask) stay fixed (R21).  ``velocity(latent,
+    t)`` returns [B, out_ch, F, H8, W8] for timestep inputs t [B].  With a
+    guidance scale the batch is one conditional / unconditional pair (R20):
+    both samples move by the guided velocity.  Returns the latent at tau = 1."""
+    x = _f(latent0).copy()
+    B = x.shape[0]
+    tau, tmodel = sampler_times(n_steps)
+    if guidance is not None and B != 2:
+        raise ValueError("guidance needs a conditional / unconditional pair")
+    for k in range(n_steps):
+        v = _f(velocity(x, np.full(B, tmodel[k])))
+        if guidance is not None:
+            g = cfg_combine(v[0], v[1], guidance)
+            v = np.stack([g, g])
+        x[:, :out_ch] = x[:, :out_ch] + (tau[k + 1] - tau[k]) * v
+    return x
+
+
+def text_kv(ctx, wts: Dict[str, np.ndarray], img=None):
+    """The cross-attention keys and values of one block: they depend only on
+    the text context (and image context) and the block's weights, not on the
+    latent or the timestep, so a sampler computes them once
+    [Note, Infra / 推理优化: work shared across sampling steps].
+    ctx [Lc, d] -> (k [Lc, d], v [Lc, d]) (+ the image pair)."""
+    d = _f(ctx).shape[-1]
+    kv = linear(ctx, wts["ca_wkv"], wts["ca_bkv"])
+    out = (kv[:, :d], kv[:, d:])
+    if img is not None:
+        kvi = linear(img, wts["ca_wkv_img"], wts["ca_bkv_img"])
+        out = out + (kvi[:, :d], kvi[:, d:])
+    return out
+

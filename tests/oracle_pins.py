@@ -393,3 +393,69 @@ def pin_step(O):
     out = O.step(lat, t, ctx, mw, H)
     out1 = O.step(lat[1:], t[1:], ctx[1:], mw, H)
     _close(out1[0], out[1], 1e-9, "step batch independence")
+
+
+# ---------------------------------------------------------------- sampler
+def pin_sampler(O):
+    """Euler along the flow x_tau = tau x1 + (1 - tau) x0 ([Note, 训练方法]):
+    the exact conditional velocity (x1 - x)/(1 - tau), evaluated at the model
+    timestep t = 1000 tau, keeps Euler on the straight line, so N steps land
+    on x1 for every N; a constant velocity c moves x0 by exactly c; the I2V
+    channels beyond the first 16 never move; the guided field of a
+    conditional / unconditional pair lands on x1u + s (x1c - x1u)."""
+    r = _rng(40)
+    for cin in (16, 36):
+        x0 = r.standard_normal((1, cin, 2, 4, 6))
+        x1 = r.standard_normal((1, 16, 2, 4, 6))
+        vel = lambda x, t: (x1 - x[:, :16]) / (1.0 - t[:, None, None, None, None] / 1000.0)
+        for n in (1, 3, 50):
+            with np.errstate(divide="ignore", invalid="ignore"):   # a wrong time grid may hit tau = 1
+                out = O.sample(x0, n, vel)
+            _close(out[:, :16], x1, 1e-10, f"straight-path Euler, N={n}, Cin={cin}")
+            assert np.array_equal(out[:, 16:], x0[:, 16:]), "I2V channels moved"
+        c = r.standard_normal((1, 16, 2, 4, 6))
+        out = O.sample(x0, 7, lambda x, t: np.broadcast_to(c, (1,) + c.shape[1:]))
+        _close(out[:, :16], x0[:, :16] + c, 1e-12, "constant velocity")
+    tau, tm = O.sampler_times(4)
+    _close(tau, [0, 0.25, 0.5, 0.75, 1.0], 0, "tau grid")
+    _close(tm, [0, 250, 500, 750], 0, "model timesteps")
+    # guidance: closed forms of the combine, then the guided straight path
+    vc, vu = r.standard_normal(5), r.standard_normal(5)
+    _close(O.cfg_combine(vc, vu, 0.0), vu, 0, "guidance 0")
+    _close(O.cfg_combine(vc, vu, 1.0), vc, 1e-15, "guidance 1")
+    _close(O.cfg_combine(vc, vu, 5.0), 5 * vc - 4 * vu, 1e-12, "guidance 5")
+    x0 = np.repeat(r.standard_normal((1, 16, 2, 4, 6)), 2, axis=0)
+    x1c, x1u = r.standard_normal((16, 2, 4, 6)), r.standard_normal((16, 2, 4, 6))
+
+    def pair(x, t):
+        den = 1.0 - t[0] / 1000.0
+        return np.stack([(x1c - x[0, :16]) / den, (x1u - x[1, :16]) / den])
+
+    for s in (0.0, 1.0, 5.0):
+        out = O.sample(x0, 10, pair, guidance=s)
+        _close(out[0], x1u + s * (x1c - x1u), 1e-10, f"guided path, s={s}")
+        assert np.array_equal(out[0], out[1]), "guided pair diverged"
+
+
+def pin_text_kv(O):
+    """The cached cross-attention keys / values are the K / V halves of the
+    block's KV projection (torch Linear), and cross_attention with them is the
+    block's cross-attention (multihead attention over those K, V)."""
+    r = _rng(41)
+    d, Lc, Li, L, H = 32, 6, 5, 9, 2
+    w = {"ca_wkv": r.standard_normal((2 * d, d)) * 0.2, "ca_bkv": r.standard_normal(2 * d) * 0.2,
+         "ca_wkv_img": r.standard_normal((2 * d, d)) * 0.2, "ca_bkv_img": r.standard_normal(2 * d) * 0.2}
+    ctx, img = r.standard_normal((Lc, d)), r.standard_normal((Li, d))
+    k, v, ki, vi = O.text_kv(ctx, w, img)
+    kv = TF.linear(_t(ctx), _t(w["ca_wkv"]), _t(w["ca_bkv"])).numpy()
+    _close(k, kv[:, :d], 1e-12, "text K")
+    _close(v, kv[:, d:], 1e-12, "text V")
+    kvi = TF.linear(_t(img), _t(w["ca_wkv_img"]), _t(w["ca_bkv_img"])).numpy()
+    _close(ki, kvi[:, :d], 1e-12, "image K")
+    _close(vi, kvi[:, d:], 1e-12, "image V")
+    wq, bq = r.standard_normal((d, d)) * 0.2, r.standard_normal(d) * 0.2
+    wo, bo = r.standard_normal((d, d)) * 0.2, r.standard_normal(d) * 0.2
+    xq = r.standard_normal((L, d))
+    ca = O.cross_attention(xq, ctx, wq, bq, w["ca_wkv"], w["ca_bkv"], wo, bo, H)
+    q = O.linear(O.layer_norm(xq), wq, bq)
+    _close(ca, O.linear(O.multihead(q, k, v, H), wo, bo), 1e-12, "CA from cached K/V")

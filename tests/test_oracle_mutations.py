@@ -36,6 +36,12 @@ MUTATIONS = {
     "sinusoid base": ("math.log(10000.0)", "math.log(1000.0)"),
     "LN on modulated input for CA": ("q = linear(layer_norm(xq, eps), wq, bq)", "q = linear(xq, wq, bq)"),
     "seq_len off by one": ("return (1 + T // 4) * (height // 16)", "return (T // 4) * (height // 16)"),
+    "Euler step sign": ("x[:, :out_ch] = x[:, :out_ch] + (tau[k + 1] - tau[k]) * v",
+                        "x[:, :out_ch] = x[:, :out_ch] - (tau[k + 1] - tau[k]) * v"),
+    "model time reversed": ("return tau, 1000.0 * tau[:-1]", "return tau, 1000.0 * (1.0 - tau[:-1])"),
+    "guidance pair order": ("g = cfg_combine(v[0], v[1], guidance)", "g = cfg_combine(v[1], v[0], guidance)"),
+    "guidance base": ("return vu + F64(scale) * (vc - vu)", "return vc + F64(scale) * (vc - vu)"),
+    "text V from K": ("out = (kv[:, :d], kv[:, d:])", "out = (kv[:, :d], kv[:, :d])"),
     "head split strided": ("k[:, h * hd:(h + 1) * hd],\n                                     v[:, h * hd:(h + 1) * hd])",
                            "k[:, h::heads],\n                                     v[:, h::heads])"),
 }
