@@ -122,6 +122,71 @@ def traffic_pass(W, B, L, d, H, dev):
     print(json.dumps({"traffic_pass": "done", "copy_bytes": 512 << 20}), flush=True)
 
 
+def sampler_bench(n_steps: int, warmup: int):
+    """Sampler steps of the 1.3B guidance pair at 480P (30 blocks, B = 2:
+    conditional and unconditional contexts, one latent): wan_sample_fwd with
+    the cross-attention K/V cache against the plain path (wan_dit_step_fwd,
+    which projects the text K/V in every block, + wan_euler_fwd)."""
+    import torch
+
+    import synth
+    import video_diffusion_transformer_block_amd as W
+    work = synth.CONFIGS[3]
+    m = work.model
+    B, L = work.batch, work.L
+    cfg = W.make_cfg(dim=m.dim, heads=m.heads, ffn=m.ffn, n_blocks=m.n_blocks, in_ch=m.in_ch,
+                     out_ch=m.out_ch, freq_dim=m.freq_dim, text_len=m.text_len, eps=m.eps,
+                     dtype=m.dtype)
+    mw = synth.device_model_weights(work)
+    mws, keep = W.model_weights(mw, [W.block_weights(b) for b in mw["blocks"]])
+    inp = synth.workload_inputs(work)
+    lat0 = torch.from_numpy(inp["latent"][:1].repeat(B, 0)).cuda()
+    ctx = torch.from_numpy(inp["ctx"]).to(torch.bfloat16).cuda()
+    ws = torch.empty(W.sample_workspace_bytes(cfg, B, work.lat_f, work.lat_h, work.lat_w),
+                     dtype=torch.uint8, device="cuda")
+    cache = torch.empty(W.kv_cache_bytes(cfg, B), dtype=torch.uint8, device="cuda")
+    vel = torch.empty((B, 16) + tuple(lat0.shape[2:]), dtype=torch.float32, device="cuda")
+    tb = torch.zeros(B, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    fill_ms = [timed(lambda: W.kv_cache_fwd(cfg, B, ctx, None, mws, cache, ws, stream))
+               for _ in range(3)][-1]
+    lat = lat0.clone()
+    W.sample_fwd(cfg, lat, warmup, cache, mws, ws, True, 5.0, stream)
+    lat = lat0.clone()
+    cached_ms = timed(lambda: W.sample_fwd(cfg, lat, n_steps, cache, mws, ws, True, 5.0, stream))
+
+    def plain():
+        for k in range(n_steps):
+            tb.fill_(1000.0 * k / n_steps)
+            W.dit_step_fwd(cfg, lat, tb, ctx, None, mws, vel, ws, stream)
+            W.euler_fwd(lat, vel, 1.0 / n_steps, True, 5.0, stream)
+
+    lat = lat0.clone()
+    plain_ms = timed(plain)
+    if not bool(torch.isfinite(lat).all()):
+        raise RuntimeError("non-finite sample")
+    per_c, per_p = cached_ms / n_steps, plain_ms / n_steps
+    print(json.dumps({
+        "sampler": "wan1.3b-480p guidance pair (30 blocks, B=2, L=32760, 512 text tokens)",
+        "steps": n_steps, "guidance": 5.0,
+        "ms_per_step_cached": round(per_c, 3), "ms_per_step_plain": round(per_p, 3),
+        "kv_cache_fill_ms": round(fill_ms, 3),
+        "saving_per_step_ms": round(per_p - per_c, 3),
+        "latent_tokens_per_s_cached": round(B * L / (per_c * 1e-3), 1),
+        "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latent and text)",
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +194,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", type=int, default=2, help="block workload id (2: 1.3B, 4: 14B)")
+    ap.add_argument("--sampler", type=int, default=0, metavar="STEPS",
+                    help="time STEPS sampler steps of the 1.3B guidance pair with and without the "
+                         "cross-attention K/V cache (prints its own JSON line) instead of the block")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="only run 3 self-attention launches and 3 plain 512-MiB device copies "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and their calibration)")
@@ -140,6 +208,10 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.sampler:
+        sampler_bench(args.sampler, max(1, args.warmup))
+        return
 
     import numpy as np
     import torch

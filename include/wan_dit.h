@@ -8,6 +8,8 @@
  *          配置表, I2V 架构扩展, 训练方法.
  *   [News] "超越Sora！阿里正式完全开源最新、最强大的视频生成模型 Wan2.1",
  *          sections 核心创新二 (视频扩散 DiT) and 核心创新四 (Image-to-Video).
+ *   [Guide] "Wan 2.1 AI：下一代开源视频生成技术的突破性实践", section 工作原理
+ *          (the sampling knobs: number of inference steps, guidance scale).
  *
  * Conventions shared by every entry point
  *   - Row-major.  Linear weights are [out, in] (y = x W^T + b), so both GEMM
@@ -151,6 +153,69 @@ int wan_dit_step_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, 
  * temporal stride) and the position within the group is the channel.
  * Requires n_frames = 4*(lat_f-1)+1.  Touches no device. */
 int wan_i2v_mask(const uint8_t *frame_mask, int n_frames, int lat_f, int H8, int W8, float *out);
+
+/* ---- sampler around the step -------------------------------------------- */
+/* [Note] 训练方法: the flow x_tau = tau x1 + (1 - tau) x0 runs from noise x0
+ * (tau = 0) to data x1 (tau = 1) with velocity x1 - x0, which the step
+ * predicts; [Note] Infra (推理优化): about 50 sampling steps, work that does
+ * not change between steps is reused; [Guide] 工作原理: step count and
+ * guidance scale.  Integration: explicit Euler on tau_k = k / n_steps with the
+ * model's timestep input 1000 tau_k; guidance v = v_u + s (v_c - v_u). */
+
+/* Bytes of the cross-attention key / value cache for B samples: per block the
+ * text keys [B*text_len, d] and V^T [d, B*round_up(text_len, 64)] (for I2V
+ * also the image pair), in cfg->dtype, each region 256-byte aligned.  The
+ * float32 path stores keys and values side by side ([B*len, 2d], no V^T).
+ * 0 for an invalid configuration or B outside 1..8. */
+size_t wan_kv_cache_bytes(const wan_cfg_t *cfg, int B);
+
+/* Fill the cache: for every block, the keys and V^T of the text context
+ * ctx [B, text_len, d] (device) and, for I2V, of the image context (the image
+ * MLP of clip_feat [B, img_len, img_feat], device; NULL for T2V).  These
+ * depend only on the contexts and the weights, so a sampler fills the cache
+ * once and every step reads it.  cache (device, cache_bytes >=
+ * wan_kv_cache_bytes) is written; ws (device) holds the image MLP's
+ * temporaries: at least 3 regions of round_up(B*img_len*d*elem, 256) bytes
+ * for I2V (any step workspace of the same B is large enough); unused (may be
+ * NULL) for T2V.  Errors: WAN_ERR_WORKSPACE for a short cache or ws,
+ * WAN_ERR_CONFIG when clip_feat does not match cfg->img_len. */
+int wan_kv_cache_fwd(const wan_cfg_t *cfg, int B, const void *ctx, const void *clip_feat,
+                     const wan_model_weights_t *w, void *cache, size_t cache_bytes, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* wan_dit_step_fwd with the cross-attention keys / values read from a cache
+ * that wan_kv_cache_fwd filled for the same cfg, B and weights (the image
+ * MLP weights are not read).  Same latent, t, out and workspace contract as
+ * wan_dit_step_fwd; its output equals wan_dit_step_fwd's bit for bit. */
+int wan_dit_step_cached_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, int B,
+                            int lat_f, int H8, int W8, const void *kv_cache, size_t cache_bytes,
+                            const wan_model_weights_t *w, float *out, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* One Euler step on the moving channels: latent [B, in_ch, lat_f, H8, W8]
+ * float32 device, channels 0..out_ch-1 updated in place, the rest (I2V
+ * condition and mask) untouched; vel [B, out_ch, lat_f, H8, W8] float32
+ * device.  guided == 0: latent[b] += dt * vel[b] for every sample.
+ * guided != 0: B must be 2 (sample 0 conditional, 1 unconditional, same
+ * latent); both samples become latent[0] + dt * (vel[1] + scale (vel[0] - vel[1])).
+ * WAN_ERR_SHAPE for in_ch < out_ch, guided with B != 2, or non-finite dt / scale. */
+int wan_euler_fwd(float *latent, const float *vel, int B, int in_ch, int out_ch, int lat_f, int H8,
+                  int W8, float dt, int guided, float scale, void *stream);
+
+/* Workspace of wan_sample_fwd: the step workspace plus the timestep [B] and
+ * velocity [B, out_ch, lat_f, H8, W8] buffers.  0 on invalid arguments. */
+size_t wan_sample_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, int W8);
+
+/* The whole sampler: n_steps evaluations of the step (cross-attention K/V
+ * from kv_cache, filled by wan_kv_cache_fwd for the same B), each followed by
+ * wan_euler_fwd with dt = 1/n_steps, timestep input 1000 k / n_steps for
+ * step k.  latent [B, in_ch, lat_f, H8, W8] float32 device: on entry the
+ * noise (tau = 0) in channels 0..out_ch-1 (+ I2V condition and mask), on
+ * return the sample at tau = 1.  guided / scale as in wan_euler_fwd (the
+ * pair's two latents must be equal on entry). */
+int wan_sample_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, int H8, int W8,
+                   int n_steps, int guided, float scale, const void *kv_cache, size_t cache_bytes,
+                   const wan_model_weights_t *w, void *ws, size_t ws_bytes, void *stream);
 
 /* ---- component entry points (the kernels the block is made of) ---------- */
 

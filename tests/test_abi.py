@@ -1,0 +1,106 @@
+"""The C ABI on the host (no GPU needed): libwandit.so loads and exports every
+function include/wan_dit.h declares; the host-only entry points (status
+strings, workspace / cache sizing, the I2V mask helper) behave as declared;
+invalid arguments are rejected before anything is enqueued."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.wan_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wan_dit.h")
+
+
+def _declared():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w \*]*?\b(wan_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def W():
+    import video_diffusion_transformer_block_amd as W
+    W.lib()   # raises if the library has not been built
+    return W
+
+
+def test_every_declared_symbol_is_exported(W):
+    names = _declared()
+    assert len(names) >= 14, names
+    L = C.CDLL(W.binding.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(names) == set(W.binding.EXPORTS), "binding EXPORTS out of date with the header"
+
+
+def test_status_strings(W):
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert W.status_str(st) and W.status_str(st) != "unknown status"
+    assert W.status_str(-99) == "unknown status"
+
+
+def _cfg(W, **kw):
+    base = dict(dim=256, heads=2, ffn=512, n_blocks=3, text_len=40, dtype="bf16")
+    base.update(kw)
+    return W.make_cfg(**base)
+
+
+def test_workspace_and_cache_sizes(W):
+    c = _cfg(W)
+    ws = W.workspace_bytes(c, 2, 3, 8, 12)
+    assert ws > 0 and ws % 256 == 0
+    # sampler workspace = step workspace + timestep and velocity buffers
+    sw = W.sample_workspace_bytes(c, 2, 3, 8, 12)
+    assert sw == ws + 256 + (2 * 16 * 3 * 8 * 12 * 4 + 255) // 256 * 256
+    # cache: per block text K [B*Lc, d] and V^T [d, B*round_up(Lc, 64)] in bf16
+    per = (2 * 40 * 256 * 2 + 255) // 256 * 256 + 256 * 2 * 64 * 2
+    assert W.kv_cache_bytes(c, 2) == 3 * per
+    ci = _cfg(W, in_ch=36, img_len=257, img_feat=1280)
+    assert W.kv_cache_bytes(ci, 1) > W.kv_cache_bytes(_cfg(W, in_ch=36), 1)
+    # invalid configurations size to 0
+    assert W.workspace_bytes(_cfg(W, heads=3), 1, 1, 8, 8) == 0        # head_dim != 128
+    assert W.workspace_bytes(c, 1, 1, 7, 8) == 0                        # odd H8
+    assert W.workspace_bytes(c, 9, 1, 8, 8) == 0                        # B > 8
+    assert W.kv_cache_bytes(c, 0) == 0
+    assert W.sample_workspace_bytes(_cfg(W, ffn=500), 1, 1, 8, 8) == 0  # ffn % 64
+
+
+def test_i2v_mask_matches_oracle(W):
+    rng = np.random.default_rng(3)
+    for n in (1, 5, 81):
+        lat_f = (n - 1) // 4 + 1
+        fm = rng.integers(0, 2, n)
+        fm[0] = 1
+        got = W.i2v_mask(fm.tolist(), lat_f, 6, 4).numpy()
+        assert np.array_equal(got, O.i2v_mask(fm, lat_f, 6, 4).astype(np.float32))
+    with pytest.raises(W.WanError):
+        W.i2v_mask([1] * 6, 2, 4, 4)      # 6 frames is not 4k+1
+
+
+def test_invalid_arguments_enqueue_nothing(W):
+    L = W.lib()
+    c = _cfg(W)
+    dummy = C.c_void_p(16)   # never dereferenced: every call below fails validation first
+    # guidance needs a pair; in_ch < out_ch; non-finite dt
+    assert L.wan_euler_fwd(dummy, dummy, 3, 16, 16, 1, 2, 2, 0.1, 1, 1.0, None) == -2
+    assert L.wan_euler_fwd(dummy, dummy, 2, 8, 16, 1, 2, 2, 0.1, 0, 1.0, None) == -2
+    assert L.wan_euler_fwd(dummy, dummy, 1, 16, 16, 1, 2, 2, float("nan"), 0, 1.0, None) == -2
+    assert L.wan_euler_fwd(None, dummy, 1, 16, 16, 1, 2, 2, 0.1, 0, 1.0, None) == -1
+    mw, keep = W.model_weights({"patch_w": None, "patch_b": None, "tmlp": {"w1": None, "b1": None,
+                                "w2": None, "b2": None}, "head_w": None, "head_b": None}, [])
+    # NULL weights, zero steps, short cache / workspace
+    assert L.wan_sample_fwd(C.byref(c), dummy, 2, 3, 8, 12, 4, 1, 5.0, dummy, 1 << 30, C.byref(mw),
+                            dummy, 1 << 40, None) == -1
+    assert L.wan_sample_fwd(C.byref(c), dummy, 2, 3, 8, 12, 0, 1, 5.0, dummy, 1 << 30, C.byref(mw),
+                            dummy, 1 << 40, None) == -2
+    assert L.wan_kv_cache_fwd(C.byref(c), 2, None, None, C.byref(mw), dummy, 1 << 30, None, 0,
+                              None) == -1
+    assert L.wan_dit_step_cached_fwd(C.byref(c), dummy, dummy, 2, 3, 7, 12, dummy, 1 << 30,
+                                     C.byref(mw), dummy, dummy, 1 << 40, None) == -2   # odd H8
+    assert L.wan_attention_fwd(dummy, 100, dummy, 256, dummy, 64, 64, dummy, 256, 1, 2, 4, 4,
+                               None) == -2                                          # ldq < H*128
+    assert L.wan_linear_fwd(dummy, dummy, None, dummy, 4, 4, 100, 0, None) == -2   # K % 64

@@ -60,6 +60,28 @@ def test_c3_step_batch_independence_and_determinism():
     assert not torch.equal(out2[0], out2[1])
 
 
+def test_c3_cached_step_equals_plain_step_bitwise():
+    """The 30-block 1.3B guidance pair: the step with the cross-attention K/V
+    from the cache equals the plain step bit for bit."""
+    import video_diffusion_transformer_block_amd as W
+    from tests.gpu_util import cfg_of
+    work = synth.CONFIGS[3]
+    print(f"C3 cached step: B=2, L={work.L}, {work.model.n_blocks} blocks", flush=True)
+    cfg = cfg_of(work)
+    mw = synth.device_model_weights(work)
+    lat, t, ctx, _ = _inputs(work, 2)
+    out = _run(work, mw, lat, t, ctx, None)
+    mws, keep = W.model_weights(mw, [W.block_weights(b) for b in mw["blocks"]])
+    ws = torch.empty(W.workspace_bytes(cfg, 2, work.lat_f, work.lat_h, work.lat_w),
+                     dtype=torch.uint8, device="cuda")
+    cache = torch.empty(W.kv_cache_bytes(cfg, 2), dtype=torch.uint8, device="cuda")
+    W.kv_cache_fwd(cfg, 2, ctx, None, mws, cache, ws)
+    out_c = torch.empty_like(out)
+    W.dit_step_cached_fwd(cfg, lat, t, cache, mws, out_c, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_c), "cached cross-attention K/V changed the 1.3B step"
+
+
 def test_c5_step_zero_projection_and_identity():
     work = synth.CONFIGS[5]
     m = work.model

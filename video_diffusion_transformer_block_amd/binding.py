@@ -19,8 +19,10 @@ LIB_PATH = os.environ.get("WANDIT_LIB") or os.path.join(_HERE, "libwandit.so")
 
 WAN_F32, WAN_BF16 = 0, 1
 
-EXPORTS = ("wan_workspace_bytes", "wan_status_str", "wan_tmlp_fwd", "wan_dit_block_fwd",
-           "wan_dit_step_fwd", "wan_i2v_mask", "wan_attention_fwd", "wan_linear_fwd")
+EXPORTS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
+           "wan_status_str", "wan_tmlp_fwd", "wan_dit_block_fwd", "wan_dit_step_fwd",
+           "wan_i2v_mask", "wan_attention_fwd", "wan_linear_fwd", "wan_kv_cache_fwd",
+           "wan_dit_step_cached_fwd", "wan_euler_fwd", "wan_sample_fwd")
 
 
 class WanError(RuntimeError):
@@ -78,8 +80,20 @@ def lib() -> C.CDLL:
         L.wan_i2v_mask.argtypes = [vp, i, i, i, i, vp]
         L.wan_attention_fwd.argtypes = [vp, i, vp, i, vp, i, i, vp, i, i, i, i, i, vp]
         L.wan_linear_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
-        for n in EXPORTS[2:]:
-            getattr(L, n).restype = i
+        L.wan_kv_cache_bytes.argtypes = [C.POINTER(Cfg), i]
+        L.wan_kv_cache_bytes.restype = sz
+        L.wan_sample_workspace_bytes.argtypes = [C.POINTER(Cfg), i, i, i, i]
+        L.wan_sample_workspace_bytes.restype = sz
+        L.wan_kv_cache_fwd.argtypes = [C.POINTER(Cfg), i, vp, vp, C.POINTER(ModelW), vp, sz, vp, sz, vp]
+        L.wan_dit_step_cached_fwd.argtypes = [C.POINTER(Cfg), vp, vp, i, i, i, i, vp, sz,
+                                              C.POINTER(ModelW), vp, vp, sz, vp]
+        L.wan_euler_fwd.argtypes = [vp, vp, i, i, i, i, i, i, C.c_float, i, C.c_float, vp]
+        L.wan_sample_fwd.argtypes = [C.POINTER(Cfg), vp, i, i, i, i, i, i, C.c_float, vp, sz,
+                                     C.POINTER(ModelW), vp, sz, vp]
+        for n in EXPORTS:
+            if n not in ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
+                         "wan_status_str"):
+                getattr(L, n).restype = i
         _lib = L
     return _lib
 
@@ -179,3 +193,51 @@ def i2v_mask(frame_mask: Sequence[int], lat_f: int, H8: int, W8: int):
     _check("wan_i2v_mask", lib().wan_i2v_mask(C.cast(fm, C.c_void_p), len(frame_mask), lat_f, H8, W8,
                                               _p(out)))
     return out
+
+
+# ---- sampler around the step
+
+def kv_cache_bytes(cfg: Cfg, B: int) -> int:
+    return int(lib().wan_kv_cache_bytes(C.byref(cfg), B))
+
+
+def sample_workspace_bytes(cfg: Cfg, B: int, lat_f: int, H8: int, W8: int) -> int:
+    return int(lib().wan_sample_workspace_bytes(C.byref(cfg), B, lat_f, H8, W8))
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def kv_cache_fwd(cfg: Cfg, B: int, ctx: torch.Tensor, clip: Optional[torch.Tensor], mw: ModelW,
+                 cache: torch.Tensor, ws: Optional[torch.Tensor], stream=None):
+    _check("wan_kv_cache_fwd",
+           lib().wan_kv_cache_fwd(C.byref(cfg), B, _p(ctx), _p(clip), C.byref(mw), _p(cache),
+                                  _nbytes(cache), _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def dit_step_cached_fwd(cfg: Cfg, latent: torch.Tensor, t: torch.Tensor, cache: torch.Tensor,
+                        mw: ModelW, out: torch.Tensor, ws: torch.Tensor, stream=None):
+    B, _, F, H8, W8 = latent.shape
+    _check("wan_dit_step_cached_fwd",
+           lib().wan_dit_step_cached_fwd(C.byref(cfg), _p(latent), _p(t), B, F, H8, W8, _p(cache),
+                                         _nbytes(cache), C.byref(mw), _p(out), _p(ws), _nbytes(ws),
+                                         _stream(stream)))
+
+
+def euler_fwd(latent: torch.Tensor, vel: torch.Tensor, dt: float, guided: bool = False,
+              scale: float = 1.0, stream=None):
+    B, cin, F, H8, W8 = latent.shape
+    _check("wan_euler_fwd",
+           lib().wan_euler_fwd(_p(latent), _p(vel), B, cin, vel.shape[1], F, H8, W8, dt,
+                               1 if guided else 0, scale, _stream(stream)))
+
+
+def sample_fwd(cfg: Cfg, latent: torch.Tensor, n_steps: int, cache: torch.Tensor, mw: ModelW,
+               ws: torch.Tensor, guided: bool = False, scale: float = 1.0, stream=None):
+    B, _, F, H8, W8 = latent.shape
+    _check("wan_sample_fwd",
+           lib().wan_sample_fwd(C.byref(cfg), _p(latent), B, F, H8, W8, n_steps, 1 if guided else 0,
+                                scale, _p(cache), _nbytes(cache), C.byref(mw), _p(ws), _nbytes(ws),
+                                _stream(stream)))
+

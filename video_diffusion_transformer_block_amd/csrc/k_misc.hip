@@ -196,4 +196,51 @@ hipError_t launch_head_unpatchify(const float *x, int B, int F, int Hp, int Wp, 
   return hipGetLastError();
 }
 
+// ---- sampler ("Wan: Open and Advanced Large-Scale Video Generative Models
+// (Wan 2.1)", section 训练方法: the flow x_tau = tau x1 + (1 - tau) x0 with
+// velocity x1 - x0, integrated here by explicit Euler steps; "Wan 2.1 AI：下一代
+// 开源视频生成技术的突破性实践", section 工作原理: the guidance scale)
+
+__global__ void k_fill(float *__restrict__ p, int n, float v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill(float *p, int n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_fill<<<(n + 255) / 256, 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+// x += dt * v on channels 0..out_ch-1 of every sample (latent [B, in_ch,
+// plane], velocity [B, out_ch, plane]).  guided: B == 2, sample 0 is the
+// conditional and sample 1 the unconditional prediction for the same latent;
+// both samples receive x0 + dt * (v1 + s (v0 - v1)).
+__global__ __launch_bounds__(256) void k_euler(float *__restrict__ lat, const float *__restrict__ vel,
+                                               int B, int in_ch, int out_ch, long plane, float dt,
+                                               int guided, float scale) {
+  const long n = (long)out_ch * plane;   // moving elements per sample
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const long ls = (long)in_ch * plane;   // latent sample stride
+  if (guided) {
+    const float vc = vel[e], vu = vel[n + e];
+    const float v = vu + scale * (vc - vu);
+    const float x = lat[e] + dt * v;
+    lat[e] = x;
+    lat[ls + e] = x;
+  } else {
+    for (int b = 0; b < B; ++b) lat[b * ls + e] += dt * vel[b * n + e];
+  }
+}
+
+hipError_t launch_euler(float *lat, const float *vel, int B, int in_ch, int out_ch, long plane,
+                        float dt, int guided, float scale, hipStream_t s) {
+  const long n = (long)out_ch * plane;
+  if (n <= 0) return hipSuccess;
+  k_euler<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(lat, vel, B, in_ch, out_ch, plane, dt, guided,
+                                                      scale);
+  return hipGetLastError();
+}
+
 }  // namespace wan

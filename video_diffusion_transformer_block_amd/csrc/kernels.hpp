@@ -53,5 +53,8 @@ hipError_t launch_head_unpatchify(const float *x, int B, int F, int Hp, int Wp, 
                                   const void *w, const void *b, int out_ch, float *out, int f32,
                                   hipStream_t s);
 hipError_t launch_pad_rows(const void *src, int R, int K, int Kp, void *dst, int f32, hipStream_t s);
+hipError_t launch_fill(float *p, int n, float v, hipStream_t s);
+hipError_t launch_euler(float *lat, const float *vel, int B, int in_ch, int out_ch, long plane,
+                        float dt, int guided, float scale, hipStream_t s);
 
 }  // namespace wan

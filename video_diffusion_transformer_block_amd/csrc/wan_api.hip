@@ -74,6 +74,32 @@ Layout make_layout(const wan_cfg_t &c, int B, long L, bool step) {
   return y;
 }
 
+// Cross-attention K/V cache: one region per block holding the text keys and
+// V^T (and, for I2V, the image pair) exactly as the block would project them.
+struct KvLayout {
+  size_t kc, vtc, ki, vti, per_block;
+};
+
+KvLayout kv_layout(const wan_cfg_t &c, int B) {
+  KvLayout k;
+  const bool f32 = c.dtype == WAN_F32;
+  const size_t es = f32 ? 4 : 2;
+  const long d = c.dim, Lc = c.text_len, Li = c.img_len;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up(bytes, ALIGN); return o; };
+  k.kc = take(B * Lc * (f32 ? 2 : 1) * d * es);
+  k.vtc = take(f32 ? 0 : d * B * rup(Lc, 64) * es);
+  k.ki = take(Li ? B * Li * (f32 ? 2 : 1) * d * es : 0);
+  k.vti = take(Li && !f32 ? d * B * rup(Li, 64) * es : 0);
+  k.per_block = off;
+  return k;
+}
+
+// where a block finds its cross-attention keys / values
+struct KvPtrs {
+  const void *kc, *vtc, *ki, *vti;
+};
+
 int check_cfg(const wan_cfg_t *c) {
   if (!c) return WAN_ERR_NULL;
   if (c->dtype != WAN_F32 && c->dtype != WAN_BF16) return WAN_ERR_DTYPE;
@@ -160,9 +186,11 @@ AttnDesc attn(const void *q, long ldq, const void *k, long ldk, const void *v, l
   return a;
 }
 
+// One block.  Cross-attention keys / values come from `cached` when it is
+// given, else they are projected from ctx (and img) into the workspace.
 int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
-              const wan_block_weights_t &w, const void *ctx, const void *img, char *ws,
-              const Layout &y, hipStream_t s) {
+              const wan_block_weights_t &w, const void *ctx, const void *img, const KvPtrs *cached,
+              char *ws, const Layout &y, hipStream_t s) {
   const int d = c.dim, F = c.ffn, H = c.heads, hd = c.head_dim, Lc = c.text_len, Li = c.img_len;
   const int f32 = c.dtype == WAN_F32;
   const size_t es = f32 ? 4 : 2;
@@ -197,14 +225,21 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
   // ---- cross-attention branch (pre-LN without modulation, ungated)
   WAN_TRY(launch_ln_mod(x, M, (int)L, d, modb, 6 * d, 0, 0, 0, c.eps, h, f32, s));
   WAN_TRY(launch_gemm(gemm(h, d, w.ca_wq, d, M, d, d, w.ca_bq, OUT_BF16, qc, d, f32), s));
-  int st = kv_project(c, B, Lc, ctx, w.ca_wkv, w.ca_bkv, kc, vtc, y.Lcp, s);
-  if (st) return st;
+  int st;
+  if (cached) {
+    kc = (char *)cached->kc; vtc = (char *)cached->vtc; ki = (char *)cached->ki; vti = (char *)cached->vti;
+  } else {
+    st = kv_project(c, B, Lc, ctx, w.ca_wkv, w.ca_bkv, kc, vtc, y.Lcp, s);
+    if (st) return st;
+  }
   const long kld = f32 ? 2 * d : d;
   AttnDesc at = f32 ? attn(qc, d, kc, kld, off(kc, d, es), kld, 0, o, d, B, H, (int)L, Lc, hd, 1)
                     : attn(qc, d, kc, kld, vtc, (long)B * y.Lcp, y.Lcp, o, d, B, H, (int)L, Lc, hd, 0);
   if (Li > 0) {
-    st = kv_project(c, B, Li, img, w.ca_wkv_img, w.ca_bkv_img, ki, vti, y.Lip, s);
-    if (st) return st;
+    if (!cached) {
+      st = kv_project(c, B, Li, img, w.ca_wkv_img, w.ca_bkv_img, ki, vti, y.Lip, s);
+      if (st) return st;
+    }
     at.out_mode = 1;
     at.acc32 = acc32;
     WAN_TRY(launch_attention(at, s));
@@ -234,6 +269,88 @@ int check_block_weights(const wan_cfg_t &c, const wan_block_weights_t *w) {
     if (!p) return WAN_ERR_NULL;
   if (c.img_len > 0 && (!w->ca_wkv_img || !w->ca_bkv_img)) return WAN_ERR_CONFIG;
   return WAN_OK;
+}
+
+// I2V image context: three Linear layers with GELU between them
+// ([Note] I2V 架构扩展: CLIP features through a 3-layer MLP); returns its
+// [B*Li, d] output in the workspace regions img1 / img2 / imgc.
+int image_context(const wan_cfg_t &c, int B, const void *clip, const wan_model_weights_t &w,
+                  char *img1, char *img2, char *imgc, hipStream_t s) {
+  const int d = c.dim, f32 = c.dtype == WAN_F32;
+  const int Mi = B * c.img_len;
+  WAN_TRY(launch_gemm(gemm(clip, c.img_feat, w.img_w1, c.img_feat, Mi, d, c.img_feat, w.img_b1,
+                           OUT_GELU, img1, d, f32), s));
+  WAN_TRY(launch_gemm(gemm(img1, d, w.img_w2, d, Mi, d, d, w.img_b2, OUT_GELU, img2, d, f32), s));
+  WAN_TRY(launch_gemm(gemm(img2, d, w.img_w3, d, Mi, d, d, w.img_b3, OUT_BF16, imgc, d, f32), s));
+  return WAN_OK;
+}
+
+// every weight the step reads (image MLP only when `need_img`)
+int check_model_weights(const wan_cfg_t &c, const wan_model_weights_t *w, bool need_img) {
+  if (!w) return WAN_ERR_NULL;
+  if (!w->patch_w || !w->patch_b || !w->head_w || !w->head_b || !w->tmlp.w1 || !w->tmlp.b1 ||
+      !w->tmlp.w2 || !w->tmlp.b2)
+    return WAN_ERR_NULL;
+  if (c.n_blocks > 0 && !w->blocks) return WAN_ERR_NULL;
+  int st;
+  for (int i = 0; i < c.n_blocks; ++i)
+    if ((st = check_block_weights(c, &w->blocks[i]))) return st;
+  if (need_img && (!w->img_w1 || !w->img_b1 || !w->img_w2 || !w->img_b2 || !w->img_w3 || !w->img_b3))
+    return WAN_ERR_CONFIG;
+  return WAN_OK;
+}
+
+// patchify -> t-MLP -> (image context) -> blocks -> head + unpatchify.  With
+// `cache` the blocks read their cross-attention K/V from it (ctx / clip unused).
+int step_run(const wan_cfg_t &c, const float *latent, const float *t, int B, int lat_f, int H8,
+             int W8, const void *ctx, const void *clip, const char *cache,
+             const wan_model_weights_t &w, float *out, char *wsb, const Layout &y, hipStream_t s) {
+  const int d = c.dim, f32 = c.dtype == WAN_F32;
+  const int Hp = H8 / 2, Wp = W8 / 2;
+  const long L = (long)lat_f * Hp * Wp;
+  float *x = reinterpret_cast<float *>(wsb + y.x);
+  float *mod = reinterpret_cast<float *>(wsb + y.mod);
+  const int M = (int)(B * L);
+  // patchify: gather the (1,2,2) patches, then one GEMM against the padded Conv3d weight
+  WAN_TRY(launch_patch_gather(latent, B, c.in_ch, lat_f, H8, W8, y.Kp, wsb + y.P, f32, s));
+  WAN_TRY(launch_pad_rows(w.patch_w, d, 4 * c.in_ch, y.Kp, wsb + y.pw, f32, s));
+  WAN_TRY(launch_gemm(gemm(wsb + y.P, y.Kp, wsb + y.pw, y.Kp, M, d, y.Kp, w.patch_b, OUT_F32, x, d,
+                           f32), s));
+  // shared timestep MLP
+  WAN_TRY(launch_tmlp(t, B, c.freq_dim, d, w.tmlp.w1, w.tmlp.b1, w.tmlp.w2, w.tmlp.b2,
+                      reinterpret_cast<float *>(wsb + y.hid), mod, f32, s));
+  int st;
+  const void *img = nullptr;
+  if (c.img_len > 0 && !cache) {
+    if ((st = image_context(c, B, clip, w, wsb + y.img1, wsb + y.img2, wsb + y.imgc, s))) return st;
+    img = wsb + y.imgc;
+  }
+  const KvLayout kl = kv_layout(c, B);
+  for (int i = 0; i < c.n_blocks; ++i) {
+    KvPtrs kp;
+    const KvPtrs *pk = nullptr;
+    if (cache) {
+      const char *base = cache + (size_t)i * kl.per_block;
+      kp = {base + kl.kc, base + kl.vtc, base + kl.ki, base + kl.vti};
+      pk = &kp;
+    }
+    st = block_run(c, x, B, L, mod, w.blocks[i], ctx, img, pk, wsb, y, s);
+    if (st) return st;
+  }
+  WAN_TRY(launch_head_unpatchify(x, B, lat_f, Hp, Wp, d, w.head_w, w.head_b, c.out_ch, out, f32, s));
+  return WAN_OK;
+}
+
+// latent geometry of a step
+int check_step_dims(int B, int lat_f, int H8, int W8) {
+  if (H8 <= 0 || W8 <= 0 || H8 % 2 || W8 % 2) return WAN_ERR_SHAPE;
+  return check_dims(B, lat_f, H8 / 2, W8 / 2);
+}
+
+size_t sample_extra(int B, int out_ch, long plane, size_t *t_off, size_t *v_off, size_t base) {
+  *t_off = base;
+  *v_off = *t_off + up((size_t)B * 4, ALIGN);
+  return *v_off + up((size_t)B * out_ch * plane * 4, ALIGN);
 }
 
 }  // namespace
@@ -286,7 +403,7 @@ int wan_dit_block_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, 
   const long L = (long)lat_f * Hp * Wp;
   Layout y = make_layout(*cfg, B, L, false);
   if (ws_bytes < y.total) return WAN_ERR_WORKSPACE;
-  return block_run(*cfg, x, B, L, mod, *w, ctx, img_ctx, (char *)ws, y, S(stream));
+  return block_run(*cfg, x, B, L, mod, *w, ctx, img_ctx, nullptr, (char *)ws, y, S(stream));
 }
 
 int wan_dit_step_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, int B, int lat_f,
@@ -296,57 +413,126 @@ int wan_dit_step_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, 
   int st = check_cfg(cfg);
   if (st) return st;
   if (!latent || !t || !ctx || !w || !out || !ws) return WAN_ERR_NULL;
-  if (H8 <= 0 || W8 <= 0 || H8 % 2 || W8 % 2) return WAN_ERR_SHAPE;
-  if ((st = check_dims(B, lat_f, H8 / 2, W8 / 2))) return st;
-  if (!w->patch_w || !w->patch_b || !w->head_w || !w->head_b || !w->tmlp.w1 || !w->tmlp.b1 ||
-      !w->tmlp.w2 || !w->tmlp.b2)
-    return WAN_ERR_NULL;
-  if (cfg->n_blocks > 0 && !w->blocks) return WAN_ERR_NULL;
-  for (int i = 0; i < cfg->n_blocks; ++i)
-    if ((st = check_block_weights(*cfg, &w->blocks[i]))) return st;
+  if ((st = check_step_dims(B, lat_f, H8, W8))) return st;
   const bool i2v = cfg->img_len > 0;
+  if ((st = check_model_weights(*cfg, w, i2v))) return st;
   if (i2v != (clip_feat != nullptr)) return WAN_ERR_CONFIG;
-  if (i2v && (!w->img_w1 || !w->img_b1 || !w->img_w2 || !w->img_b2 || !w->img_w3 || !w->img_b3))
-    return WAN_ERR_CONFIG;
-  const int Hp = H8 / 2, Wp = W8 / 2;
-  const long L = (long)lat_f * Hp * Wp;
+  const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
   Layout y = make_layout(*cfg, B, L, true);
   if (ws_bytes < y.total) return WAN_ERR_WORKSPACE;
+  return step_run(*cfg, latent, t, B, lat_f, H8, W8, ctx, clip_feat, nullptr, *w, out, (char *)ws,
+                  y, S(stream));
+}
 
+size_t wan_kv_cache_bytes(const wan_cfg_t *cfg, int B) {
+  if (check_cfg(cfg) != WAN_OK || B <= 0 || B > 8) return 0;
+  return kv_layout(*cfg, B).per_block * (size_t)cfg->n_blocks;
+}
+
+int wan_kv_cache_fwd(const wan_cfg_t *cfg, int B, const void *ctx, const void *clip_feat,
+                     const wan_model_weights_t *w, void *cache, size_t cache_bytes, void *ws,
+                     size_t ws_bytes, void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (!ctx || !w || (!cache && cfg->n_blocks > 0)) return WAN_ERR_NULL;
+  if (B <= 0 || B > 8) return WAN_ERR_SHAPE;
+  const bool i2v = cfg->img_len > 0;
+  if ((st = check_model_weights(*cfg, w, i2v))) return st;
+  if (i2v != (clip_feat != nullptr)) return WAN_ERR_CONFIG;
+  const KvLayout kl = kv_layout(*cfg, B);
+  if (cache_bytes < kl.per_block * (size_t)cfg->n_blocks) return WAN_ERR_WORKSPACE;
+  const size_t es = cfg->dtype == WAN_F32 ? 4 : 2;
+  const size_t img_bytes = up((size_t)B * cfg->img_len * cfg->dim * es, ALIGN);
+  if (i2v && (!ws || ws_bytes < 3 * img_bytes)) return i2v && !ws ? WAN_ERR_NULL : WAN_ERR_WORKSPACE;
   hipStream_t s = S(stream);
-  const int d = cfg->dim, f32 = cfg->dtype == WAN_F32;
-  const size_t es = f32 ? 4 : 2;
   char *wsb = (char *)ws;
-  float *x = reinterpret_cast<float *>(wsb + y.x);
-  float *mod = reinterpret_cast<float *>(wsb + y.mod);
-  const int M = (int)(B * L);
-  // patchify: gather the (1,2,2) patches, then one GEMM against the padded Conv3d weight
-  WAN_TRY(launch_patch_gather(latent, B, cfg->in_ch, lat_f, H8, W8, y.Kp, wsb + y.P, f32, s));
-  WAN_TRY(launch_pad_rows(w->patch_w, d, 4 * cfg->in_ch, y.Kp, wsb + y.pw, f32, s));
-  WAN_TRY(launch_gemm(gemm(wsb + y.P, y.Kp, wsb + y.pw, y.Kp, M, d, y.Kp, w->patch_b, OUT_F32, x, d,
-                           f32), s));
-  // shared timestep MLP
-  WAN_TRY(launch_tmlp(t, B, cfg->freq_dim, d, w->tmlp.w1, w->tmlp.b1, w->tmlp.w2, w->tmlp.b2,
-                      reinterpret_cast<float *>(wsb + y.hid), mod, f32, s));
-  // I2V image context: three Linear layers with GELU between them
   const void *img = nullptr;
   if (i2v) {
-    const int Mi = B * cfg->img_len;
-    WAN_TRY(launch_gemm(gemm(clip_feat, cfg->img_feat, w->img_w1, cfg->img_feat, Mi, d,
-                             cfg->img_feat, w->img_b1, OUT_GELU, wsb + y.img1, d, f32), s));
-    WAN_TRY(launch_gemm(gemm(wsb + y.img1, d, w->img_w2, d, Mi, d, d, w->img_b2, OUT_GELU,
-                             wsb + y.img2, d, f32), s));
-    WAN_TRY(launch_gemm(gemm(wsb + y.img2, d, w->img_w3, d, Mi, d, d, w->img_b3, OUT_BF16,
-                             wsb + y.imgc, d, f32), s));
-    img = wsb + y.imgc;
+    if ((st = image_context(*cfg, B, clip_feat, *w, wsb, wsb + img_bytes, wsb + 2 * img_bytes, s)))
+      return st;
+    img = wsb + 2 * img_bytes;
   }
-  (void)es;
   for (int i = 0; i < cfg->n_blocks; ++i) {
-    st = block_run(*cfg, x, B, L, mod, w->blocks[i], ctx, img, wsb, y, s);
-    if (st) return st;
+    char *base = (char *)cache + (size_t)i * kl.per_block;
+    const wan_block_weights_t &bw = w->blocks[i];
+    if ((st = kv_project(*cfg, B, cfg->text_len, ctx, bw.ca_wkv, bw.ca_bkv, base + kl.kc,
+                         base + kl.vtc, rup(cfg->text_len, 64), s)))
+      return st;
+    if (i2v && (st = kv_project(*cfg, B, cfg->img_len, img, bw.ca_wkv_img, bw.ca_bkv_img,
+                                base + kl.ki, base + kl.vti, rup(cfg->img_len, 64), s)))
+      return st;
   }
-  WAN_TRY(launch_head_unpatchify(x, B, lat_f, Hp, Wp, d, w->head_w, w->head_b, cfg->out_ch, out,
-                                 f32, s));
+  return WAN_OK;
+}
+
+int wan_dit_step_cached_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, int B,
+                            int lat_f, int H8, int W8, const void *kv_cache, size_t cache_bytes,
+                            const wan_model_weights_t *w, float *out, void *ws, size_t ws_bytes,
+                            void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (!latent || !t || !w || !out || !ws || (!kv_cache && cfg->n_blocks > 0)) return WAN_ERR_NULL;
+  if ((st = check_step_dims(B, lat_f, H8, W8))) return st;
+  if ((st = check_model_weights(*cfg, w, false))) return st;
+  if (cache_bytes < kv_layout(*cfg, B).per_block * (size_t)cfg->n_blocks) return WAN_ERR_WORKSPACE;
+  const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
+  Layout y = make_layout(*cfg, B, L, true);
+  if (ws_bytes < y.total) return WAN_ERR_WORKSPACE;
+  return step_run(*cfg, latent, t, B, lat_f, H8, W8, nullptr, nullptr, (const char *)kv_cache, *w,
+                  out, (char *)ws, y, S(stream));
+}
+
+int wan_euler_fwd(float *latent, const float *vel, int B, int in_ch, int out_ch, int lat_f, int H8,
+                  int W8, float dt, int guided, float scale, void *stream) {
+  if (!latent || !vel) return WAN_ERR_NULL;
+  if (B <= 0 || B > 8 || out_ch <= 0 || in_ch < out_ch || lat_f <= 0 || H8 <= 0 || W8 <= 0)
+    return WAN_ERR_SHAPE;
+  if (guided && B != 2) return WAN_ERR_SHAPE;
+  if (!isfinite(dt) || !isfinite(scale)) return WAN_ERR_SHAPE;
+  const long plane = (long)lat_f * H8 * W8;
+  if ((long)B * in_ch * plane > (1L << 31)) return WAN_ERR_SHAPE;
+  WAN_TRY(launch_euler(latent, vel, B, in_ch, out_ch, plane, dt, guided, scale, S(stream)));
+  return WAN_OK;
+}
+
+size_t wan_sample_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, int W8) {
+  if (check_cfg(cfg) != WAN_OK || check_step_dims(B, lat_f, H8, W8) != WAN_OK) return 0;
+  const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
+  size_t t_off, v_off;
+  return sample_extra(B, cfg->out_ch, (long)lat_f * H8 * W8, &t_off, &v_off,
+                      make_layout(*cfg, B, L, true).total);
+}
+
+int wan_sample_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, int H8, int W8,
+                   int n_steps, int guided, float scale, const void *kv_cache, size_t cache_bytes,
+                   const wan_model_weights_t *w, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (!latent || !w || !ws || (!kv_cache && cfg->n_blocks > 0)) return WAN_ERR_NULL;
+  if ((st = check_step_dims(B, lat_f, H8, W8))) return st;
+  if (n_steps <= 0 || (guided && B != 2) || !isfinite(scale)) return WAN_ERR_SHAPE;
+  if (cfg->in_ch < cfg->out_ch) return WAN_ERR_SHAPE;
+  if ((st = check_model_weights(*cfg, w, false))) return st;
+  if (cache_bytes < kv_layout(*cfg, B).per_block * (size_t)cfg->n_blocks) return WAN_ERR_WORKSPACE;
+  const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
+  const long plane = (long)lat_f * H8 * W8;
+  Layout y = make_layout(*cfg, B, L, true);
+  size_t t_off, v_off;
+  if (ws_bytes < sample_extra(B, cfg->out_ch, plane, &t_off, &v_off, y.total)) return WAN_ERR_WORKSPACE;
+  hipStream_t s = S(stream);
+  char *wsb = (char *)ws;
+  float *tb = reinterpret_cast<float *>(wsb + t_off);
+  float *vel = reinterpret_cast<float *>(wsb + v_off);
+  // flow time tau_k = k / n from noise (0) to data (1); the model's timestep
+  // input is 1000 tau_k; one Euler step of length 1/n per evaluation
+  const float dt = (float)(1.0 / n_steps);
+  for (int k = 0; k < n_steps; ++k) {
+    WAN_TRY(launch_fill(tb, B, (float)(1000.0 * k / n_steps), s));
+    st = step_run(*cfg, latent, tb, B, lat_f, H8, W8, nullptr, nullptr, (const char *)kv_cache, *w,
+                  vel, wsb, y, s);
+    if (st) return st;
+    WAN_TRY(launch_euler(latent, vel, B, cfg->in_ch, cfg->out_ch, plane, dt, guided, scale, s));
+  }
   return WAN_OK;
 }
 
