@@ -182,11 +182,78 @@ __global__ __launch_bounds__(256) void k_head_unpatch(const float *__restrict__ 
   }
 }
 
+// bf16 weights: the head is a skinny GEMM (N = 4*out_ch outputs, K = d), bound
+// by reading the float32 stream once.  A workgroup owns 32 tokens; its four
+// wavefronts split K, each lane rounds its x values to bf16 in registers
+// (the operand rounding of every GEMM here) and feeds
+// v_mfma_f32_32x32x16_bf16 with weight rows straight from L2; the four
+// partial 32 x N tiles are added through LDS and scattered by the unpatchify
+// rule, bias added.
+template <int NB>   // N = 32 * NB outputs
+__global__ __launch_bounds__(256) void k_head_mfma(const float *__restrict__ x, int M, int L, int F,
+                                                   int Hp, int Wp, int d, const bf16 *__restrict__ W,
+                                                   const bf16 *__restrict__ bias,
+                                                   float *__restrict__ out) {
+  __shared__ float part[4][NB * 16][64];   // [wave][register][lane]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const long m0 = (long)blockIdx.x * 32;
+  const long row = m0 + l32 < M ? m0 + l32 : M - 1;   // tail rows read a valid row, never stored
+  const int kw = d / 4, kbeg = w * kw;                 // this wavefront's K range
+  const float *xp = x + row * d + kbeg + g * 8;
+  const bf16 *wp = W + (long)l32 * d + kbeg + g * 8;
+  f32x16 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
+#pragma unroll 4
+  for (int k = 0; k < kw; k += 16) {
+    const float4 u0 = *reinterpret_cast<const float4 *>(xp + k);
+    const float4 u1 = *reinterpret_cast<const float4 *>(xp + k + 4);
+    bf16x8 a;
+    a[0] = f2bf(u0.x); a[1] = f2bf(u0.y); a[2] = f2bf(u0.z); a[3] = f2bf(u0.w);
+    a[4] = f2bf(u1.x); a[5] = f2bf(u1.y); a[6] = f2bf(u1.z); a[7] = f2bf(u1.w);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8 *>(wp + (long)nb * 32 * d + k);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[nb], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[w][nb * 16 + r][lane] = acc[nb][r];
+  __syncthreads();
+  // lane (g, l32), register r of block nb holds token row (r/4)*8 + g*4 + r%4, output nb*32 + l32
+  const int H8 = 2 * Hp, W8 = 2 * Wp, C = NB * 8;
+  for (int i = threadIdx.x; i < NB * 16 * 64; i += 256) {
+    const int reg = i >> 6, ln = i & 63, nb = reg >> 4, r = reg & 15;
+    const long m = m0 + (r >> 2) * 8 + (ln >> 5) * 4 + (r & 3);
+    if (m >= M) continue;
+    const int o = nb * 32 + (ln & 31);
+    float v = part[0][reg][ln] + part[1][reg][ln] + part[2][reg][ln] + part[3][reg][ln];
+    if (bias) v += (float)bias[o];
+    const long bq = m / L, n = m % L;
+    const int f = (int)(n / (Hp * Wp)), rem = (int)(n % (Hp * Wp)), ii = rem / Wp, jj = rem % Wp;
+    const int c = o >> 2, aa = (o >> 1) & 1, bb = o & 1;
+    out[((bq * C + c) * F + f) * (long)H8 * W8 + (long)(2 * ii + aa) * W8 + 2 * jj + bb] = v;
+  }
+}
+
 hipError_t launch_head_unpatchify(const float *x, int B, int F, int Hp, int Wp, int d,
                                   const void *w, const void *b, int out_ch, float *out, int f32,
                                   hipStream_t s) {
   const int L = F * Hp * Wp, M = B * L, NO = out_ch * 4;
   const int blocks = ((M + 63) / 64) * ((NO + 63) / 64);
+  if (!f32 && d % 64 == 0 && (NO == 32 || NO == 64)) {
+    const int wgs = (M + 31) / 32;
+    if (NO == 64)
+      k_head_mfma<2><<<wgs, 256, 0, s>>>(x, M, L, F, Hp, Wp, d, (const bf16 *)w, (const bf16 *)b, out);
+    else
+      k_head_mfma<1><<<wgs, 256, 0, s>>>(x, M, L, F, Hp, Wp, d, (const bf16 *)w, (const bf16 *)b, out);
+    return hipGetLastError();
+  }
   if (f32)
     k_head_unpatch<float><<<blocks, 256, 0, s>>>(x, M, L, F, Hp, Wp, d, (const float *)w,
                                                   (const float *)b, NO, out);
