@@ -66,6 +66,12 @@ READINGS = {
                     "and both carry the same latent",
     "R21 I2V sampling": "only the 16 noise channels move; the condition latent and the mask "
                         "channels of the 36-channel input stay as given",
+    "R22 FP8 GEMM": "[Note, Infra / 推理优化]: per-tensor weight scale, per-token activation "
+                    "scale; format OCP E4M3 (largest finite 448, round to nearest even); "
+                    "scale = amax / 448 so the largest magnitude maps to 448; the code is "
+                    "decided in float32 as the kernel does: inv = 448 / amax (float32 "
+                    "division), v = x * inv (float32), clamp to +-448, round to E4M3; an "
+                    "all-zero row or tensor gets scale 1; y = (xq wq^T) sx sw + b",
 }
 
 
@@ -403,4 +409,87 @@ def text_kv(ctx, wts: Dict[str, np.ndarray], img=None):
         kvi = linear(img, wts["ca_wkv_img"], wts["ca_bkv_img"])
         out = out + (kvi[:, :d], kvi[:, d:])
     return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) GEMM emulation (R22)
+
+E4M3_MAX = 448.0
+
+
+def e4m3_values() -> np.ndarray:
+    """All finite non-negative OCP E4M3 values, ascending: subnormals m/8 * 2^-6
+    (m = 0..7), normals (1 + m/8) * 2^(e-7) for e = 1..15 except the NaN code
+    e = 15, m = 7 (largest finite 1.75 * 2^8 = 448)."""
+    v = [m / 8.0 * 2.0 ** -6 for m in range(8)]
+    for e in range(1, 16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            v.append((1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(v, dtype=F64)
+
+
+_E4M3 = e4m3_values()
+
+
+def e4m3_round(v):
+    """Round to the nearest E4M3 value, ties to the even code (the value whose
+    3-bit mantissa is even); |v| must be <= 448 (R22 clamps first)."""
+    a = np.abs(_f(v))
+    if np.any(a > E4M3_MAX):
+        raise ValueError("E4M3 rounding input beyond 448")
+    idx = np.searchsorted(_E4M3, a)                 # first value >= a
+    hi = np.minimum(idx, len(_E4M3) - 1)
+    lo = np.maximum(idx - 1, 0)
+    dlo, dhi = a - _E4M3[lo], _E4M3[hi] - a
+    take_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))   # code index parity = mantissa parity
+    q = np.where(take_hi, _E4M3[hi], _E4M3[lo])
+    return np.sign(_f(v)) * q
+
+
+def _scale_f32(amax):
+    """(inv, scale) in float32 for an amax (float32): inv = 448 / amax, scale =
+    amax / 448; amax = 0 gives (1, 1)."""
+    amax = np.float32(amax)
+    if amax == 0:
+        return np.float32(1.0), np.float32(1.0)
+    return np.float32(E4M3_MAX) / amax, amax / np.float32(E4M3_MAX)
+
+
+def _quant_f32(x, inv):
+    v = np.asarray(x, np.float32) * np.float32(inv)            # float32 product, as on the GPU
+    v = np.clip(v, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return e4m3_round(v.astype(F64))
+
+
+def quantize_rows_fp8(x):
+    """Per-token quantisation of x [M, K] (R22): returns (q [M, K] E4M3 values,
+    scale [M]) with x ~= q * scale[:, None]."""
+    x32 = np.asarray(x, np.float32)
+    q = np.empty(x32.shape, F64)
+    sc = np.empty(x32.shape[0], F64)
+    for i in range(x32.shape[0]):
+        inv, s = _scale_f32(np.max(np.abs(x32[i])) if x32.shape[1] else 0.0)
+        q[i] = _quant_f32(x32[i], inv)
+        sc[i] = s
+    return q, sc
+
+
+def quantize_tensor_fp8(w):
+    """Per-tensor quantisation of a weight (R22): (q, scale) with w ~= q * scale."""
+    w32 = np.asarray(w, np.float32)
+    inv, s = _scale_f32(np.max(np.abs(w32)) if w32.size else 0.0)
+    return _quant_f32(w32, inv), F64(s)
+
+
+def linear_fp8(x, w, b=None):
+    """y = (xq wq^T) * sx[:, None] * sw + b with per-token xq, per-tensor wq (R22)
+    [Note, Infra / 推理优化: FP8 GEMM, per-tensor weights + per-token activations]."""
+    qx, sx = quantize_rows_fp8(x)
+    qw, sw = quantize_tensor_fp8(w)
+    y = (qx @ qw.T) * sx[:, None] * sw
+    if b is not None:
+        y = y + _f(b)[None, :]
+    return y
 

@@ -459,3 +459,50 @@ def pin_text_kv(O):
     ca = O.cross_attention(xq, ctx, wq, bq, w["ca_wkv"], w["ca_bkv"], wo, bo, H)
     q = O.linear(O.layer_norm(xq), wq, bq)
     _close(ca, O.linear(O.multihead(q, k, v, H), wo, bo), 1e-12, "CA from cached K/V")
+
+
+# ---------------------------------------------------------------- FP8 GEMM
+def pin_fp8(O):
+    """OCP E4M3 value set and rounding against torch's float8_e4m3fn (decode of
+    every code, conversion of random values), ties to the even code, the
+    per-token / per-tensor scale mapping the largest magnitude to 448, the
+    rounding error bound, and linear_fp8 on operands already on the E4M3 grid
+    against the exact product."""
+    vals = O.e4m3_values()
+    codes = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    _close(vals, codes.numpy(), 0, "E4M3 value set")
+    assert vals[-1] == 448.0 and vals[1] == 2.0 ** -9
+    _close(O.e4m3_round(vals), vals, 0, "idempotent on representable values")
+    _close(O.e4m3_round(-vals), -vals, 0, "sign")
+    mids = (vals[:-1] + vals[1:]) / 2
+    even = np.where(np.arange(len(mids)) % 2 == 0, vals[:-1], vals[1:])
+    _close(O.e4m3_round(mids), even, 0, "ties to the even code")
+    r = _rng(50)
+    x = np.clip(r.standard_normal(20000) * 40, -448, 448).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    _close(O.e4m3_round(x.astype(np.float64)), ref, 0, "vs torch float8_e4m3fn")
+    # per-token quantisation: the row max maps to 448, error within half a step
+    xr = (r.standard_normal((7, 300)) * np.array([1e-3, 1, 10, 100, 0.5, 3, 1e4])[:, None]).astype(np.float32)
+    xr[3] = 0.0
+    q, s = O.quantize_rows_fp8(xr)
+    for i in range(7):
+        if i == 3:
+            assert s[i] == 1.0 and not q[i].any(), "zero row"
+            continue
+        assert np.max(np.abs(q[i])) == 448.0, ("row max", i)
+        v = xr[i].astype(np.float64) / s[i]
+        # half the E4M3 spacing at |v| (relative 2^-4 for normals, 2^-10 absolute below 2^-6)
+        bound = np.maximum(np.abs(v) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-6)
+        assert np.all(np.abs(v - q[i]) <= bound), ("rounding bound", i)
+    qw, sw = O.quantize_tensor_fp8(xr)
+    assert np.max(np.abs(qw)) == 448.0 and np.isclose(sw, np.max(np.abs(xr)) / 448.0, rtol=1e-7)
+    # operands already on the grid (q * power-of-two scales) -> the exact product
+    qa = vals[r.integers(0, 127, (5, 64))] * np.sign(r.standard_normal((5, 64)))
+    qa[:, 0] = 448.0                                      # each row's max is 448
+    qb = vals[r.integers(0, 127, (9, 64))] * np.sign(r.standard_normal((9, 64)))
+    qb[0, 0] = -448.0
+    xa = (qa * 0.25).astype(np.float32)                   # scale 1/4 per row
+    wb = (qb * 2.0).astype(np.float32)                    # scale 2 for the tensor
+    bias = r.standard_normal(9)
+    _close(O.linear_fp8(xa, wb, bias), xa.astype(np.float64) @ wb.astype(np.float64).T + bias, 1e-9,
+           "linear_fp8 on grid operands")

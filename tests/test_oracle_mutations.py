@@ -42,6 +42,13 @@ MUTATIONS = {
     "guidance pair order": ("g = cfg_combine(v[0], v[1], guidance)", "g = cfg_combine(v[1], v[0], guidance)"),
     "guidance base": ("return vu + F64(scale) * (vc - vu)", "return vc + F64(scale) * (vc - vu)"),
     "text V from K": ("out = (kv[:, :d], kv[:, d:])", "out = (kv[:, :d], kv[:, :d])"),
+    "e4m3 ties away from zero": ("take_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))",
+                                 "take_hi = (dhi <= dlo)"),
+    "fp8 scale to 240": ("return np.float32(E4M3_MAX) / amax, amax / np.float32(E4M3_MAX)",
+                         "return np.float32(240.0) / amax, amax / np.float32(240.0)"),
+    "fp8 activation scale per tensor": ("inv, s = _scale_f32(np.max(np.abs(x32[i])) if x32.shape[1] else 0.0)",
+                                        "inv, s = _scale_f32(np.max(np.abs(x32)))"),
+    "fp8 dequant without weight scale": ("y = (qx @ qw.T) * sx[:, None] * sw", "y = (qx @ qw.T) * sx[:, None]"),
     "head split strided": ("k[:, h * hd:(h + 1) * hd],\n                                     v[:, h * hd:(h + 1) * hd])",
                            "k[:, h::heads],\n                                     v[:, h::heads])"),
 }
