@@ -239,6 +239,33 @@ int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void
 int wan_linear_fwd(const void *x, const void *w, const void *b, void *y, int M, int N, int K,
                    int mode, void *stream);
 
+/* ---- FP8 GEMM ------------------------------------------------------------- */
+/* [Note] Infra (推理优化): FP8 GEMM with per-tensor weight scales and
+ * per-token activation scales.  Format: OCP E4M3 (one byte, largest finite
+ * 448, round to nearest even).  A scale maps the largest magnitude to 448:
+ * inv = 448 / amax (float32, correctly rounded), code = E4M3(clamp(x * inv,
+ * +-448)), scale = amax / 448 (so x ~= code * scale); an all-zero row or
+ * tensor gets scale 1. */
+
+/* Per-token quantisation: x bf16 [M, K] row stride ldx (device) -> q E4M3
+ * [M, K] row stride ldq bytes (device), scale float32 [M] (device).
+ * K, ldx and ldq multiples of 8 (16-byte / 8-byte aligned rows). */
+int wan_quantize_rows_fp8(const void *x, int M, int K, int ldx, void *q, int ldq, float *scale,
+                          void *stream);
+
+/* Per-tensor quantisation of n bf16 values (n % 8 == 0, device) -> q E4M3 [n]
+ * (device) and one float32 scale (device).  ws: at least 4 bytes of device
+ * scratch (the running maximum). */
+int wan_quantize_tensor_fp8(const void *w, long n, void *q, float *scale, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* y = (xq wq^T) * x_scale[m] * w_scale[0] + b: xq E4M3 [M, K], wq E4M3 [N, K]
+ * (rows contiguous, K % 64 == 0), x_scale float32 [M], w_scale float32 [1],
+ * b bf16 [N] or NULL (all device).  mode 0: y bf16 [M, N]; 1: y float32;
+ * 2: y bf16 = GELU_tanh(.).  float32 accumulation. */
+int wan_linear_fp8_fwd(const void *xq, const float *x_scale, const void *wq, const float *w_scale,
+                       const void *b, void *y, int M, int N, int K, int mode, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

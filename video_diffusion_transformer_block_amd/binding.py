@@ -22,7 +22,8 @@ WAN_F32, WAN_BF16 = 0, 1
 EXPORTS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
            "wan_status_str", "wan_tmlp_fwd", "wan_dit_block_fwd", "wan_dit_step_fwd",
            "wan_i2v_mask", "wan_attention_fwd", "wan_linear_fwd", "wan_kv_cache_fwd",
-           "wan_dit_step_cached_fwd", "wan_euler_fwd", "wan_sample_fwd")
+           "wan_dit_step_cached_fwd", "wan_euler_fwd", "wan_sample_fwd", "wan_quantize_rows_fp8",
+           "wan_quantize_tensor_fp8", "wan_linear_fp8_fwd")
 
 
 class WanError(RuntimeError):
@@ -90,6 +91,9 @@ def lib() -> C.CDLL:
         L.wan_euler_fwd.argtypes = [vp, vp, i, i, i, i, i, i, C.c_float, i, C.c_float, vp]
         L.wan_sample_fwd.argtypes = [C.POINTER(Cfg), vp, i, i, i, i, i, i, C.c_float, vp, sz,
                                      C.POINTER(ModelW), vp, sz, vp]
+        L.wan_quantize_rows_fp8.argtypes = [vp, i, i, i, vp, i, vp, vp]
+        L.wan_quantize_tensor_fp8.argtypes = [vp, C.c_long, vp, vp, vp, sz, vp]
+        L.wan_linear_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
         for n in EXPORTS:
             if n not in ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
                          "wan_status_str"):
@@ -240,4 +244,26 @@ def sample_fwd(cfg: Cfg, latent: torch.Tensor, n_steps: int, cache: torch.Tensor
            lib().wan_sample_fwd(C.byref(cfg), _p(latent), B, F, H8, W8, n_steps, 1 if guided else 0,
                                 scale, _p(cache), _nbytes(cache), C.byref(mw), _p(ws), _nbytes(ws),
                                 _stream(stream)))
+
+
+# ---- FP8 GEMM (OCP E4M3 operands, per-token / per-tensor scales)
+
+def quantize_rows_fp8(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream=None):
+    M, K = x.shape
+    _check("wan_quantize_rows_fp8", lib().wan_quantize_rows_fp8(_p(x), M, K, x.stride(0), _p(q),
+                                                                q.stride(0), _p(scale),
+                                                                _stream(stream)))
+
+
+def quantize_tensor_fp8(w: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, ws: torch.Tensor,
+                        stream=None):
+    _check("wan_quantize_tensor_fp8", lib().wan_quantize_tensor_fp8(_p(w), w.numel(), _p(q), _p(scale),
+                                                                    _p(ws), _nbytes(ws),
+                                                                    _stream(stream)))
+
+
+def linear_fp8_fwd(xq, x_scale, wq, w_scale, b, y, M, N, K, mode, stream=None):
+    _check("wan_linear_fp8_fwd", lib().wan_linear_fp8_fwd(_p(xq), _p(x_scale), _p(wq), _p(w_scale),
+                                                          _p(b), _p(y), M, N, K, mode,
+                                                          _stream(stream)))
 

@@ -58,10 +58,15 @@ template <> struct Vec8<bf16> {
 
 // Epilogue on 8 consecutive columns n..n+7 of row m (n + 8 <= N and 16-byte
 // aligned rows), or element-wise for a ragged column tail.
-template <int KIND, bool BROWS>
+template <int KIND, bool BROWS, bool SCALED = false>
 WAN_DEV void epi8(const GemmDesc &g, int m, int n, float *v) {
   const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
   const bool full = n + 8 <= g.N;
+  if (SCALED) {   // FP8 dequantisation: per-row (token) scale times the per-tensor weight scale
+    const float sc = g.a_scale[m] * g.b_scale[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= sc;
+  }
   if (bias) {
     if (BROWS) {
       const float bb = (float)bias[m];
@@ -114,6 +119,47 @@ WAN_DEV void epi8(const GemmDesc &g, int m, int n, float *v) {
     } else {
       for (int i = 0; i < 8 && n + i < g.N; ++i) xp[i] += (gp ? gp[i] : 1.0f) * v[i];
     }
+  }
+}
+
+// Epilogue through LDS: per wave 4 slabs of 32 rows x 64 columns (fp32,
+// padded rows), so every lane handles 8 contiguous columns of one row.  The
+// caller has synchronised the workgroup (the LDS tiles are free).
+template <int KIND, bool BROWS, bool SCALED>
+WAN_DEV void epilogue(const GemmDesc &g, const f32x16 (&acc)[4][2], float *lds, int w, int lane,
+                      int m0, int n0, int wm, int wn) {
+  const int half = lane >> 5, l32 = lane & 31;
+  constexpr int EP = 68;
+  float *ep = lds + w * 32 * EP;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (r >> 2) * 8 + half * 4 + (r & 3);
+        ep[row * EP + jj * 32 + l32] = acc[i][jj][r];
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    const int row = lane >> 1, cb = (lane & 1) * 32;
+    const int m = m0 + wm * 128 + i * 32 + row;
+    if (m < g.M) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 64 + cb + q * 8;
+        if (n < g.N || n < g.npad) {
+          float v[8];
+          const float4 u0 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8);
+          const float4 u1 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8 + 4);
+          v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+          v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+          epi8<KIND, BROWS, SCALED>(g, m, n, v);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -261,43 +307,181 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
   if (kt < KT) tile(kt, 0);
   if (kt + 1 < KT) tile(kt + 1, 1);
 
-  // ---- epilogue through LDS: per wave 4 slabs of 32 rows x 64 columns (fp32, padded rows)
   __syncthreads();
-  constexpr int EP = 68;
-  float *ep = reinterpret_cast<float *>(smem) + w * 32 * EP;
+  epilogue<KIND, BROWS, false>(g, acc, reinterpret_cast<float *>(smem), w, lane, m0, n0, wm, wn);
+}
+
+// FP8 operands (OCP E4M3; "Wan: Open and Advanced Large-Scale Video Generative
+// Models (Wan 2.1)", section Infra / 推理优化: FP8 GEMM with per-tensor weight
+// and per-token activation scales).  256x256 output tile, 8 wavefronts (2x4,
+// 128x64 each), v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales (E8M0
+// 127).  A K tile is 64 one-byte elements (one MFMA depth): 64-byte rows,
+// 16-byte chunks XOR-swizzled by (row >> 2) & 3, two LDS stages of 32 KB, so
+// every fragment read fits the LDS immediate offset.  A fragment is 32 bytes
+// per lane -- row l%32, k = 32*(l/32) .. +32, two ds_read_b128 -- with A and B
+// in the same k order, which is all the dot product needs.  Per tile: the
+// loads of tile kt+2 start, the 8 MFMAs of tile kt run from registers, one
+// barrier, then the fragments of tile kt+1 are read into the same registers
+// while those MFMAs execute.  The epilogue scales by a_scale[m] * b_scale[0].
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void k_gemm_fp8(GemmDesc g) {
+  constexpr int GBK8 = 64;                    // K tile, bytes = elements
+  constexpr int RPB = 1024 / GBK8;            // rows per 1-KB direct-load block (16)
+  constexpr int BPW = GBM / RPB / GW;         // blocks per wavefront per operand tile (2)
+  constexpr int LPT = 2 * BPW;                // direct loads per wavefront per K tile
+  // one LDS variable per stage and operand (16 KB each): the compiler gives
+  // each its own alias scope, so reads of one stage need not wait for the
+  // direct loads still landing in the other; stages are picked with
+  // compile-time parities in the steady-state loop
+  __shared__ __attribute__((aligned(16))) uint8_t sA0[GBM * GBK8];
+  __shared__ __attribute__((aligned(16))) uint8_t sA1[GBM * GBK8];
+  __shared__ __attribute__((aligned(16))) uint8_t sB0[GBN * GBK8];
+  __shared__ __attribute__((aligned(16))) uint8_t sB1[GBN * GBK8];
+  auto abuf = [&](auto P) -> uint8_t * {
+    if constexpr (std::is_integral_v<decltype(P)>) return P ? sA1 : sA0;
+    else if constexpr (decltype(P)::value == 0) return sA0;
+    else return sA1;
+  };
+  auto bbuf = [&](auto P) -> uint8_t * {
+    if constexpr (std::is_integral_v<decltype(P)>) return P ? sB1 : sB0;
+    else if constexpr (decltype(P)::value == 0) return sB0;
+    else return sB1;
+  };
+  auto other = [](auto P) {
+    if constexpr (std::is_integral_v<decltype(P)>) return 1 - P;
+    else return std::integral_constant<int, 1 - decltype(P)::value>{};
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // a workgroup barrier without a memory fence: a fence would wait for every
+  // direct load in flight; the counter waits before it order the hardware and
+  // the empty asm statements keep the compiler from moving memory accesses
+  auto barrier = []() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 2, wn = w & 3;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int tiles_m = (g.M + GBM - 1) / GBM;
+  const int tiles_n = (g.N + GBN - 1) / GBN;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int group = GROUP_M * tiles_n;
+  const int first_m = (bid / group) * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (bid % group) % gm;
+  const int tn = (bid % group) / gm;
+  const int m0 = tm * GBM, n0 = tn * GBN;
+
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)g.A, 0, (int)((unsigned)g.M * (unsigned)g.lda), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)g.B, 0, (int)((unsigned)g.N * (unsigned)g.ldb), 0x00020000);
+  int oa[BPW], ob[BPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    {
-      const int jh = 0;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = (r >> 2) * 8 + half * 4 + (r & 3);
-          ep[row * EP + jj * 32 + l32] = acc[i][jj][r];
-        }
-      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
-      __builtin_amdgcn_wave_barrier();
-      const int row = lane >> 1, cb = (lane & 1) * 32;
-      const int m = m0 + wm * 128 + i * 32 + row;
-      if (m < g.M) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * 64 + jh * 64 + cb + q * 8;
-          if (n < g.N || n < g.npad) {
-            float v[8];
-            const float4 u0 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8);
-            const float4 u1 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8 + 4);
-            v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
-            v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
-            epi8<KIND, BROWS>(g, m, n, v);
-          }
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-    }
+  for (int r = 0; r < BPW; ++r) {
+    const int row = (w * BPW + r) * RPB + lane / 4;
+    const int c = (lane % 4) ^ swz_row<4>(row);
+    oa[r] = (int)((unsigned)min(m0 + row, g.M - 1) * (unsigned)g.lda + c * 16);
+    ob[r] = (int)((unsigned)min(n0 + row, g.N - 1) * (unsigned)g.ldb + c * 16);
   }
+  auto gload = [&](int kt, auto st) {
+    const int k0b = kt * GBK8;
+    uint8_t *da = abuf(st) + w * BPW * 1024;
+    uint8_t *db = bbuf(st) + w * BPW * 1024;
+#pragma unroll
+    for (int r = 0; r < BPW; ++r) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(da + r * 1024), 16, oa[r], k0b, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(db + r * 1024), 16, ob[r], k0b, 0, 0);
+    }
+  };
+  // byte offsets of a fragment's two chunks (logical 2 half + {0, 1}); the row
+  // swizzle depends only on l32 (row offsets are multiples of 32)
+  int aoff[2], boff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = ((2 * half + j) ^ swz_row<4>(l32)) * 16;
+    aoff[j] = (wm * 128 + l32) * GBK8 + c;
+    boff[j] = (wn * 64 + l32) * GBK8 + c;
+  }
+
+  // accumulators in AGPRs (an AGPR operand makes the compiler split the 256
+  // registers 128 / 128); fragments and addresses use the VGPRs
+  asm volatile("; accumulators in AGPRs" :: "a"(0.0f));
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  i32x8 fa[4], fb[2];
+  auto frag = [&](const uint8_t *p, const int (&off)[2]) -> i32x8 {
+    const uint4 lo = *reinterpret_cast<const uint4 *>(p + off[0]);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(p + off[1]);
+    i32x8 v;
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    return v;
+  };
+  auto frags = [&](auto st) {
+    const uint8_t *a_s = abuf(st), *b_s = bbuf(st);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag(a_s + i * 32 * GBK8, aoff);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = frag(b_s + j * 32 * GBK8, boff);
+  };
+  auto mfmas = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fa[i], fb[j], acc[i][j], 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+  };
+
+  const int KT = g.K / GBK8;
+  gload(0, I0{});
+  if (KT > 1) gload(1, I1{});
+  if (KT > 1) wait_vm<LPT>();
+  else wait_vm<0>();
+  barrier();
+  frags(I0{});
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): tile 0's fragments are in registers
+  barrier();                            // every wavefront has read stage 0
+
+  // tile kt (fragments in registers, stage kt&1 free, stage (kt+1)&1 holding
+  // tile kt+1 or still receiving it): start the loads of tile kt+2 into the
+  // free stage (load2), issue the MFMAs, wait for tile kt+1, one barrier, read
+  // its fragments (next) while the MFMAs execute, and a second barrier so the
+  // stage just read may be refilled by the next tile.
+  auto tile = [&](int kt, auto st, bool load2, bool next) {
+    if (load2) gload(kt + 2, st);
+    mfmas();
+    __builtin_amdgcn_sched_barrier(0);
+    if (load2) wait_vm<LPT>();
+    else wait_vm<0>();
+    barrier();
+    if (next) frags(other(st));
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): fragments read
+    barrier();
+  };
+  int kt = 0;
+  for (; kt + 3 < KT; kt += 2) {   // tiles kt .. kt+3 exist
+    tile(kt, I0{}, true, true);
+    tile(kt + 1, I1{}, true, true);
+  }
+  for (; kt < KT; ++kt)             // the last 1 .. 3 tiles: one generic copy with run-time flags
+    tile(kt, kt & 1, kt + 2 < KT, kt + 1 < KT);
+
+  // the epilogue stages 8 wavefronts x 32 rows x 68 floats through its own LDS buffer
+  __shared__ __attribute__((aligned(16))) float sEp[GW * 32 * 68];
+  epilogue<KIND, false, true>(g, acc, sEp, w, lane, m0, n0, wm, wn);
 }
 
 // per-element epilogue (float32 path)
@@ -373,6 +557,19 @@ static void gemm_go(const GemmDesc &g, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmDesc &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.fp8) {
+    if (g.K % 64 || !g.a_scale || !g.b_scale || g.bias_rows || g.f32) return hipErrorInvalidValue;
+    if ((long)g.M * g.lda >= (1L << 31) || (long)g.N * g.ldb >= (1L << 31)) return hipErrorInvalidValue;
+    const int blocks = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
+    switch (g.kind) {
+      case OUT_BF16: k_gemm_fp8<OUT_BF16><<<blocks, GW * 64, 0, s>>>(g); break;
+      case OUT_F32: k_gemm_fp8<OUT_F32><<<blocks, GW * 64, 0, s>>>(g); break;
+      case OUT_GELU: k_gemm_fp8<OUT_GELU><<<blocks, GW * 64, 0, s>>>(g); break;
+      case OUT_RESID: k_gemm_fp8<OUT_RESID><<<blocks, GW * 64, 0, s>>>(g); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (!g.f32 && (g.K % GBK)) return hipErrorInvalidValue;
   // the bf16 kernel addresses A and B with 32-bit byte offsets
   if (!g.f32 && ((long)g.M * g.lda * 2 >= (1L << 31) || (long)g.N * g.ldb * 2 >= (1L << 31)))

@@ -22,6 +22,11 @@ struct GemmDesc {
   const float *gate; long gate_bstride; int rows_per_batch;
   int f32;                     // operands / bias / C are float32 instead of bf16
   int npad;                    // OUT_BF16: columns N .. npad-1 of C are written as zeros
+  // FP8 (OCP E4M3) operands: A and B hold one byte per element, K % 128 == 0;
+  // acc is multiplied by a_scale[m] * b_scale[0] before the bias (per-token /
+  // per-tensor dequantisation)
+  int fp8;
+  const float *a_scale, *b_scale;
 };
 
 // Attention O = softmax(Q K^T * scale) V for every (batch, head); hd = 128, bf16.
@@ -54,6 +59,11 @@ hipError_t launch_head_unpatchify(const float *x, int B, int F, int Hp, int Wp, 
                                   hipStream_t s);
 hipError_t launch_pad_rows(const void *src, int R, int K, int Kp, void *dst, int f32, hipStream_t s);
 hipError_t launch_fill(float *p, int n, float v, hipStream_t s);
+// FP8 (OCP E4M3) quantisation: per row (one scale per row) and per tensor
+hipError_t launch_quant_rows_fp8(const void *x, int M, int K, long ldx, void *q, long ldq,
+                                 float *scale, hipStream_t s);
+hipError_t launch_quant_tensor_fp8(const void *w, long n, void *q, float *scale, unsigned *amax_bits,
+                                   hipStream_t s);
 hipError_t launch_euler(float *lat, const float *vel, int B, int in_ch, int out_ch, long plane,
                         float dt, int guided, float scale, hipStream_t s);
 

@@ -567,6 +567,38 @@ int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void
   return WAN_OK;
 }
 
+int wan_quantize_rows_fp8(const void *x, int M, int K, int ldx, void *q, int ldq, float *scale,
+                          void *stream) {
+  if (!x || !q || !scale) return WAN_ERR_NULL;
+  if (M <= 0 || K <= 0 || K % 8 || ldx < K || ldq < K || ldx % 8 || ldq % 8) return WAN_ERR_SHAPE;
+  WAN_TRY(launch_quant_rows_fp8(x, M, K, ldx, q, ldq, scale, S(stream)));
+  return WAN_OK;
+}
+
+int wan_quantize_tensor_fp8(const void *w, long n, void *q, float *scale, void *ws, size_t ws_bytes,
+                            void *stream) {
+  if (!w || !q || !scale || !ws) return WAN_ERR_NULL;
+  if (n <= 0 || n % 8) return WAN_ERR_SHAPE;
+  if (ws_bytes < 4) return WAN_ERR_WORKSPACE;
+  WAN_TRY(launch_quant_tensor_fp8(w, n, q, scale, (unsigned *)ws, S(stream)));
+  return WAN_OK;
+}
+
+int wan_linear_fp8_fwd(const void *xq, const float *x_scale, const void *wq, const float *w_scale,
+                       const void *b, void *y, int M, int N, int K, int mode, void *stream) {
+  if (!xq || !x_scale || !wq || !w_scale || !y) return WAN_ERR_NULL;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 64) return WAN_ERR_SHAPE;
+  if ((long)M * K >= (1L << 31) || (long)N * K >= (1L << 31)) return WAN_ERR_SHAPE;
+  int kind = mode == 0 ? OUT_BF16 : mode == 1 ? OUT_F32 : mode == 2 ? OUT_GELU : -1;
+  if (kind < 0) return WAN_ERR_CONFIG;
+  GemmDesc g = gemm(xq, K, wq, K, M, N, K, b, kind, y, N, 0);
+  g.fp8 = 1;
+  g.a_scale = x_scale;
+  g.b_scale = w_scale;
+  WAN_TRY(launch_gemm(g, S(stream)));
+  return WAN_OK;
+}
+
 int wan_linear_fwd(const void *x, const void *w, const void *b, void *y, int M, int N, int K,
                    int mode, void *stream) {
   if (!x || !w || !y) return WAN_ERR_NULL;
