@@ -192,31 +192,42 @@ def multihead(q, k, v, heads: int):
                                      v[:, h * hd:(h + 1) * hd]) for h in range(heads)], axis=1)
 
 
-def self_attention(hmod, wqkv, bqkv, wo, bo, heads: int, rows: Optional[np.ndarray] = None):
+def self_attention(hmod, wqkv, bqkv, wo, bo, heads: int, rows: Optional[np.ndarray] = None,
+                   fp8: bool = False):
     """Self-attention of one sample: qkv = h Wqkv^T + b (q | k | v blocks of d
     rows in Wqkv), o = MHA(q, k, v), y = o Wo^T + bo.  ``rows`` restricts the
     query side (and the returned rows) to a subset of tokens; keys and values
-    always cover all tokens."""
+    always cover all tokens.  ``fp8``: both projections in FP8 (R22), the
+    stored Wqkv quantised as one tensor."""
     hmod = _f(hmod)
     d = hmod.shape[1]
     wqkv, bqkv = _f(wqkv), _f(bqkv)
-    k = linear(hmod, wqkv[d:2 * d], bqkv[d:2 * d])
-    v = linear(hmod, wqkv[2 * d:], bqkv[2 * d:])
+    if fp8:
+        qw, sw = quantize_tensor_fp8(wqkv)
+        lin = lambda x, sl, b: linear_fp8_q(x, qw[sl], sw, b)
+        lin_o = linear_fp8
+    else:
+        lin = lambda x, sl, b: linear(x, wqkv[sl], b)
+        lin_o = linear
+    k = lin(hmod, slice(d, 2 * d), bqkv[d:2 * d])
+    v = lin(hmod, slice(2 * d, 3 * d), bqkv[2 * d:])
     hq = hmod if rows is None else hmod[rows]
-    q = linear(hq, wqkv[:d], bqkv[:d])
+    q = lin(hq, slice(0, d), bqkv[:d])
     o = multihead(q, k, v, heads)
-    return linear(o, wo, bo)
+    return lin_o(o, wo, bo)
 
 
 def cross_attention(xq, ctx, wq, bq, wkv, bkv, wo, bo, heads: int, eps: float = 1e-6,
-                    img=None, wkv_img=None, bkv_img=None):
+                    img=None, wkv_img=None, bkv_img=None, fp8: bool = False):
     """Cross-attention of one sample (R5, R12): q from LayerNorm(x) without
     modulation, keys/values from the text context; with ``img`` a second,
     separately normalised attention over the image tokens is added before the
     shared out-projection.  [News, 核心创新二; Note, I2V 架构扩展: decoupled
-    cross-attention in the manner of IP-Adapter]"""
+    cross-attention in the manner of IP-Adapter].  ``fp8``: the query and
+    out-projections in FP8 (R22); the text / image keys and values stay exact."""
     d = ctx.shape[1]
-    q = linear(layer_norm(xq, eps), wq, bq)
+    lin = linear_fp8 if fp8 else linear
+    q = lin(layer_norm(xq, eps), wq, bq)
     wkv, bkv = _f(wkv), _f(bkv)
     kt = linear(ctx, wkv[:d], bkv[:d])
     vt = linear(ctx, wkv[d:], bkv[d:])
@@ -226,19 +237,22 @@ def cross_attention(xq, ctx, wq, bq, wkv, bkv, wo, bo, heads: int, eps: float = 
         ki = linear(img, wkv_img[:d], bkv_img[:d])
         vi = linear(img, wkv_img[d:], bkv_img[d:])
         o = o + multihead(q, ki, vi, heads)
-    return linear(o, wo, bo)
+    return lin(o, wo, bo)
 
 
-def ffn(hmod, w1, b1, w2, b2):
-    """z = GELU_tanh(h W1^T + b1) W2^T + b2.  [Note, 配置表: FFN dimension]"""
-    return linear(gelu_tanh(linear(hmod, w1, b1)), w2, b2)
+def ffn(hmod, w1, b1, w2, b2, fp8: bool = False):
+    """z = GELU_tanh(h W1^T + b1) W2^T + b2.  [Note, 配置表: FFN dimension]
+    ``fp8``: both projections in FP8 (R22)."""
+    lin = linear_fp8 if fp8 else linear
+    return lin(gelu_tanh(lin(hmod, w1, b1)), w2, b2)
 
 
 # ---------------------------------------------------------------------------
 # one DiT block
 
 def block(x, m, wts: Dict[str, np.ndarray], ctx, heads: int, eps: float = 1e-6,
-          img=None, rows: Optional[np.ndarray] = None, return_parts: bool = False):
+          img=None, rows: Optional[np.ndarray] = None, return_parts: bool = False,
+          fp8: bool = False):
     """One block for a batch.  x [B, L, d]; m [B, 6d] (shared t-MLP output);
     ctx [B, Lc, d]; img [B, Li, d] or None.
 
@@ -249,7 +263,10 @@ def block(x, m, wts: Dict[str, np.ndarray], ctx, heads: int, eps: float = 1e-6,
     [News, 核心创新二 and Note, Diffusion Transformer: shared AdaLN, full
     self-attention, text cross-attention in every block; readings R3, R5.]
     With ``rows`` only those token rows of the output are computed (self-
-    attention still reads all tokens' keys and values)."""
+    attention still reads all tokens' keys and values).  ``fp8``: the six
+    Linear layers (QKV, SA out, CA query, CA out, FFN up, FFN down) in FP8
+    with per-token activation and per-tensor weight scales (R22)
+    [Note, Infra / 推理优化: FP8 GEMM]."""
     x = _f(x)
     mod = block_modulation(m, wts["mod_bias"])
     outs, parts = [], []
@@ -257,16 +274,17 @@ def block(x, m, wts: Dict[str, np.ndarray], ctx, heads: int, eps: float = 1e-6,
         xb = x[b]
         h1 = modulate(layer_norm(xb, eps), mod["shift1"][b], mod["scale1"][b])
         sa = self_attention(h1, wts["sa_wqkv"], wts["sa_bqkv"], wts["sa_wo"], wts["sa_bo"],
-                            heads, rows=rows)
+                            heads, rows=rows, fp8=fp8)
         xr = xb if rows is None else xb[rows]
         x1 = xr + mod["gate1"][b] * sa
         ca = cross_attention(x1, _f(ctx[b]), wts["ca_wq"], wts["ca_bq"], wts["ca_wkv"],
                              wts["ca_bkv"], wts["ca_wo"], wts["ca_bo"], heads, eps,
                              img=None if img is None else _f(img[b]),
-                             wkv_img=wts.get("ca_wkv_img"), bkv_img=wts.get("ca_bkv_img"))
+                             wkv_img=wts.get("ca_wkv_img"), bkv_img=wts.get("ca_bkv_img"),
+                             fp8=fp8)
         x2 = x1 + ca
         h2 = modulate(layer_norm(x2, eps), mod["shift2"][b], mod["scale2"][b])
-        z = ffn(h2, wts["ffn_w1"], wts["ffn_b1"], wts["ffn_w2"], wts["ffn_b2"])
+        z = ffn(h2, wts["ffn_w1"], wts["ffn_b1"], wts["ffn_w2"], wts["ffn_b2"], fp8=fp8)
         x3 = x2 + mod["gate2"][b] * z
         outs.append(x3)
         parts.append({"sa": sa, "ca": ca, "ffn": z})
@@ -483,13 +501,20 @@ def quantize_tensor_fp8(w):
     return _quant_f32(w32, inv), F64(s)
 
 
-def linear_fp8(x, w, b=None):
-    """y = (xq wq^T) * sx[:, None] * sw + b with per-token xq, per-tensor wq (R22)
-    [Note, Infra / 推理优化: FP8 GEMM, per-tensor weights + per-token activations]."""
+def linear_fp8_q(x, qw, sw, b=None):
+    """y = (xq qw^T) * sx[:, None] * sw + b for a weight already quantised
+    (qw, sw) -- possibly a row slice of a tensor quantised as a whole -- and
+    the per-token quantisation of x (R22)."""
     qx, sx = quantize_rows_fp8(x)
-    qw, sw = quantize_tensor_fp8(w)
-    y = (qx @ qw.T) * sx[:, None] * sw
+    y = (qx @ _f(qw).T) * sx[:, None] * F64(sw)
     if b is not None:
         y = y + _f(b)[None, :]
     return y
+
+
+def linear_fp8(x, w, b=None):
+    """y = (xq wq^T) * sx[:, None] * sw + b with per-token xq, per-tensor wq (R22)
+    [Note, Infra / 推理优化: FP8 GEMM, per-tensor weights + per-token activations]."""
+    qw, sw = quantize_tensor_fp8(w)
+    return linear_fp8_q(x, qw, sw, b)
 

@@ -506,3 +506,45 @@ def pin_fp8(O):
     bias = r.standard_normal(9)
     _close(O.linear_fp8(xa, wb, bias), xa.astype(np.float64) @ wb.astype(np.float64).T + bias, 1e-9,
            "linear_fp8 on grid operands")
+
+
+def pin_fp8_block(O):
+    """The FP8 switch of the block touches only the six Linear layers: with the
+    quantisers replaced by the identity (scale 1) the FP8 block equals the
+    exact block bit for bit; with real E4M3 quantisation the block update stays
+    within a few percent of the exact one."""
+    r = _rng(51)
+    d, F, H, L, Lc = 64, 128, 2, 20, 6
+    w = {"sa_wqkv": r.standard_normal((3 * d, d)) * 0.1, "sa_bqkv": r.standard_normal(3 * d) * 0.02,
+         "sa_wo": r.standard_normal((d, d)) * 0.1, "sa_bo": r.standard_normal(d) * 0.02,
+         "ca_wq": r.standard_normal((d, d)) * 0.1, "ca_bq": r.standard_normal(d) * 0.02,
+         "ca_wkv": r.standard_normal((2 * d, d)) * 0.1, "ca_bkv": r.standard_normal(2 * d) * 0.02,
+         "ca_wo": r.standard_normal((d, d)) * 0.1, "ca_bo": r.standard_normal(d) * 0.02,
+         "ffn_w1": r.standard_normal((F, d)) * 0.1, "ffn_b1": r.standard_normal(F) * 0.02,
+         "ffn_w2": r.standard_normal((d, F)) * 0.1, "ffn_b2": r.standard_normal(d) * 0.02,
+         "mod_bias": r.standard_normal(6 * d) * 0.02}
+    x, m, ctx = r.standard_normal((1, L, d)), r.standard_normal((1, 6 * d)) * 0.3, r.standard_normal((1, Lc, d))
+    exact = O.block(x, m, w, ctx, H)
+    qr, qt = O.quantize_rows_fp8, O.quantize_tensor_fp8
+    seen_w, seen_x = [], []
+    try:
+        def fake_rows(a):
+            seen_x.append(np.shape(a))
+            return np.asarray(a, np.float64), np.ones(np.shape(a)[0])
+
+        def fake_tensor(a):
+            seen_w.append(np.shape(a))
+            return np.asarray(a, np.float64), 1.0
+        O.quantize_rows_fp8, O.quantize_tensor_fp8 = fake_rows, fake_tensor
+        same = O.block(x, m, w, ctx, H, fp8=True)
+    finally:
+        O.quantize_rows_fp8, O.quantize_tensor_fp8 = qr, qt
+    assert np.array_equal(same, exact), "fp8 switch changed more than the Linear layers"
+    # six weight tensors, each quantised whole (Wqkv as one [3d, d] tensor)
+    assert sorted(seen_w) == sorted([(3 * d, d), (d, d), (d, d), (d, d), (F, d), (d, F)]), seen_w
+    # activations: h1 for Q, K, V; o; LN(x) for the CA query; CA o; h2; GELU(u)
+    assert sorted(seen_x) == sorted([(L, d)] * 7 + [(L, F)]), seen_x
+    q8 = O.block(x, m, w, ctx, H, fp8=True)
+    upd, upd8 = exact - x, q8 - x
+    rel = np.abs(upd8 - upd).sum() / np.abs(upd).sum()
+    assert 1e-4 < rel < 0.05, rel

@@ -12,8 +12,8 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 
 MUTATIONS = {
     "no attention scale": ("scale = 1.0 / math.sqrt(hd)", "scale = 1.0"),
-    "k/v weights swapped": ("k = linear(hmod, wqkv[d:2 * d], bqkv[d:2 * d])",
-                            "k = linear(hmod, wqkv[2 * d:], bqkv[2 * d:])"),
+    "k/v weights swapped": ("k = lin(hmod, slice(d, 2 * d), bqkv[d:2 * d])",
+                            "k = lin(hmod, slice(2 * d, 3 * d), bqkv[2 * d:])"),
     "modulate sign": ("_f(xhat) * (1.0 + _f(scale))", "_f(xhat) * (1.0 - _f(scale))"),
     "sin/cos order": ("[np.cos(arg), np.sin(arg)]", "[np.sin(arg), np.cos(arg)]"),
     "unbiased variance": ("var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)",
@@ -34,7 +34,7 @@ MUTATIONS = {
     "t-MLP without SiLU": ("linear(silu(linear(e, w1, b1)), w2, b2)", "linear(linear(e, w1, b1), w2, b2)"),
     "block bias sign": ("_f(m) + _f(beta)[None, :]", "_f(m) - _f(beta)[None, :]"),
     "sinusoid base": ("math.log(10000.0)", "math.log(1000.0)"),
-    "LN on modulated input for CA": ("q = linear(layer_norm(xq, eps), wq, bq)", "q = linear(xq, wq, bq)"),
+    "LN on modulated input for CA": ("q = lin(layer_norm(xq, eps), wq, bq)", "q = lin(xq, wq, bq)"),
     "seq_len off by one": ("return (1 + T // 4) * (height // 16)", "return (T // 4) * (height // 16)"),
     "Euler step sign": ("x[:, :out_ch] = x[:, :out_ch] + (tau[k + 1] - tau[k]) * v",
                         "x[:, :out_ch] = x[:, :out_ch] - (tau[k + 1] - tau[k]) * v"),
@@ -48,7 +48,14 @@ MUTATIONS = {
                          "return np.float32(240.0) / amax, amax / np.float32(240.0)"),
     "fp8 activation scale per tensor": ("inv, s = _scale_f32(np.max(np.abs(x32[i])) if x32.shape[1] else 0.0)",
                                         "inv, s = _scale_f32(np.max(np.abs(x32)))"),
-    "fp8 dequant without weight scale": ("y = (qx @ qw.T) * sx[:, None] * sw", "y = (qx @ qw.T) * sx[:, None]"),
+    "fp8 dequant without weight scale": ("y = (qx @ _f(qw).T) * sx[:, None] * F64(sw)",
+                                         "y = (qx @ _f(qw).T) * sx[:, None]"),
+    "fp8 Wqkv scale per slice": ("lin = lambda x, sl, b: linear_fp8_q(x, qw[sl], sw, b)",
+                                 "lin = lambda x, sl, b: linear_fp8(x, wqkv[sl], b)"),
+    "fp8 FFN down left exact": ("return lin(gelu_tanh(lin(hmod, w1, b1)), w2, b2)",
+                                "return linear(gelu_tanh(lin(hmod, w1, b1)), w2, b2)"),
+    "fp8 flag dropped for CA": ("wkv_img=wts.get(\"ca_wkv_img\"), bkv_img=wts.get(\"ca_bkv_img\"),\n                             fp8=fp8)",
+                                "wkv_img=wts.get(\"ca_wkv_img\"), bkv_img=wts.get(\"ca_bkv_img\"))"),
     "head split strided": ("k[:, h * hd:(h + 1) * hd],\n                                     v[:, h * hd:(h + 1) * hd])",
                            "k[:, h::heads],\n                                     v[:, h::heads])"),
 }
