@@ -72,6 +72,10 @@ READINGS = {
                     "decided in float32 as the kernel does: inv = 448 / amax (float32 "
                     "division), v = x * inv (float32), clamp to +-448, round to E4M3; an "
                     "all-zero row or tensor gets scale 1; y = (xq wq^T) sx sw + b",
+    "R23 FP8 activations": "the input of an FP8 GEMM is the bf16 activation a bf16 model holds "
+                           "(the pages run the model in bf16 and quantise for the GEMM); it is "
+                           "rounded to bf16 (nearest even) before its per-token quantisation, so "
+                           "the E4M3 code is decided from a bf16 value on both sides",
 }
 
 
@@ -501,11 +505,20 @@ def quantize_tensor_fp8(w):
     return _quant_f32(w32, inv), F64(s)
 
 
+def bf16_round(x):
+    """Round to the nearest bfloat16 value, ties to even, returned as float64:
+    the float32 value's low 16 bits are dropped after adding 0x7FFF plus the
+    lowest kept bit (finite inputs)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(F64)
+
+
 def linear_fp8_q(x, qw, sw, b=None):
     """y = (xq qw^T) * sx[:, None] * sw + b for a weight already quantised
     (qw, sw) -- possibly a row slice of a tensor quantised as a whole -- and
-    the per-token quantisation of x (R22)."""
-    qx, sx = quantize_rows_fp8(x)
+    the per-token quantisation of the bf16 activation x (R22, R23)."""
+    qx, sx = quantize_rows_fp8(bf16_round(x))
     y = (qx @ _f(qw).T) * sx[:, None] * F64(sw)
     if b is not None:
         y = y + _f(b)[None, :]

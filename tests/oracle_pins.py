@@ -525,7 +525,7 @@ def pin_fp8_block(O):
          "mod_bias": r.standard_normal(6 * d) * 0.02}
     x, m, ctx = r.standard_normal((1, L, d)), r.standard_normal((1, 6 * d)) * 0.3, r.standard_normal((1, Lc, d))
     exact = O.block(x, m, w, ctx, H)
-    qr, qt = O.quantize_rows_fp8, O.quantize_tensor_fp8
+    qr, qt, br = O.quantize_rows_fp8, O.quantize_tensor_fp8, O.bf16_round
     seen_w, seen_x = [], []
     try:
         def fake_rows(a):
@@ -536,9 +536,10 @@ def pin_fp8_block(O):
             seen_w.append(np.shape(a))
             return np.asarray(a, np.float64), 1.0
         O.quantize_rows_fp8, O.quantize_tensor_fp8 = fake_rows, fake_tensor
+        O.bf16_round = lambda a: np.asarray(a, np.float64)
         same = O.block(x, m, w, ctx, H, fp8=True)
     finally:
-        O.quantize_rows_fp8, O.quantize_tensor_fp8 = qr, qt
+        O.quantize_rows_fp8, O.quantize_tensor_fp8, O.bf16_round = qr, qt, br
     assert np.array_equal(same, exact), "fp8 switch changed more than the Linear layers"
     # six weight tensors, each quantised whole (Wqkv as one [3d, d] tensor)
     assert sorted(seen_w) == sorted([(3 * d, d), (d, d), (d, d), (d, d), (F, d), (d, F)]), seen_w
@@ -548,3 +549,27 @@ def pin_fp8_block(O):
     upd, upd8 = exact - x, q8 - x
     rel = np.abs(upd8 - upd).sum() / np.abs(upd).sum()
     assert 1e-4 < rel < 0.05, rel
+    # the activation enters the quantiser as bf16 (R23): x and its bf16 rounding agree
+    xa = r.standard_normal((5, d))
+    assert np.array_equal(O.linear_fp8(xa, w["ffn_w1"], w["ffn_b1"]),
+                          O.linear_fp8(O.bf16_round(xa), w["ffn_w1"], w["ffn_b1"]))
+    assert not np.array_equal(O.linear_fp8(xa, w["ffn_w1"], w["ffn_b1"]),
+                              O.linear_fp8(xa.astype(np.float32).astype(np.float64) * (1 + 2.0 ** -7),
+                                           w["ffn_w1"], w["ffn_b1"]))
+
+
+def pin_bf16_round(O):
+    """bf16 rounding against torch's float32 -> bfloat16 conversion (a library
+    routine), including exact ties, and its closed-form error bound."""
+    import torch
+    r = _rng(52)
+    x = np.concatenate([r.standard_normal(4000) * 10.0 ** r.integers(-6, 6, 4000),
+                        # ties: a bf16 value plus half its unit in the last place
+                        (1.0 + np.arange(1, 200) * 2.0 ** -7) + 2.0 ** -8,
+                        -(1.0 + np.arange(1, 200) * 2.0 ** -7) - 2.0 ** -8, [0.0, -0.0, 65504.0]])
+    got = O.bf16_round(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, ref)
+    x32 = x.astype(np.float32).astype(np.float64)
+    assert np.all(np.abs(got - x32) <= np.abs(x32) * 2.0 ** -8)
+

@@ -50,6 +50,9 @@ MUTATIONS = {
                                         "inv, s = _scale_f32(np.max(np.abs(x32)))"),
     "fp8 dequant without weight scale": ("y = (qx @ _f(qw).T) * sx[:, None] * F64(sw)",
                                          "y = (qx @ _f(qw).T) * sx[:, None]"),
+    "fp8 activation not bf16": ("qx, sx = quantize_rows_fp8(bf16_round(x))", "qx, sx = quantize_rows_fp8(x)"),
+    "bf16 ties away from zero": ("u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000",
+                                 "u = (u + 0x8000) & 0xFFFF0000"),
     "fp8 Wqkv scale per slice": ("lin = lambda x, sl, b: linear_fp8_q(x, qw[sl], sw, b)",
                                  "lin = lambda x, sl, b: linear_fp8(x, wqkv[sl], b)"),
     "fp8 FFN down left exact": ("return lin(gelu_tanh(lin(hmod, w1, b1)), w2, b2)",
