@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 
 # HBM bytes per self-attention launch of this workload, from two rocprofv3
 # --pmc passes over `bench.py --traffic-pass` (FETCH_SIZE, then WRITE_SIZE,
@@ -187,6 +188,119 @@ def sampler_bench(n_steps: int, warmup: int):
     }), flush=True)
 
 
+def gemm_bench(reps: int):
+    """The block's Linear layers of the 1.3B model at 480P (M = 32760 tokens) in
+    bf16 (wan_linear_fwd) and FP8 (wan_linear_fp8_fwd on operands quantised
+    beforehand; the per-token quantisation of the activations is timed on its
+    own).  Seeded N(0, 1) activations, N(0, 0.02) weights."""
+    import torch
+
+    import video_diffusion_transformer_block_amd as W
+    M = 32760
+    shapes = [("qk", 3072, 1536, 0), ("oproj", 1536, 1536, 1), ("ffn_up", 8960, 1536, 2),
+              ("ffn_down", 1536, 8960, 1)]
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    g = torch.Generator(device="cpu").manual_seed(11)
+    res = {}
+    for name, N, K, mode in shapes:
+        x = torch.randn((M, K), generator=g).to(torch.bfloat16).cuda()
+        w = (torch.randn((N, K), generator=g) * 0.02).to(torch.bfloat16).cuda()
+        b = (torch.randn(N, generator=g) * 0.02).to(torch.bfloat16).cuda()
+        y = torch.empty((M, N), dtype=torch.float32 if mode == 1 else torch.bfloat16, device="cuda")
+        qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        sx = torch.empty(M, dtype=torch.float32, device="cuda")
+        qw = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+        sw = torch.empty(1, dtype=torch.float32, device="cuda")
+        W.quantize_tensor_fp8(w, qw, sw, torch.empty(256, dtype=torch.uint8, device="cuda"), stream)
+        W.quantize_rows_fp8(x, qx, sx, stream)
+        fl = 2.0 * M * N * K
+        ms_bf = timed(lambda: W.linear_fwd(x, w, b, y, M, N, K, mode, stream))
+        ms_f8 = timed(lambda: W.linear_fp8_fwd(qx, sx, qw, sw, b, y, M, N, K, mode, stream))
+        ms_q = timed(lambda: W.quantize_rows_fp8(x, qx, sx, stream))
+        res[name] = {"M": M, "N": N, "K": K,
+                     "bf16_ms": round(ms_bf, 4), "bf16_tflops": round(fl / ms_bf / 1e9, 1),
+                     "fp8_ms": round(ms_f8, 4), "fp8_tflops": round(fl / ms_f8 / 1e9, 1),
+                     "fp8_frac_of_fp8_peak": round(fl / ms_f8 / 1e9 / PEAK_FP8_TFLOPS, 4),
+                     "quant_rows_ms": round(ms_q, 4),
+                     "quant_rows_gbs": round(M * K * 3 / ms_q / 1e6, 1)}
+    print(json.dumps({"gemm": "1.3B block Linear layers at 480P, bf16 vs FP8 (E4M3)",
+                      "shapes": res, "peak_bf16_tflops": PEAK_BF16_TFLOPS,
+                      "peak_fp8_tflops": PEAK_FP8_TFLOPS, "data": "synthetic"}), flush=True)
+
+
+def fp8_block_bench(steps: int, warmup: int):
+    """The 1.3B block at 480P (L = 32760) with bf16 Linear layers
+    (wan_dit_block_fwd) and with E4M3 ones (wan_dit_block_fp8_fwd, weights
+    quantised once beforehand, activation quantisation inside the timed
+    region), same weights and inputs."""
+    import numpy as np
+    import torch
+
+    import synth
+    import video_diffusion_transformer_block_amd as W
+    work = synth.CONFIGS[2]
+    m = work.model
+    B, L, d = work.batch, work.L, m.dim
+    cfg = W.make_cfg(dim=d, heads=m.heads, ffn=m.ffn, n_blocks=1, text_len=m.text_len, eps=m.eps,
+                     dtype="bf16")
+    inp = synth.workload_inputs(work)
+    bw = synth.block_weights(work, 0)
+
+    def up(a, dt):
+        t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+        return (t.to(torch.bfloat16) if dt == "bf16" else t).cuda()
+
+    bwd = {k: up(v, "f32" if k == "mod_bias" else "bf16") for k, v in bw.items()}
+    desc = W.block_weights(bwd)
+    x0 = up(inp["x"], "f32")
+    x = x0.clone()
+    ctx = up(inp["ctx"], "bf16")
+    mod = (torch.randn((B, 6 * d), generator=torch.Generator().manual_seed(5)) * 0.3).cuda()
+    stream = torch.cuda.current_stream()
+    qbuf = torch.empty(W.block_fp8_bytes(cfg), dtype=torch.uint8, device="cuda")
+    W.quantize_block_fp8(cfg, desc, qbuf, stream)
+    ws = torch.empty(W.block_fp8_workspace_bytes(cfg, B, work.lat_f, work.Hp, work.Wp),
+                     dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        x.copy_(x0)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    geo = (B, work.lat_f, work.Hp, work.Wp)
+    ms_bf = timed(lambda: W.dit_block_fwd(cfg, x, *geo, mod, desc, ctx, None, ws, stream))
+    ms_f8 = timed(lambda: W.dit_block_fp8_fwd(cfg, x, *geo, mod, desc, qbuf, ctx, None, ws, stream))
+    if not bool(torch.isfinite(x).all()):
+        raise RuntimeError("non-finite FP8 block output")
+    print(json.dumps({"fp8_block": f"{work.name}: bf16 vs FP8 (E4M3) Linear layers",
+                      "tokens": B * L, "steps": steps, "warmup": warmup,
+                      "bf16_ms": round(ms_bf, 4), "fp8_ms": round(ms_f8, 4),
+                      "speedup": round(ms_bf / ms_f8, 4),
+                      "fp8_tokens_per_s": round(B * L / (ms_f8 * 1e-3), 1), "data": "synthetic"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +311,11 @@ def main():
     ap.add_argument("--sampler", type=int, default=0, metavar="STEPS",
                     help="time STEPS sampler steps of the 1.3B guidance pair with and without the "
                          "cross-attention K/V cache (prints its own JSON line) instead of the block")
+    ap.add_argument("--gemm", action="store_true",
+                    help="time the block's Linear layers in bf16 and FP8 (prints its own JSON line)")
+    ap.add_argument("--fp8-block", action="store_true",
+                    help="time the 1.3B block with bf16 and with FP8 Linear layers "
+                         "(prints its own JSON line)")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="only run 3 self-attention launches and 3 plain 512-MiB device copies "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and their calibration)")
@@ -211,6 +330,12 @@ def main():
 
     if args.sampler:
         sampler_bench(args.sampler, max(1, args.warmup))
+        return
+    if args.gemm:
+        gemm_bench(10)
+        return
+    if args.fp8_block:
+        fp8_block_bench(args.steps, max(1, args.warmup))
         return
 
     import numpy as np

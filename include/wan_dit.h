@@ -43,7 +43,8 @@ extern "C" {
 #define WAN_ERR_NULL      -1  /* a required pointer is NULL                         */
 #define WAN_ERR_SHAPE     -2  /* sizes inconsistent: odd H/8 or W/8, dim != heads*head_dim,
                                  unsupported head_dim, empty sequence, ...          */
-#define WAN_ERR_DTYPE     -3  /* cfg->dtype is neither WAN_F32 nor WAN_BF16          */
+#define WAN_ERR_DTYPE     -3  /* cfg->dtype is neither WAN_F32 nor WAN_BF16, or is
+                                 WAN_F32 for an FP8 entry point                     */
 #define WAN_ERR_WORKSPACE -4  /* ws_bytes smaller than wan_workspace_bytes()         */
 #define WAN_ERR_CONFIG    -5  /* I2V pointers inconsistent with in_ch / img_len      */
 #define WAN_ERR_HIP       -6  /* a HIP launch failed                                 */
@@ -265,6 +266,39 @@ int wan_quantize_tensor_fp8(const void *w, long n, void *q, float *scale, void *
  * 2: y bf16 = GELU_tanh(.).  float32 accumulation. */
 int wan_linear_fp8_fwd(const void *xq, const float *x_scale, const void *wq, const float *w_scale,
                        const void *b, void *y, int M, int N, int K, int mode, void *stream);
+
+/* ---- FP8 block -------------------------------------------------------------- */
+/* The block of wan_dit_block_fwd with its six Linear layers -- QKV, self-
+ * attention out, cross-attention query, cross-attention out, FFN up, FFN
+ * down -- on E4M3 operands ([Note] Infra (推理优化): FP8 GEMM; the block of
+ * [Note] Diffusion Transformer): each weight quantised per tensor (Wqkv as one
+ * [3d, d] tensor), each bf16 activation quantised per token right before the
+ * GEMM that reads it, float32 accumulation, dequantisation and bias in the
+ * epilogue.  LayerNorm, modulation, attention, GELU, gates and the residual
+ * stream are those of wan_dit_block_fwd; the text / image keys and values are
+ * projected in bf16.  bf16 configurations only (WAN_ERR_DTYPE otherwise). */
+
+/* Bytes of one block's packed FP8 weights; 0 for an invalid or float32 cfg. */
+size_t wan_block_fp8_bytes(const wan_cfg_t *cfg);
+
+/* Quantise the six Linear weights of block w (bf16, device) into qbuf (device,
+ * 256-byte aligned, at least wan_block_fp8_bytes; the layout is private to the
+ * library).  Done once per set of weights; every wan_dit_block_fp8_fwd call
+ * with those weights reads the result. */
+int wan_quantize_block_fp8(const wan_cfg_t *cfg, const wan_block_weights_t *w, void *qbuf,
+                           size_t qbuf_bytes, void *stream);
+
+/* Workspace bytes of wan_dit_block_fp8_fwd (0 for an invalid cfg / shape). */
+size_t wan_block_fp8_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int Hp, int Wp);
+
+/* wan_dit_block_fwd with FP8 Linear layers.  Arguments as there, plus qbuf
+ * written by wan_quantize_block_fp8 from the same w.  From w only the biases,
+ * mod_bias and the text / image K/V weights are read: the six quantised weight
+ * pointers may be NULL.  B * L * max(d, ffn) < 2^31. */
+int wan_dit_block_fp8_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, int Wp,
+                          const float *mod, const wan_block_weights_t *w, const void *qbuf,
+                          const void *ctx, const void *img_ctx, void *ws, size_t ws_bytes,
+                          void *stream);
 
 #ifdef __cplusplus
 }

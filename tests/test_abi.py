@@ -104,3 +104,35 @@ def test_invalid_arguments_enqueue_nothing(W):
     assert L.wan_attention_fwd(dummy, 100, dummy, 256, dummy, 64, 64, dummy, 256, 1, 2, 4, 4,
                                None) == -2                                          # ldq < H*128
     assert L.wan_linear_fwd(dummy, dummy, None, dummy, 4, 4, 100, 0, None) == -2   # K % 64
+
+
+def test_fp8_block_sizes(W):
+    c = _cfg(W)
+    d, F = 256, 512
+    # six scales, six running-maximum words, then the E4M3 weights, each region 256-aligned
+    want = 256 + 256 + 3 * d * d + 3 * d * d + 2 * F * d
+    assert W.block_fp8_bytes(c) == want
+    assert W.block_fp8_bytes(_cfg(W, dtype="f32", heads=4)) == 0
+    # the FP8 block workspace is a bf16 block workspace plus one activation's
+    # codes (the widest, [B*L, ffn]) and its per-token scales
+    B, L = 2, 3 * 4 * 6
+    ws8 = W.block_fp8_workspace_bytes(c, B, 3, 4, 6)
+    assert ws8 >= B * L * F + B * L * 4 and ws8 % 256 == 0
+    assert W.block_fp8_workspace_bytes(c, 9, 3, 4, 6) == 0
+
+
+def test_fp8_block_invalid_arguments(W):
+    L = W.lib()
+    c = _cfg(W)
+    cf = _cfg(W, dtype="f32", heads=4)
+    dummy = C.c_void_p(256)   # never dereferenced: every call below fails validation first
+    bw = W.block_weights({})
+    assert L.wan_quantize_block_fp8(C.byref(cf), C.byref(bw), dummy, 1 << 30, None) == -3
+    assert L.wan_quantize_block_fp8(C.byref(c), C.byref(bw), dummy, 1 << 30, None) == -1
+    args = (dummy, 2, 3, 4, 6, dummy, C.byref(bw))
+    assert L.wan_dit_block_fp8_fwd(C.byref(cf), *args, dummy, dummy, None, dummy, 1 << 40, None) == -3
+    assert L.wan_dit_block_fp8_fwd(C.byref(c), *args, None, dummy, None, dummy, 1 << 40, None) == -1
+    assert L.wan_dit_block_fp8_fwd(C.byref(c), *args, C.c_void_p(272), dummy, None, dummy, 1 << 40,
+                                   None) == -2                                     # qbuf misaligned
+    assert L.wan_dit_block_fp8_fwd(C.byref(c), *args, dummy, dummy, None, dummy, 1 << 40, None) == -1
+

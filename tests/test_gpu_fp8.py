@@ -133,3 +133,99 @@ def test_linear_fp8_full_ffn_shape_sampled_rows():
     gs = y[torch.from_numpy(rows).cuda()].cpu().numpy()
     bound = _rel_bound(K) * (np.abs(qxo) @ np.abs(qwo).T) * sxo[:, None] * swo + 1e-7
     assert np.max(np.abs(gs - o) - bound) <= 0, np.max(np.abs(gs - o))
+
+
+# ---- FP8 block: wan_quantize_block_fp8 + wan_dit_block_fp8_fwd against the
+# oracle's block with its six Linear layers in E4M3 (same weights, inputs).
+FP8_BLOCKS = {
+    "bf16-ragged-b2": synth.mini(11, "bf16-ragged-b2", dim=384, heads=3, ffn=640, n_blocks=1,
+                                 lat_f=3, lat_h=20, lat_w=40, batch=2, text_len=40, kind="block"),
+    "bf16-i2v": synth.mini(12, "bf16-i2v", dim=256, heads=2, ffn=512, n_blocks=1, lat_f=2,
+                           lat_h=16, lat_w=24, batch=1, text_len=64, img_len=257, kind="block"),
+}
+
+
+def _run_block_fp8(work, rows=None):
+    import video_diffusion_transformer_block_amd as W
+    from tests.gpu_util import cfg_of, run_tmlp, up, up_block
+    m = work.model
+    cfg = cfg_of(work)
+    inp = synth.workload_inputs(work)
+    tw = synth.tmlp_weights(work)
+    bw = synth.block_weights(work, 0)
+    img = None
+    if m.img_len:
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2025, work.cid, 77])))
+        img = synth.bf16_round(g.standard_normal((work.batch, m.img_len, m.dim), dtype=np.float32))
+    twd = {k: up(v, m.dtype) for k, v in tw.items()}
+    mod = run_tmlp(cfg, work, twd, up(inp["t"], "f32"))
+    x = up(inp["x"], "f32")
+    bwd = up_block(bw, m.dtype)
+    desc = W.block_weights(bwd)
+    qbuf = torch.empty(W.block_fp8_bytes(cfg), dtype=torch.uint8, device="cuda")
+    W.quantize_block_fp8(cfg, desc, qbuf)
+    # the six quantised weights are not read: pass their pointers as NULL
+    desc8 = W.block_weights({k: v for k, v in bwd.items()
+                             if k not in ("sa_wqkv", "sa_wo", "ca_wq", "ca_wo", "ffn_w1", "ffn_w2")})
+    ws = torch.empty(W.block_fp8_workspace_bytes(cfg, work.batch, work.lat_f, work.Hp, work.Wp),
+                     dtype=torch.uint8, device="cuda")
+    W.dit_block_fp8_fwd(cfg, x, work.batch, work.lat_f, work.Hp, work.Wp, mod, desc8, qbuf,
+                        up(inp["ctx"], m.dtype), up(img, m.dtype) if img is not None else None, ws)
+    torch.cuda.synchronize()
+    o_mod = O.tmlp(inp["t"], tw["w1"], tw["b1"], tw["w2"], tw["b2"])
+    o_x = O.block(inp["x"], o_mod, bw, inp["ctx"], m.heads, m.eps, img=img, rows=rows, fp8=True)
+    e_x = O.block(inp["x"], o_mod, bw, inp["ctx"], m.heads, m.eps, img=img, rows=rows)
+    return inp["x"], x.cpu().numpy(), o_x, e_x, qbuf, bw
+
+
+def _check_fp8_block(x0, g_x, o_x, e_x):
+    """The block output to the usual bound (max-abs 3e-2, mean-rel 1e-2).  The
+    block's update (x_out - x_in) is judged against the size of the FP8 effect
+    itself: an E4M3 code is an integer decided from a bf16 activation, and the
+    GPU's bf16 activations (attention with bf16 probabilities, float32
+    LayerNorm and GELU) differ from the oracle's in the last bf16 place often
+    enough that some codes move by one E4M3 step (6-12 %) -- deviations that
+    two correct FP8 implementations show between each other.  The GPU update
+    must sit within half the distance between the FP8 and the exact oracle
+    block, i.e. decisively on the FP8 side."""
+    from tests.gpu_util import assert_parity, metrics
+    du, de = g_x - x0, o_x - x0
+    dev = metrics(du, de)
+    eff = metrics(e_x - x0, de)
+    print("output", metrics(g_x, o_x), "update", dev, "fp8 effect", eff, flush=True)
+    assert_parity(g_x, o_x, 3e-2, 1e-2, "fp8 block output")
+    assert dev["mean_rel"] <= 0.5 * eff["mean_rel"], (dev, eff)
+    assert dev["max_abs"] <= 0.75 * eff["max_abs"], (dev, eff)
+
+
+@pytest.mark.parametrize("name", list(FP8_BLOCKS))
+def test_block_fp8_mini(name):
+    work = FP8_BLOCKS[name]
+    print(f"fp8 block {name} L={work.L} d={work.model.dim}", flush=True)
+    x0, g_x, o_x, e_x, qbuf, bw = _run_block_fp8(work)
+    _check_fp8_block(x0, g_x, o_x, e_x)
+    # the packed weights: the scales and codes of Wqkv (quantised whole) and FFN down
+    q = qbuf.cpu()
+    d, F = work.model.dim, work.model.ffn
+    sc = q[:24].view(torch.float32).numpy()
+    qo, so = O.quantize_tensor_fp8(bw["sa_wqkv"])
+    assert sc[0] == np.float32(so)
+    codes = q[512:512 + 3 * d * d].view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(codes.reshape(3 * d, d), qo)
+    q6, s6 = O.quantize_tensor_fp8(bw["ffn_w2"])
+    assert sc[5] == np.float32(s6)
+    off6 = 512 + 3 * d * d + 3 * d * d + F * d
+    codes6 = q[off6:off6 + d * F].view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(codes6.reshape(d, F), q6)
+
+
+def test_block_fp8_full_size_sampled_rows():
+    """The 1.3B block at 480P (L = 32760) in FP8: the whole block on the GPU,
+    sampled token rows in the oracle."""
+    work = synth.CONFIGS[2]
+    L = work.L
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, L - 1, L - 2], rng.integers(0, L, 26)]))
+    print(f"fp8 block C2 full size L={L}, {len(rows)} sampled rows", flush=True)
+    x0, g_x, o_x, e_x, _, _ = _run_block_fp8(work, rows=rows)
+    _check_fp8_block(x0[:, rows], g_x[:, rows], o_x, e_x)

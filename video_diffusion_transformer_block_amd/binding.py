@@ -23,7 +23,10 @@ EXPORTS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_by
            "wan_status_str", "wan_tmlp_fwd", "wan_dit_block_fwd", "wan_dit_step_fwd",
            "wan_i2v_mask", "wan_attention_fwd", "wan_linear_fwd", "wan_kv_cache_fwd",
            "wan_dit_step_cached_fwd", "wan_euler_fwd", "wan_sample_fwd", "wan_quantize_rows_fp8",
-           "wan_quantize_tensor_fp8", "wan_linear_fp8_fwd")
+           "wan_quantize_tensor_fp8", "wan_linear_fp8_fwd", "wan_block_fp8_bytes",
+           "wan_quantize_block_fp8", "wan_block_fp8_workspace_bytes", "wan_dit_block_fp8_fwd")
+_SIZE_FNS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
+             "wan_block_fp8_bytes", "wan_block_fp8_workspace_bytes")
 
 
 class WanError(RuntimeError):
@@ -94,9 +97,15 @@ def lib() -> C.CDLL:
         L.wan_quantize_rows_fp8.argtypes = [vp, i, i, i, vp, i, vp, vp]
         L.wan_quantize_tensor_fp8.argtypes = [vp, C.c_long, vp, vp, vp, sz, vp]
         L.wan_linear_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+        L.wan_block_fp8_bytes.argtypes = [C.POINTER(Cfg)]
+        L.wan_quantize_block_fp8.argtypes = [C.POINTER(Cfg), C.POINTER(BlockW), vp, sz, vp]
+        L.wan_block_fp8_workspace_bytes.argtypes = [C.POINTER(Cfg), i, i, i, i]
+        L.wan_dit_block_fp8_fwd.argtypes = [C.POINTER(Cfg), vp, i, i, i, i, vp, C.POINTER(BlockW), vp,
+                                            vp, vp, vp, sz, vp]
         for n in EXPORTS:
-            if n not in ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
-                         "wan_status_str"):
+            if n in _SIZE_FNS:
+                getattr(L, n).restype = sz
+            elif n != "wan_status_str":
                 getattr(L, n).restype = i
         _lib = L
     return _lib
@@ -267,3 +276,24 @@ def linear_fp8_fwd(xq, x_scale, wq, w_scale, b, y, M, N, K, mode, stream=None):
                                                           _p(b), _p(y), M, N, K, mode,
                                                           _stream(stream)))
 
+
+def block_fp8_bytes(cfg: Cfg) -> int:
+    return int(lib().wan_block_fp8_bytes(C.byref(cfg)))
+
+
+def block_fp8_workspace_bytes(cfg: Cfg, B: int, lat_f: int, Hp: int, Wp: int) -> int:
+    return int(lib().wan_block_fp8_workspace_bytes(C.byref(cfg), B, lat_f, Hp, Wp))
+
+
+def quantize_block_fp8(cfg: Cfg, bw: BlockW, qbuf: torch.Tensor, stream=None):
+    _check("wan_quantize_block_fp8", lib().wan_quantize_block_fp8(C.byref(cfg), C.byref(bw), _p(qbuf),
+                                                                  _nbytes(qbuf), _stream(stream)))
+
+
+def dit_block_fp8_fwd(cfg: Cfg, x: torch.Tensor, B: int, lat_f: int, Hp: int, Wp: int,
+                      mod: torch.Tensor, bw: BlockW, qbuf: torch.Tensor, ctx: torch.Tensor,
+                      img_ctx: Optional[torch.Tensor], ws: torch.Tensor, stream=None):
+    _check("wan_dit_block_fp8_fwd",
+           lib().wan_dit_block_fp8_fwd(C.byref(cfg), _p(x), B, lat_f, Hp, Wp, _p(mod), C.byref(bw),
+                                       _p(qbuf), _p(ctx), _p(img_ctx), _p(ws), _nbytes(ws),
+                                       _stream(stream)))

@@ -62,10 +62,16 @@ template <int KIND, bool BROWS, bool SCALED = false>
 WAN_DEV void epi8(const GemmDesc &g, int m, int n, float *v) {
   const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
   const bool full = n + 8 <= g.N;
-  if (SCALED) {   // FP8 dequantisation: per-row (token) scale times the per-tensor weight scale
-    const float sc = g.a_scale[m] * g.b_scale[0];
+  if (SCALED) {   // FP8 dequantisation: row scale (per token or per tensor) times column scale
+    const float sa = g.a_scale[g.a_per_row ? m : 0];
+    if (g.b_per_col) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] *= sc;
+      for (int i = 0; i < 8; ++i) v[i] *= sa * g.b_scale[n + i < g.N ? n + i : g.N - 1];
+    } else {
+      const float sc = sa * g.b_scale[0];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] *= sc;
+    }
   }
   if (bias) {
     if (BROWS) {
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
 // while those MFMAs execute.  The epilogue scales by a_scale[m] * b_scale[0].
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-template <int KIND>
+template <int KIND, bool BROWS>
 __global__ __launch_bounds__(512, 1) void k_gemm_fp8(GemmDesc g) {
   constexpr int GBK8 = 64;                    // K tile, bytes = elements
   constexpr int RPB = 1024 / GBK8;            // rows per 1-KB direct-load block (16)
@@ -481,7 +487,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(GemmDesc g) {
 
   // the epilogue stages 8 wavefronts x 32 rows x 68 floats through its own LDS buffer
   __shared__ __attribute__((aligned(16))) float sEp[GW * 32 * 68];
-  epilogue<KIND, false, true>(g, acc, sEp, w, lane, m0, n0, wm, wn);
+  epilogue<KIND, BROWS, true>(g, acc, sEp, w, lane, m0, n0, wm, wn);
 }
 
 // per-element epilogue (float32 path)
@@ -558,14 +564,19 @@ static void gemm_go(const GemmDesc &g, hipStream_t s) {
 hipError_t launch_gemm(const GemmDesc &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.fp8) {
-    if (g.K % 64 || !g.a_scale || !g.b_scale || g.bias_rows || g.f32) return hipErrorInvalidValue;
+    if (g.K % 64 || !g.a_scale || !g.b_scale || g.f32) return hipErrorInvalidValue;
     if ((long)g.M * g.lda >= (1L << 31) || (long)g.N * g.ldb >= (1L << 31)) return hipErrorInvalidValue;
     const int blocks = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
+    if (g.bias_rows) {
+      if (g.kind != OUT_BF16) return hipErrorInvalidValue;
+      k_gemm_fp8<OUT_BF16, true><<<blocks, GW * 64, 0, s>>>(g);
+      return hipGetLastError();
+    }
     switch (g.kind) {
-      case OUT_BF16: k_gemm_fp8<OUT_BF16><<<blocks, GW * 64, 0, s>>>(g); break;
-      case OUT_F32: k_gemm_fp8<OUT_F32><<<blocks, GW * 64, 0, s>>>(g); break;
-      case OUT_GELU: k_gemm_fp8<OUT_GELU><<<blocks, GW * 64, 0, s>>>(g); break;
-      case OUT_RESID: k_gemm_fp8<OUT_RESID><<<blocks, GW * 64, 0, s>>>(g); break;
+      case OUT_BF16: k_gemm_fp8<OUT_BF16, false><<<blocks, GW * 64, 0, s>>>(g); break;
+      case OUT_F32: k_gemm_fp8<OUT_F32, false><<<blocks, GW * 64, 0, s>>>(g); break;
+      case OUT_GELU: k_gemm_fp8<OUT_GELU, false><<<blocks, GW * 64, 0, s>>>(g); break;
+      case OUT_RESID: k_gemm_fp8<OUT_RESID, false><<<blocks, GW * 64, 0, s>>>(g); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -22,11 +22,12 @@ struct GemmDesc {
   const float *gate; long gate_bstride; int rows_per_batch;
   int f32;                     // operands / bias / C are float32 instead of bf16
   int npad;                    // OUT_BF16: columns N .. npad-1 of C are written as zeros
-  // FP8 (OCP E4M3) operands: A and B hold one byte per element, K % 128 == 0;
-  // acc is multiplied by a_scale[m] * b_scale[0] before the bias (per-token /
-  // per-tensor dequantisation)
+  // FP8 (OCP E4M3) operands: A and B hold one byte per element, K % 64 == 0;
+  // acc is multiplied by a_scale[a_per_row ? m : 0] * b_scale[b_per_col ? n : 0]
+  // before the bias (per-token / per-tensor dequantisation, either side)
   int fp8;
   const float *a_scale, *b_scale;
+  int a_per_row, b_per_col;
 };
 
 // Attention O = softmax(Q K^T * scale) V for every (batch, head); hd = 128, bf16.

@@ -31,12 +31,13 @@ long rup(long v, long a) { return (v + a - 1) / a * a; }
 struct Layout {
   size_t modb, hid, h, qk, vt, o, qc, kc, vtc, ki, vti, acc32, u;   // block
   size_t mod, x, P, pw, img1, img2, imgc;                           // step
+  size_t aq, as;                                                    // FP8 activations
   size_t total;
   long Lp, Lcp, Lip;
   int Kp;
 };
 
-Layout make_layout(const wan_cfg_t &c, int B, long L, bool step) {
+Layout make_layout(const wan_cfg_t &c, int B, long L, bool step, bool fp8 = false) {
   Layout y;
   memset(&y, 0, sizeof(y));
   const bool f32 = c.dtype == WAN_F32;
@@ -70,6 +71,10 @@ Layout make_layout(const wan_cfg_t &c, int B, long L, bool step) {
     y.img2 = take(Li ? B * Li * d * es : 0);
     y.imgc = take(Li ? B * Li * d * es : 0);
   }
+  if (fp8) {   // E4M3 codes of one activation (the widest: FFN hidden) + per-token scales
+    y.aq = take(B * L * (F > d ? F : d));
+    y.as = take(B * L * 4);
+  }
   y.total = off;
   return y;
 }
@@ -98,6 +103,38 @@ KvLayout kv_layout(const wan_cfg_t &c, int B) {
 // where a block finds its cross-attention keys / values
 struct KvPtrs {
   const void *kc, *vtc, *ki, *vti;
+};
+
+// Packed FP8 weights of one block: six float32 dequantisation scales (QKV,
+// SA out, CA query, CA out, FFN up, FFN down), six running-maximum words
+// used while quantising, then the six E4M3 weight tensors [out, in].
+struct Fp8Layout {
+  size_t sc, amax, w[6], total;
+  long n[6];   // elements of each weight
+};
+
+Fp8Layout fp8_layout(const wan_cfg_t &c) {
+  Fp8Layout q;
+  const long d = c.dim, F = c.ffn;
+  const long n[6] = {3 * d * d, d * d, d * d, d * d, F * d, d * F};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up(bytes, ALIGN); return o; };
+  q.sc = take(6 * 4);
+  q.amax = take(6 * 4);
+  for (int i = 0; i < 6; ++i) {
+    q.n[i] = n[i];
+    q.w[i] = take((size_t)n[i]);
+  }
+  q.total = off;
+  return q;
+}
+
+// FP8 operands of a block run: the packed weights and the activation buffers
+struct Fp8Ptrs {
+  const uint8_t *w[6];   // qkv, sa_wo, ca_wq, ca_wo, ffn_w1, ffn_w2
+  const float *sc;       // [6]
+  uint8_t *aq;           // activation codes
+  float *as;             // per-token scales
 };
 
 int check_cfg(const wan_cfg_t *c) {
@@ -176,6 +213,14 @@ int kv_project(const wan_cfg_t &c, int B, int Lk, const void *src, const void *w
   return WAN_OK;
 }
 
+// the same GEMM on E4M3 operands: acc * a_scale[m or 0] * b_scale[n or 0]
+GemmDesc fp8(GemmDesc g, const float *as, int a_per_row, const float *bs, int b_per_col) {
+  g.fp8 = 1;
+  g.a_scale = as; g.a_per_row = a_per_row;
+  g.b_scale = bs; g.b_per_col = b_per_col;
+  return g;
+}
+
 AttnDesc attn(const void *q, long ldq, const void *k, long ldk, const void *v, long ldv,
               long vbs, void *o, long ldo, int B, int H, int Lq, int Lk, int hd, int f32) {
   AttnDesc a;
@@ -187,10 +232,13 @@ AttnDesc attn(const void *q, long ldq, const void *k, long ldk, const void *v, l
 }
 
 // One block.  Cross-attention keys / values come from `cached` when it is
-// given, else they are projected from ctx (and img) into the workspace.
+// given, else they are projected from ctx (and img) into the workspace.  With
+// `q8` the six Linear layers run on E4M3 operands: each bf16 activation is
+// quantised per token right before the GEMM that reads it ([Note] Infra /
+// 推理优化: FP8 GEMM); the text / image K/V projections stay bf16.
 int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
               const wan_block_weights_t &w, const void *ctx, const void *img, const KvPtrs *cached,
-              char *ws, const Layout &y, hipStream_t s) {
+              char *ws, const Layout &y, hipStream_t s, const Fp8Ptrs *q8 = nullptr) {
   const int d = c.dim, F = c.ffn, H = c.heads, hd = c.head_dim, Lc = c.text_len, Li = c.img_len;
   const int f32 = c.dtype == WAN_F32;
   const size_t es = f32 ? 4 : 2;
@@ -207,6 +255,19 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
     WAN_TRY(launch_gemm(gemm(h, d, w.sa_wqkv, d, M, 3 * d, d, w.sa_bqkv, OUT_BF16, qk, 3 * d, 1), s));
     WAN_TRY(launch_attention(attn(qk, 3 * d, off(qk, d, es), 3 * d, off(qk, 2 * d, es), 3 * d, 0,
                                   o, d, B, H, (int)L, (int)L, hd, 1), s));
+  } else if (q8) {
+    WAN_TRY(launch_quant_rows_fp8(h, M, d, d, q8->aq, d, q8->as, s));
+    WAN_TRY(launch_gemm(fp8(gemm(q8->aq, d, q8->w[0], d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0),
+                            q8->as, 1, q8->sc + 0, 0), s));
+    for (int b = 0; b < B; ++b) {   // V^T = Wv h_b^T: weight scale per tensor, token scale per column
+      GemmDesc g = gemm(q8->w[0] + 2L * d * d, d, q8->aq + (long)b * L * d, d, d, (int)L, d,
+                        off(w.sa_bqkv, 2 * d, es), OUT_BF16, vt + b * y.Lp * es, (long)B * y.Lp, 0);
+      g.bias_rows = 1;
+      g.npad = (int)y.Lp;
+      WAN_TRY(launch_gemm(fp8(g, q8->sc + 0, 0, q8->as + (long)b * L, 1), s));
+    }
+    WAN_TRY(launch_attention(attn(qk, 2 * d, off(qk, d, es), 2 * d, vt, (long)B * y.Lp, y.Lp, o,
+                                  d, B, H, (int)L, (int)L, hd, 0), s));
   } else {
     WAN_TRY(launch_gemm(gemm(h, d, w.sa_wqkv, d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0), s));
     for (int b = 0; b < B; ++b) {
@@ -220,11 +281,21 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
     WAN_TRY(launch_attention(attn(qk, 2 * d, off(qk, d, es), 2 * d, vt, (long)B * y.Lp, y.Lp, o,
                                   d, B, H, (int)L, (int)L, hd, 0), s));
   }
-  WAN_TRY(launch_gemm(resid(o, d, w.sa_wo, M, d, d, w.sa_bo, x, modb + 2 * d, 6 * d, (int)L, f32), s));
+  // y = act W^T + b with the residual / GELU / plain epilogue g; on E4M3
+  // operands with q8 (act quantised per token first, K = g.K)
+  auto linear = [&](GemmDesc g, int wi) -> hipError_t {
+    if (!q8) return launch_gemm(g, s);
+    hipError_t e = launch_quant_rows_fp8(g.A, M, g.K, g.lda, q8->aq, g.K, q8->as, s);
+    if (e != hipSuccess) return e;
+    g.A = q8->aq; g.lda = g.K;
+    g.B = q8->w[wi]; g.ldb = g.K;
+    return launch_gemm(fp8(g, q8->as, 1, q8->sc + wi, 0), s);
+  };
+  WAN_TRY(linear(resid(o, d, w.sa_wo, M, d, d, w.sa_bo, x, modb + 2 * d, 6 * d, (int)L, f32), 1));
 
   // ---- cross-attention branch (pre-LN without modulation, ungated)
   WAN_TRY(launch_ln_mod(x, M, (int)L, d, modb, 6 * d, 0, 0, 0, c.eps, h, f32, s));
-  WAN_TRY(launch_gemm(gemm(h, d, w.ca_wq, d, M, d, d, w.ca_bq, OUT_BF16, qc, d, f32), s));
+  WAN_TRY(linear(gemm(h, d, w.ca_wq, d, M, d, d, w.ca_bq, OUT_BF16, qc, d, f32), 2));
   int st;
   if (cached) {
     kc = (char *)cached->kc; vtc = (char *)cached->vtc; ki = (char *)cached->ki; vti = (char *)cached->vti;
@@ -251,22 +322,24 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
   } else {
     WAN_TRY(launch_attention(at, s));
   }
-  WAN_TRY(launch_gemm(resid(o, d, w.ca_wo, M, d, d, w.ca_bo, x, nullptr, 0, (int)L, f32), s));
+  WAN_TRY(linear(resid(o, d, w.ca_wo, M, d, d, w.ca_bo, x, nullptr, 0, (int)L, f32), 3));
 
   // ---- FFN branch
   WAN_TRY(launch_ln_mod(x, M, (int)L, d, modb, 6 * d, 3 * d, 4 * d, 1, c.eps, h, f32, s));
-  WAN_TRY(launch_gemm(gemm(h, d, w.ffn_w1, d, M, F, d, w.ffn_b1, OUT_GELU, u, F, f32), s));
-  WAN_TRY(launch_gemm(resid(u, F, w.ffn_w2, M, d, F, w.ffn_b2, x, modb + 5 * d, 6 * d, (int)L, f32), s));
+  WAN_TRY(linear(gemm(h, d, w.ffn_w1, d, M, F, d, w.ffn_b1, OUT_GELU, u, F, f32), 4));
+  WAN_TRY(linear(resid(u, F, w.ffn_w2, M, d, F, w.ffn_b2, x, modb + 5 * d, 6 * d, (int)L, f32), 5));
   return WAN_OK;
 }
 
-int check_block_weights(const wan_cfg_t &c, const wan_block_weights_t *w) {
+// every pointer the block reads; with fp8 the six quantised weights are not read
+int check_block_weights(const wan_cfg_t &c, const wan_block_weights_t *w, bool fp8 = false) {
   if (!w) return WAN_ERR_NULL;
-  const void *req[] = {w->sa_wqkv, w->sa_bqkv, w->sa_wo, w->sa_bo, w->ca_wq, w->ca_bq, w->ca_wkv,
-                       w->ca_bkv, w->ca_wo, w->ca_bo, w->ffn_w1, w->ffn_b1, w->ffn_w2, w->ffn_b2,
-                       w->mod_bias};
+  const void *req[] = {w->sa_bqkv, w->sa_bo, w->ca_bq, w->ca_wkv, w->ca_bkv, w->ca_bo, w->ffn_b1,
+                       w->ffn_b2, w->mod_bias};
   for (const void *p : req)
     if (!p) return WAN_ERR_NULL;
+  if (!fp8 && (!w->sa_wqkv || !w->sa_wo || !w->ca_wq || !w->ca_wo || !w->ffn_w1 || !w->ffn_w2))
+    return WAN_ERR_NULL;
   if (c.img_len > 0 && (!w->ca_wkv_img || !w->ca_bkv_img)) return WAN_ERR_CONFIG;
   return WAN_OK;
 }
@@ -595,8 +668,66 @@ int wan_linear_fp8_fwd(const void *xq, const float *x_scale, const void *wq, con
   g.fp8 = 1;
   g.a_scale = x_scale;
   g.b_scale = w_scale;
+  g.a_per_row = 1;
   WAN_TRY(launch_gemm(g, S(stream)));
   return WAN_OK;
+}
+
+size_t wan_block_fp8_bytes(const wan_cfg_t *cfg) {
+  if (check_cfg(cfg) != WAN_OK || cfg->dtype != WAN_BF16) return 0;
+  return fp8_layout(*cfg).total;
+}
+
+int wan_quantize_block_fp8(const wan_cfg_t *cfg, const wan_block_weights_t *w, void *qbuf,
+                           size_t qbuf_bytes, void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (cfg->dtype != WAN_BF16) return WAN_ERR_DTYPE;
+  if (!w || !qbuf) return WAN_ERR_NULL;
+  const void *src[6] = {w->sa_wqkv, w->sa_wo, w->ca_wq, w->ca_wo, w->ffn_w1, w->ffn_w2};
+  for (const void *p : src)
+    if (!p) return WAN_ERR_NULL;
+  const Fp8Layout q = fp8_layout(*cfg);
+  if (qbuf_bytes < q.total) return WAN_ERR_WORKSPACE;
+  if ((uintptr_t)qbuf % ALIGN) return WAN_ERR_SHAPE;
+  char *b = (char *)qbuf;
+  for (int i = 0; i < 6; ++i)
+    WAN_TRY(launch_quant_tensor_fp8(src[i], q.n[i], b + q.w[i], (float *)(b + q.sc) + i,
+                                    (unsigned *)(b + q.amax) + i, S(stream)));
+  return WAN_OK;
+}
+
+size_t wan_block_fp8_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int Hp, int Wp) {
+  if (check_cfg(cfg) != WAN_OK || cfg->dtype != WAN_BF16) return 0;
+  if (check_dims(B, lat_f, Hp, Wp) != WAN_OK) return 0;
+  return make_layout(*cfg, B, (long)lat_f * Hp * Wp, false, true).total;
+}
+
+int wan_dit_block_fp8_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, int Wp,
+                          const float *mod, const wan_block_weights_t *w, const void *qbuf,
+                          const void *ctx, const void *img_ctx, void *ws, size_t ws_bytes,
+                          void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (cfg->dtype != WAN_BF16) return WAN_ERR_DTYPE;
+  if (!x || !mod || !ctx || !ws || !qbuf) return WAN_ERR_NULL;
+  if ((uintptr_t)qbuf % ALIGN) return WAN_ERR_SHAPE;
+  if ((st = check_dims(B, lat_f, Hp, Wp))) return st;
+  if ((st = check_block_weights(*cfg, w, true))) return st;
+  if ((cfg->img_len > 0) != (img_ctx != nullptr)) return WAN_ERR_CONFIG;
+  const long L = (long)lat_f * Hp * Wp;
+  // the FP8 GEMM addresses its operands with 32-bit byte offsets
+  if ((long)B * L * (cfg->ffn > cfg->dim ? cfg->ffn : cfg->dim) >= (1L << 31)) return WAN_ERR_SHAPE;
+  Layout y = make_layout(*cfg, B, L, false, true);
+  if (ws_bytes < y.total) return WAN_ERR_WORKSPACE;
+  const Fp8Layout ql = fp8_layout(*cfg);
+  const char *qb = (const char *)qbuf;
+  Fp8Ptrs q8;
+  for (int i = 0; i < 6; ++i) q8.w[i] = (const uint8_t *)(qb + ql.w[i]);
+  q8.sc = (const float *)(qb + ql.sc);
+  q8.aq = (uint8_t *)ws + y.aq;
+  q8.as = (float *)((char *)ws + y.as);
+  return block_run(*cfg, x, B, L, mod, *w, ctx, img_ctx, nullptr, (char *)ws, y, S(stream), &q8);
 }
 
 int wan_linear_fwd(const void *x, const void *w, const void *b, void *y, int M, int N, int K,
