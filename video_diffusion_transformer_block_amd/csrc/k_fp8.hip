@@ -1,43 +1,42 @@
-// FP8 quantisation for the FP8 GEMM ("Wan: Open and Advanced Large-Scale Video
-// Generative Models (Wan 2.1)", section Infra / 推理优化: FP8 GEMM with
-// per-tensor weight scales and per-token activation scales).
-//
-// Format: OCP E4M3 (v_cvt_pk_fp8_f32 on gfx950: round to nearest even, no
-// saturation -- inputs are clamped to +-448 first).  A scale maps the largest
-// magnitude to 448: inv = 448 / amax (correctly rounded float32 division),
-// code = E4M3(clamp(x * inv)), stored scale = amax / 448 (x ~= code * scale);
-// an all-zero row or tensor gets scale 1.
-#include "common.hpp"
+// Per-token and per-tensor FP8 (OCP E4M3) quantisation for the FP8 GEMM
+// ("Wan: Open and Advanced Large-Scale Video Generative Models (Wan 2.1)",
+// section Infra / 推理优化: FP8 GEMM with per-tensor weight scales and
+// per-token activation scales); format and scale rule in fp8.hpp.
+#include "fp8.hpp"
 #include "kernels.hpp"
 
 namespace wan {
 
-WAN_DEV float inv_scale(float amax) { return amax > 0.f ? 448.0f / amax : 1.0f; }
-WAN_DEV float deq_scale(float amax) { return amax > 0.f ? amax / 448.0f : 1.0f; }
-
-// two floats -> two E4M3 bytes (low byte first)
-WAN_DEV unsigned short pack2(float a, float b) {
-  a = fminf(fmaxf(a, -448.0f), 448.0f);
-  b = fminf(fmaxf(b, -448.0f), 448.0f);
-  return (unsigned short)(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFF);
-}
-
-// 8 bf16 -> 8 E4M3 bytes scaled by inv
-WAN_DEV uint2 quant8(const uint4 &u, float inv) {
-  const bf16 *e = reinterpret_cast<const bf16 *>(&u);
-  uint2 r;
-  r.x = pack2((float)e[0] * inv, (float)e[1] * inv) | ((unsigned)pack2((float)e[2] * inv, (float)e[3] * inv) << 16);
-  r.y = pack2((float)e[4] * inv, (float)e[5] * inv) | ((unsigned)pack2((float)e[6] * inv, (float)e[7] * inv) << 16);
-  return r;
-}
-
-WAN_DEV float amax8(const uint4 &u, float m) {
-  const bf16 *e = reinterpret_cast<const bf16 *>(&u);
+// one wavefront per row with the row held in registers (at most NC 16-byte
+// chunks per lane: K <= NC * 512): one read of the row, then the codes
+template <int NC>
+__global__ __launch_bounds__(256) void k_quant_rows_reg(const bf16 *__restrict__ x, int M, int K,
+                                                        long ldx, uint8_t *__restrict__ q, long ldq,
+                                                        float *__restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const bf16 *xr = x + row * ldx;
+  uint4 v[NC];
+  float m = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf((float)e[i]));
-  return m;
+  for (int i = 0; i < NC; ++i) {
+    const int c = (i * 64 + lane) * 8;
+    v[i] = c < K ? ld16(xr + c) : make_uint4(0, 0, 0, 0);
+    m = amax8(v[i], m);
+  }
+  m = wave_max(m);
+  const float inv = inv_scale(m);
+  uint8_t *qr = q + row * ldq;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = (i * 64 + lane) * 8;
+    if (c < K) *reinterpret_cast<uint2 *>(qr + c) = quant8(v[i], inv);
+  }
+  if (lane == 0) scale[row] = deq_scale(m);
 }
 
+// wider rows: two passes over the row (maximum, then codes)
 // one wavefront per row; K % 8 == 0, rows 16-byte aligned (ldx % 8 == 0, ldq % 8 == 0)
 __global__ __launch_bounds__(256) void k_quant_rows(const bf16 *__restrict__ x, int M, int K, long ldx,
                                                     uint8_t *__restrict__ q, long ldq,
@@ -59,7 +58,13 @@ __global__ __launch_bounds__(256) void k_quant_rows(const bf16 *__restrict__ x, 
 hipError_t launch_quant_rows_fp8(const void *x, int M, int K, long ldx, void *q, long ldq,
                                  float *scale, hipStream_t s) {
   if (M <= 0 || K <= 0) return hipSuccess;
-  k_quant_rows<<<(M + 3) / 4, 256, 0, s>>>((const bf16 *)x, M, K, ldx, (uint8_t *)q, ldq, scale);
+  const int grid = (M + 3) / 4;
+  const bf16 *xb = (const bf16 *)x;
+  uint8_t *qb = (uint8_t *)q;
+  if (K <= 4 * 512) k_quant_rows_reg<4><<<grid, 256, 0, s>>>(xb, M, K, ldx, qb, ldq, scale);
+  else if (K <= 8 * 512) k_quant_rows_reg<8><<<grid, 256, 0, s>>>(xb, M, K, ldx, qb, ldq, scale);
+  else if (K <= 18 * 512) k_quant_rows_reg<18><<<grid, 256, 0, s>>>(xb, M, K, ldx, qb, ldq, scale);
+  else k_quant_rows<<<grid, 256, 0, s>>>(xb, M, K, ldx, qb, ldq, scale);
   return hipGetLastError();
 }
 

@@ -48,6 +48,12 @@ hipError_t launch_mod_combine(const float *mod, const float *bias, float *out, i
 hipError_t launch_ln_mod(const float *x, int M, int L, int d, const float *modb, long modb_bstride,
                          int shift_off, int scale_off, int has_mod, float eps, void *out,
                          int out_f32, hipStream_t s);
+// LayerNorm (+ modulate) straight to E4M3 codes and per-row scales (widths
+// for which ln_mod_fp8_supported holds)
+hipError_t launch_ln_mod_fp8(const float *x, int M, int L, int d, const float *modb,
+                             long modb_bstride, int shift_off, int scale_off, int has_mod, float eps,
+                             void *q, float *scale, hipStream_t s);
+bool ln_mod_fp8_supported(int d);
 hipError_t launch_gemm(const GemmDesc &g, hipStream_t s);
 hipError_t launch_attention(const AttnDesc &a, hipStream_t s);
 hipError_t launch_tmlp(const float *t, int B, int freq_dim, int d, const void *w1, const void *b1,

@@ -248,15 +248,38 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
   char *kc = ws + y.kc, *vtc = ws + y.vtc, *ki = ws + y.ki, *vti = ws + y.vti, *u = ws + y.u;
   float *acc32 = reinterpret_cast<float *>(ws + y.acc32);
 
+  // LayerNorm (+ modulate) of x into h; with q8 into the E4M3 activation
+  // buffer instead (fused when the width allows)
+  auto ln = [&](int shift_off, int scale_off, int has_mod) -> hipError_t {
+    if (q8 && ln_mod_fp8_supported(d))
+      return launch_ln_mod_fp8(x, M, (int)L, d, modb, 6 * d, shift_off, scale_off, has_mod, c.eps,
+                               q8->aq, q8->as, s);
+    hipError_t e = launch_ln_mod(x, M, (int)L, d, modb, 6 * d, shift_off, scale_off, has_mod, c.eps,
+                                 h, f32, s);
+    if (e != hipSuccess || !q8) return e;
+    return launch_quant_rows_fp8(h, M, d, d, q8->aq, d, q8->as, s);
+  };
+  // y = act W^T + b with the residual / GELU / plain epilogue g; on E4M3
+  // operands with q8 (act quantised per token first unless `quantised`)
+  auto linear = [&](GemmDesc g, int wi, bool quantised) -> hipError_t {
+    if (!q8) return launch_gemm(g, s);
+    if (!quantised) {
+      hipError_t e = launch_quant_rows_fp8(g.A, M, g.K, g.lda, q8->aq, g.K, q8->as, s);
+      if (e != hipSuccess) return e;
+    }
+    g.A = q8->aq; g.lda = g.K;
+    g.B = q8->w[wi]; g.ldb = g.K;
+    return launch_gemm(fp8(g, q8->as, 1, q8->sc + wi, 0), s);
+  };
+
   WAN_TRY(launch_mod_combine(mod, w.mod_bias, modb, B, 6 * d, s));
   // ---- self-attention branch
-  WAN_TRY(launch_ln_mod(x, M, (int)L, d, modb, 6 * d, 0, d, 1, c.eps, h, f32, s));
+  WAN_TRY(ln(0, d, 1));
   if (f32) {
     WAN_TRY(launch_gemm(gemm(h, d, w.sa_wqkv, d, M, 3 * d, d, w.sa_bqkv, OUT_BF16, qk, 3 * d, 1), s));
     WAN_TRY(launch_attention(attn(qk, 3 * d, off(qk, d, es), 3 * d, off(qk, 2 * d, es), 3 * d, 0,
                                   o, d, B, H, (int)L, (int)L, hd, 1), s));
   } else if (q8) {
-    WAN_TRY(launch_quant_rows_fp8(h, M, d, d, q8->aq, d, q8->as, s));
     WAN_TRY(launch_gemm(fp8(gemm(q8->aq, d, q8->w[0], d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0),
                             q8->as, 1, q8->sc + 0, 0), s));
     for (int b = 0; b < B; ++b) {   // V^T = Wv h_b^T: weight scale per tensor, token scale per column
@@ -281,21 +304,12 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
     WAN_TRY(launch_attention(attn(qk, 2 * d, off(qk, d, es), 2 * d, vt, (long)B * y.Lp, y.Lp, o,
                                   d, B, H, (int)L, (int)L, hd, 0), s));
   }
-  // y = act W^T + b with the residual / GELU / plain epilogue g; on E4M3
-  // operands with q8 (act quantised per token first, K = g.K)
-  auto linear = [&](GemmDesc g, int wi) -> hipError_t {
-    if (!q8) return launch_gemm(g, s);
-    hipError_t e = launch_quant_rows_fp8(g.A, M, g.K, g.lda, q8->aq, g.K, q8->as, s);
-    if (e != hipSuccess) return e;
-    g.A = q8->aq; g.lda = g.K;
-    g.B = q8->w[wi]; g.ldb = g.K;
-    return launch_gemm(fp8(g, q8->as, 1, q8->sc + wi, 0), s);
-  };
-  WAN_TRY(linear(resid(o, d, w.sa_wo, M, d, d, w.sa_bo, x, modb + 2 * d, 6 * d, (int)L, f32), 1));
+  WAN_TRY(linear(resid(o, d, w.sa_wo, M, d, d, w.sa_bo, x, modb + 2 * d, 6 * d, (int)L, f32), 1,
+                 false));
 
   // ---- cross-attention branch (pre-LN without modulation, ungated)
-  WAN_TRY(launch_ln_mod(x, M, (int)L, d, modb, 6 * d, 0, 0, 0, c.eps, h, f32, s));
-  WAN_TRY(linear(gemm(h, d, w.ca_wq, d, M, d, d, w.ca_bq, OUT_BF16, qc, d, f32), 2));
+  WAN_TRY(ln(0, 0, 0));
+  WAN_TRY(linear(gemm(h, d, w.ca_wq, d, M, d, d, w.ca_bq, OUT_BF16, qc, d, f32), 2, true));
   int st;
   if (cached) {
     kc = (char *)cached->kc; vtc = (char *)cached->vtc; ki = (char *)cached->ki; vti = (char *)cached->vti;
@@ -322,12 +336,13 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
   } else {
     WAN_TRY(launch_attention(at, s));
   }
-  WAN_TRY(linear(resid(o, d, w.ca_wo, M, d, d, w.ca_bo, x, nullptr, 0, (int)L, f32), 3));
+  WAN_TRY(linear(resid(o, d, w.ca_wo, M, d, d, w.ca_bo, x, nullptr, 0, (int)L, f32), 3, false));
 
   // ---- FFN branch
-  WAN_TRY(launch_ln_mod(x, M, (int)L, d, modb, 6 * d, 3 * d, 4 * d, 1, c.eps, h, f32, s));
-  WAN_TRY(linear(gemm(h, d, w.ffn_w1, d, M, F, d, w.ffn_b1, OUT_GELU, u, F, f32), 4));
-  WAN_TRY(linear(resid(u, F, w.ffn_w2, M, d, F, w.ffn_b2, x, modb + 5 * d, 6 * d, (int)L, f32), 5));
+  WAN_TRY(ln(3 * d, 4 * d, 1));
+  WAN_TRY(linear(gemm(h, d, w.ffn_w1, d, M, F, d, w.ffn_b1, OUT_GELU, u, F, f32), 4, true));
+  WAN_TRY(linear(resid(u, F, w.ffn_w2, M, d, F, w.ffn_b2, x, modb + 5 * d, 6 * d, (int)L, f32), 5,
+                 false));
   return WAN_OK;
 }
 
