@@ -35,7 +35,7 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 # KiB per dispatch), each scaled by what the counter reads for a plain 512 MiB
 # copy (fetch x2.00, write x1.00); see profiles/k_attn_bf16_wan1.3b_block_480p.md.
 # Valid only for the kernel sources they were taken on: reported as null
-# once k_attn.hip, common.hpp or kernels.hpp change.
+# once k_attn.hip, common.hpp or attn.hpp change.
 ATTN_TRAFFIC = {
     "sources_sha256": "3133670ae87636397581fe73a772644188c3f2bc49f576991970bc7fd145cebc",
     "fetch_kib": 442440, "write_kib": 100681, "fetch_scale": 2.00, "write_scale": 1.00,
@@ -46,7 +46,7 @@ def attn_sources_sha256() -> str:
     import hashlib
     csrc = os.path.join(ROOT, "video_diffusion_transformer_block_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("k_attn.hip", "common.hpp", "kernels.hpp"):
+    for f in ("k_attn.hip", "common.hpp", "attn.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

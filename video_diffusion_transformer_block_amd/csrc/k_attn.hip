@@ -20,13 +20,20 @@
 //  * K and V^T tiles of 64 keys go global -> LDS directly (buffer_load ...
 //    lds), double-buffered, with XOR swizzles that keep every 16-lane group of
 //    a 16-byte read on distinct banks; K runs one tile ahead of V;
-//  * the running max is only raised (and the accumulators rescaled) when a
-//    tile's max exceeds it by more than 2^8, so most tiles skip the rescale;
-//    probabilities stay <= 256.
+//  * Q arrives pre-scaled by log2(e)/sqrt(hd) (the block's Q projections
+//    write it so; for other callers the fragments are scaled on load), and
+//    the score MFMAs start from an accumulator holding -m (m the running max
+//    in log2 units), so a score register already holds s - m and a
+//    probability is one v_exp_f32 of it;
+//  * no row max in the steady state: the max is taken once, from the first
+//    tile, and raised only when a tile's probabilities overflow 2^16 (seen in
+//    the per-lane row sum); then that tile's max is taken, the accumulators
+//    are rescaled and the tile's probabilities recomputed.  Probabilities
+//    thus stay below 2^16 and the running sum below 2^31.
 #include <type_traits>
 
+#include "attn.hpp"
 #include "common.hpp"
-#include "kernels.hpp"
 
 namespace wan {
 
@@ -36,7 +43,7 @@ namespace wan {
 constexpr int AQ = 256;   // queries per workgroup
 constexpr int AK = 64;    // keys per tile
 constexpr int HD = 128;   // head dim
-constexpr float TAU = 8.0f;
+constexpr float PMAX = 65536.0f;   // 2^16: probabilities above it raise the running max
 
 WAN_DEV float other_half(float v) { return __shfl_xor(v, 32); }
 
@@ -95,6 +102,10 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
 
   // ---- Q fragments (B operand of S^T = K Q^T): for query block qb the lane
   // holds Q[q][st*16 + g*8 .. +8] of query q = qrow[qb]
+  // times c = scale * log2 e, so that scores come out in log2 units: done by
+  // the producer when q_scaled (one rounding), else here (a second bf16
+  // rounding of q)
+  const float c = a.scale * 1.4426950408889634f;
   int qrow[QB];
   bf16x8 qf[QB][8];
 #pragma unroll
@@ -105,7 +116,12 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       uint4 v = ok ? ld16(qp + st * 16) : make_uint4(0, 0, 0, 0);
-      qf[qb][st] = *reinterpret_cast<bf16x8 *>(&v);
+      bf16x8 f = *reinterpret_cast<bf16x8 *>(&v);
+      if (!a.q_scaled) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = f2bf(bf2f(f[e]) * c);
+      }
+      qf[qb][st] = f;
     }
   }
 
@@ -116,10 +132,15 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[t][qb][r] = 0.f;
-  float m[QB], l[QB];
+  // nm[qb]: -m in all 16 entries (the score MFMAs' initial accumulator)
+  f32x16 nm[QB];
+  float l[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
-  const float c = a.scale * 1.4426950408889634f;   // scores -> log2 units
+  for (int qb = 0; qb < QB; ++qb) {
+    l[qb] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nm[qb][r] = 0.f;
+  }
 
   // ---- tile loaders: K tile = 64 keys x 16 chunks; V^T tile = 128 rows x 8 chunks
   const long vbase = (long)b * a.vt_bstride;
@@ -178,21 +199,18 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
 
   const int ntiles = (Lk + AK - 1) / AK;
 
-  // S^T of a tile (two 32-key blocks x QB query blocks); each K fragment
-  // feeds the QB query blocks
+  // S^T - m of a tile (two 32-key blocks x QB query blocks); each K
+  // fragment feeds the QB query blocks
   auto qk = [&](const bf16 *sk, f32x16 (&s)[2][QB]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sk + kb * 32 * HD + koff[st]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][st], s[kb][qb], 0, 0, 0);
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][st], st ? s[kb][qb] : nm[qb],
+                                                              0, 0, 0);
       }
     }
   };
@@ -222,34 +240,15 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
       mx[qb] = fmaxf(v, other_half(v));
     }
   };
-  // raise the running max only when the tile's max exceeds it by more than 2^TAU
-  auto rescale = [&](const float (&mx)[QB]) {
-    bool up = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) up |= mx[qb] * c > m[qb] + TAU;
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float mn = fmaxf(m[qb], mx[qb] * c);
-        const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
-        l[qb] *= alpha;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[t][qb][r] *= alpha;
-        m[qb] = mn;
-      }
-    }
-  };
-  // probabilities of a tile, bf16 in the B-operand layout, and their row sums
-  // (a row sum adds the bf16-rounded probabilities, two per v_dot2 with
-  //  (1, 1): the normaliser then matches exactly the weights the PV MFMA uses)
-  auto probs = [&](const f32x16 (&s)[2][QB], bf16x8 (&pb)[QB][2][2]) {
+  // probabilities of a tile, exp2 of the centred scores, bf16 in the
+  // B-operand layout, and this lane's part of their row sums (a row sum adds
+  // the bf16-rounded probabilities, two per v_dot2 with (1, 1): the
+  // normaliser then matches exactly the weights the PV MFMA uses)
+  auto probs = [&](const f32x16 (&s)[2][QB], bf16x8 (&pb)[QB][2][2], float (&ls)[QB]) {
     bf16x2 one;
     one[0] = (bf16)1.0f; one[1] = (bf16)1.0f;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float nm = -m[qb];
       float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -257,15 +256,51 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            pb[qb][kb][hf][e] = f2bf(__builtin_amdgcn_exp2f(fmaf(s[kb][qb][hf * 8 + e], c, nm)));
+            pb[qb][kb][hf][e] = f2bf(__builtin_amdgcn_exp2f(s[kb][qb][hf * 8 + e]));
           const bf16x2 *pp = reinterpret_cast<const bf16x2 *>(&pb[qb][kb][hf]);
           ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[0], one, ls0, false);
           ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[1], one, ls1, false);
           ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[2], one, ls0, false);
           ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[3], one, ls1, false);
         }
-      l[qb] += ls0 + ls1;
+      ls[qb] = ls0 + ls1;
     }
+  };
+  // lower every centred score of s by dm (per query block)
+  auto shift = [&](f32x16 (&s)[2][QB], const float (&dm)[QB]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][qb][r] -= dm[qb];
+  };
+  // a probability of this tile passed PMAX (or is not finite): raise the
+  // running max to the tile's max, rescale the accumulators, recompute the
+  // tile's probabilities; snxt (already scored against the old max) follows
+  auto overflow = [&](f32x16 (&scur)[2][QB], f32x16 (&snxt)[2][QB], bool has_next,
+                      bf16x8 (&pb)[QB][2][2], float (&ls)[QB]) {
+    bool big = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) big |= !(ls[qb] <= PMAX);
+    if (__builtin_amdgcn_ballot_w64(big) == 0) return;
+    float mx[QB], dm[QB];
+    rowmax(scur, mx);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      dm[qb] = fmaxf(mx[qb], 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-dm[qb]);
+      l[qb] *= alpha;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][qb][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) nm[qb][r] -= dm[qb];
+    }
+    shift(scur, dm);
+    if (has_next) shift(snxt, dm);
+    probs(scur, pb, ls);
   };
   // O^T += V^T P^T; each V^T fragment feeds the QB query blocks
   auto pv = [&](const bf16 *sv, const bf16x8 (&pb)[QB][2][2]) {
@@ -283,12 +318,12 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
   };
 
   // Pipeline: K runs one tile ahead of V.  At the top of iteration j the LDS
-  // holds K(j+1) in stage (j+1)&1 and V(j) in stage j&1; S(j) and its row max
-  // are in registers.  Iteration j: K(j+2) starts loading into the stage
-  // freed in iteration j-1; (rare) rescale; the S(j+1) MFMAs interleaved with
-  // the exponentials of tile j; V(j+1) starts loading into its freed stage;
-  // the PV(j) MFMAs interleaved with the row max of S(j+1); wait for the
-  // loads; one barrier.
+  // holds K(j+1) in stage (j+1)&1 and V(j) in stage j&1; the centred scores
+  // S(j) are in registers.  Iteration j: K(j+2) starts loading into the stage
+  // freed in iteration j-1; the S(j+1) MFMAs interleaved with the
+  // exponentials of tile j; (rare) overflow: raise the max; V(j+1) starts
+  // loading into its freed stage; the PV(j) MFMAs; wait for the loads; one
+  // barrier.
   constexpr std::integral_constant<int, 0> P0{};
   constexpr std::integral_constant<int, 1> P1{};
   gloadK(0, P0);
@@ -297,10 +332,17 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(0), K(1), V(0) landed
   __syncthreads();
   f32x16 sa[2][QB], sb[2][QB];
-  float mxa[QB];
-  qk(sK0, sa);
-  mask_tail(sa, 0);
-  rowmax(sa, mxa);
+  {   // the first tile sets the running max exactly
+    float mx[QB];
+    qk(sK0, sa);
+    mask_tail(sa, 0);
+    rowmax(sa, mx);
+    shift(sa, mx);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) nm[qb][r] = -mx[qb];
+  }
   __syncthreads();   // every wavefront has read K(0): its buffer may be refilled
 
   // MFMAs per section, and the LDS reads / VALU instructions laid between them
@@ -309,15 +351,15 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
   // (load_k2: tile j+2 exists; mask_next: tile j+1 is the last, possibly
   // ragged, tile; both are constants in the steady-state loop, so no branch
   // stays there.)
-  auto step = [&](auto P, int j, f32x16 (&scur)[2][QB], float (&mx)[QB], f32x16 (&snxt)[2][QB],
-                  bool load_k2, bool mask_next) {
+  auto step = [&](auto P, int j, f32x16 (&scur)[2][QB], f32x16 (&snxt)[2][QB], bool load_k2,
+                  bool mask_next) {
     const auto Q = other(P);
-    rescale(mx);
     if (load_k2) gloadK(j + 2, P);   // buffer of K(j), read in iteration j-1
     bf16x8 pb[QB][2][2];
+    float ls[QB];
     // matrix unit: next scores; vector unit: this tile's probabilities
     qk(kbuf(Q), snxt);
-    probs(scur, pb);
+    probs(scur, pb, ls);
     // LDS reads run ahead of their use; VALU fills the MFMA shadow
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -325,51 +367,52 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
       if (q % QB == 0 && q < NMF - 4 * QB)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
     }
     if (mask_next) mask_tail(snxt, j + 1);
+    overflow(scur, snxt, true, pb, ls);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l[qb] += ls[qb];
     // the V load is issued after the score MFMAs, so that the wavefronts
     // leaving the barrier together do not queue all their tile loads at once
     __builtin_amdgcn_sched_barrier(0);
     gloadV(j + 1, Q);                // buffer of V(j-1), read in iteration j-1
-    // matrix unit: PV of this tile; vector unit: row max of the next scores
+    // matrix unit: PV of this tile
     pv(vbuf(P), pb);
-    rowmax(snxt, mx);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int q = 0; q < NMF; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (q % QB == 0 && q < NMF - 4 * QB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(j+2), V(j+1) landed, LDS reads done
     __syncthreads();
   };
   // the last tile: no next scores
-  auto last = [&](auto P, f32x16 (&scur)[2][QB], const float (&mx)[QB]) {
-    rescale(mx);
+  auto last = [&](auto P, f32x16 (&scur)[2][QB]) {
     bf16x8 pb[QB][2][2];
-    probs(scur, pb);
+    float ls[QB];
+    probs(scur, pb, ls);
+    overflow(scur, scur, false, pb, ls);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l[qb] += ls[qb];
     pv(vbuf(P), pb);
   };
   int j = 0;
-  float mx[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) mx[qb] = mxa[qb];
   for (; j + 3 < ntiles; j += 2) {     // unrolled by two (score buffers and stages alternate);
-    step(P0, j, sa, mx, sb, true, false);        // never computes the last tile's scores
-    step(P1, j + 1, sb, mx, sa, true, false);
+    step(P0, j, sa, sb, true, false);            // never computes the last tile's scores
+    step(P1, j + 1, sb, sa, true, false);
   }
   // the last 1 .. 3 tiles, one at a time with run-time stages; the current
   // scores are in sa
   for (; j + 1 < ntiles; ++j) {
-    step(j & 1, j, sa, mx, sb, j + 2 < ntiles, j + 2 == ntiles);
+    step(j & 1, j, sa, sb, j + 2 < ntiles, j + 2 == ntiles);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sa[kb][qb] = sb[kb][qb];
   }
-  last(j & 1, sa, mx);
+  last(j & 1, sa);
 
   // ---- normalise and store: lane holds O^T[hd = t*32 + (r/4)*8 + g*4 + r%4][q = qrow[qb]]
 #pragma unroll

@@ -91,6 +91,10 @@ WAN_DEV void epi8(const GemmDesc &g, int m, int n, float *v) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = gelu_tanh(v[i]);
   }
+  if (KIND == OUT_BF16 && n < g.scale_cols) {   // scale_cols % 8 == 0: whole chunks
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= g.col_scale;
+  }
   if (KIND == OUT_BF16 || KIND == OUT_GELU) {
     bf16 *c = reinterpret_cast<bf16 *>(g.C) + (long)m * g.ldc + n;
     if (full) {

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "attn.hpp"
+
 namespace wan {
 
 enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_GELU = 2, OUT_RESID = 3 };
@@ -28,20 +30,12 @@ struct GemmDesc {
   int fp8;
   const float *a_scale, *b_scale;
   int a_per_row, b_per_col;
+  // OUT_BF16: columns 0 .. scale_cols-1 (a multiple of 8) are multiplied by
+  // col_scale after the bias, before the rounding (attention's pre-scaled Q)
+  int scale_cols;
+  float col_scale;
 };
 
-// Attention O = softmax(Q K^T * scale) V for every (batch, head); hd = 128, bf16.
-struct AttnDesc {
-  const void *q; long ldq;     // [B*Lq, ldq], head h at column h*hd
-  const void *k; long ldk;     // [B*Lk, ldk]
-  const void *vt; long ldv; long vt_bstride;  // [H*hd, ldv], batch b at column b*vt_bstride
-  void *o; long ldo;           // [B*Lq, ldo]
-  int B, H, Lq, Lk, hd;
-  float scale;                 // 1/sqrt(hd)
-  int out_mode;                // 0: o = O (bf16); 1: acc32 = O; 2: o = acc32 + O
-  float *acc32;                // [B*Lq, H*hd] float32 partial (modes 1, 2)
-  int f32;                     // float32 path (generic kernel): v given untransposed in `vt`
-};
 
 hipError_t launch_mod_combine(const float *mod, const float *bias, float *out, int B, int n,
                               hipStream_t s);
@@ -55,7 +49,6 @@ hipError_t launch_ln_mod_fp8(const float *x, int M, int L, int d, const float *m
                              void *q, float *scale, hipStream_t s);
 bool ln_mod_fp8_supported(int d);
 hipError_t launch_gemm(const GemmDesc &g, hipStream_t s);
-hipError_t launch_attention(const AttnDesc &a, hipStream_t s);
 hipError_t launch_tmlp(const float *t, int B, int freq_dim, int d, const void *w1, const void *b1,
                        const void *w2, const void *b2, float *hidden, float *mod, int f32,
                        hipStream_t s);

@@ -213,6 +213,14 @@ int kv_project(const wan_cfg_t &c, int B, int Lk, const void *src, const void *w
   return WAN_OK;
 }
 
+// the output's first `cols` columns times log2(e)/sqrt(hd): a query the bf16
+// attention kernel reads pre-scaled (AttnDesc::q_scaled)
+GemmDesc qscaled(GemmDesc g, int cols, int hd) {
+  g.scale_cols = cols;
+  g.col_scale = 1.4426950408889634f / sqrtf((float)hd);
+  return g;
+}
+
 // the same GEMM on E4M3 operands: acc * a_scale[m or 0] * b_scale[n or 0]
 GemmDesc fp8(GemmDesc g, const float *as, int a_per_row, const float *bs, int b_per_col) {
   g.fp8 = 1;
@@ -222,12 +230,13 @@ GemmDesc fp8(GemmDesc g, const float *as, int a_per_row, const float *bs, int b_
 }
 
 AttnDesc attn(const void *q, long ldq, const void *k, long ldk, const void *v, long ldv,
-              long vbs, void *o, long ldo, int B, int H, int Lq, int Lk, int hd, int f32) {
+              long vbs, void *o, long ldo, int B, int H, int Lq, int Lk, int hd, int f32,
+              int q_scaled = 0) {
   AttnDesc a;
   memset(&a, 0, sizeof(a));
   a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.vt = v; a.ldv = ldv; a.vt_bstride = vbs;
   a.o = o; a.ldo = ldo; a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk; a.hd = hd;
-  a.scale = 1.0f / sqrtf((float)hd); a.f32 = f32;
+  a.scale = 1.0f / sqrtf((float)hd); a.f32 = f32; a.q_scaled = q_scaled;
   return a;
 }
 
@@ -280,7 +289,8 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
     WAN_TRY(launch_attention(attn(qk, 3 * d, off(qk, d, es), 3 * d, off(qk, 2 * d, es), 3 * d, 0,
                                   o, d, B, H, (int)L, (int)L, hd, 1), s));
   } else if (q8) {
-    WAN_TRY(launch_gemm(fp8(gemm(q8->aq, d, q8->w[0], d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0),
+    WAN_TRY(launch_gemm(fp8(qscaled(gemm(q8->aq, d, q8->w[0], d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk,
+                                         2 * d, 0), d, hd),
                             q8->as, 1, q8->sc + 0, 0), s));
     for (int b = 0; b < B; ++b) {   // V^T = Wv h_b^T: weight scale per tensor, token scale per column
       GemmDesc g = gemm(q8->w[0] + 2L * d * d, d, q8->aq + (long)b * L * d, d, d, (int)L, d,
@@ -290,9 +300,10 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
       WAN_TRY(launch_gemm(fp8(g, q8->sc + 0, 0, q8->as + (long)b * L, 1), s));
     }
     WAN_TRY(launch_attention(attn(qk, 2 * d, off(qk, d, es), 2 * d, vt, (long)B * y.Lp, y.Lp, o,
-                                  d, B, H, (int)L, (int)L, hd, 0), s));
+                                  d, B, H, (int)L, (int)L, hd, 0, 1), s));
   } else {
-    WAN_TRY(launch_gemm(gemm(h, d, w.sa_wqkv, d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0), s));
+    WAN_TRY(launch_gemm(qscaled(gemm(h, d, w.sa_wqkv, d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0),
+                                d, hd), s));
     for (int b = 0; b < B; ++b) {
       GemmDesc g = gemm(off(w.sa_wqkv, 2L * d * d, es), d, off(h, (long)b * L * d, es), d, d,
                         (int)L, d, off(w.sa_bqkv, 2 * d, es), OUT_BF16, vt + b * y.Lp * es,
@@ -302,14 +313,15 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
       WAN_TRY(launch_gemm(g, s));
     }
     WAN_TRY(launch_attention(attn(qk, 2 * d, off(qk, d, es), 2 * d, vt, (long)B * y.Lp, y.Lp, o,
-                                  d, B, H, (int)L, (int)L, hd, 0), s));
+                                  d, B, H, (int)L, (int)L, hd, 0, 1), s));
   }
   WAN_TRY(linear(resid(o, d, w.sa_wo, M, d, d, w.sa_bo, x, modb + 2 * d, 6 * d, (int)L, f32), 1,
                  false));
 
   // ---- cross-attention branch (pre-LN without modulation, ungated)
   WAN_TRY(ln(0, 0, 0));
-  WAN_TRY(linear(gemm(h, d, w.ca_wq, d, M, d, d, w.ca_bq, OUT_BF16, qc, d, f32), 2, true));
+  GemmDesc gq = gemm(h, d, w.ca_wq, d, M, d, d, w.ca_bq, OUT_BF16, qc, d, f32);
+  WAN_TRY(linear(f32 ? gq : qscaled(gq, d, hd), 2, true));
   int st;
   if (cached) {
     kc = (char *)cached->kc; vtc = (char *)cached->vtc; ki = (char *)cached->ki; vti = (char *)cached->vti;
@@ -319,7 +331,7 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
   }
   const long kld = f32 ? 2 * d : d;
   AttnDesc at = f32 ? attn(qc, d, kc, kld, off(kc, d, es), kld, 0, o, d, B, H, (int)L, Lc, hd, 1)
-                    : attn(qc, d, kc, kld, vtc, (long)B * y.Lcp, y.Lcp, o, d, B, H, (int)L, Lc, hd, 0);
+                    : attn(qc, d, kc, kld, vtc, (long)B * y.Lcp, y.Lcp, o, d, B, H, (int)L, Lc, hd, 0, 1);
   if (Li > 0) {
     if (!cached) {
       st = kv_project(c, B, Li, img, w.ca_wkv_img, w.ca_bkv_img, ki, vti, y.Lip, s);
@@ -329,7 +341,7 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
     at.acc32 = acc32;
     WAN_TRY(launch_attention(at, s));
     AttnDesc ai = f32 ? attn(qc, d, ki, kld, off(ki, d, es), kld, 0, o, d, B, H, (int)L, Li, hd, 1)
-                      : attn(qc, d, ki, kld, vti, (long)B * y.Lip, y.Lip, o, d, B, H, (int)L, Li, hd, 0);
+                      : attn(qc, d, ki, kld, vti, (long)B * y.Lip, y.Lip, o, d, B, H, (int)L, Li, hd, 0, 1);
     ai.out_mode = 2;
     ai.acc32 = acc32;
     WAN_TRY(launch_attention(ai, s));
