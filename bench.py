@@ -37,8 +37,8 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 # Valid only for the kernel sources they were taken on: reported as null
 # once k_attn.hip, common.hpp or attn.hpp change.
 ATTN_TRAFFIC = {
-    "sources_sha256": "3133670ae87636397581fe73a772644188c3f2bc49f576991970bc7fd145cebc",
-    "fetch_kib": 442440, "write_kib": 100681, "fetch_scale": 2.00, "write_scale": 1.00,
+    "sources_sha256": "41200679e3d869ce255ae56ea7b4527fe28b63cfe2a7378d1837d0edd793f234",
+    "fetch_kib": 442445, "write_kib": 100813, "fetch_scale": 2.00, "write_scale": 1.00,
 }
 
 
@@ -117,7 +117,7 @@ def traffic_pass(W, B, L, d, H, dev):
     src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
-        W.attention_fwd(qk, 2 * d, qk[:, d:], 2 * d, vt, B * Lp, Lp, o, d, B, H, L, L)
+        W.attention_fwd(qk, 2 * d, qk[:, d:], 2 * d, vt, B * Lp, Lp, o, d, B, H, L, L, q_scaled=True)
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"traffic_pass": "done", "copy_bytes": 512 << 20}), flush=True)
@@ -403,7 +403,9 @@ def main():
     o = torch.empty((B * L, d), dtype=torch.bfloat16, device=dev)
 
     def attn():
-        W.attention_fwd(qk, 2 * d, qk[:, d:], 2 * d, vt, B * Lp, Lp, o, d, B, H, L, L, stream)
+        # queries pre-scaled by log2(e)/sqrt(hd), as the block's Q projection writes them
+        W.attention_fwd(qk, 2 * d, qk[:, d:], 2 * d, vt, B * Lp, Lp, o, d, B, H, L, L, stream,
+                        q_scaled=True)
 
     for _ in range(2):
         attn()

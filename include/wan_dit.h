@@ -222,7 +222,10 @@ int wan_sample_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, int H8
 
 /* Multi-head attention O = softmax(Q K^T / sqrt(hd)) V per (batch, head)
  * ([Note] Diffusion Transformer).  bf16 only, hd = 128, device pointers:
- *   q  [B, Lq, *] row stride ldq elements, head h at column h*128
+ *   q  [B, Lq, *] row stride ldq elements, head h at column h*128; with
+ *      q_scaled = 1 the caller has multiplied q by log2(e)/sqrt(128) (as the
+ *      block's query projections do), and the result is the same attention
+ *      of q / (log2(e)/sqrt(128)); q_scaled = 0 for a plain q
  *   k  [B, Lk, *] row stride ldk, head h at column h*128
  *   vt [H*128, *] row stride ldv: V transposed; batch b's key j sits at
  *      column b*vt_bstride + j.  ldv and vt_bstride are multiples of 8,
@@ -233,7 +236,7 @@ int wan_sample_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, int H8
  *   o  [B, Lq, H*128] bf16, row stride ldo.
  * No mask.  Returns WAN_ERR_SHAPE for unsupported strides or sizes. */
 int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv, int vt_bstride,
-                      void *o, int ldo, int B, int H, int Lq, int Lk, void *stream);
+                      void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled, void *stream);
 
 /* y = x W^T + b for a bf16 x [M, K], W [N, K], b [N] (device), K % 64 == 0.
  * mode 0: y bf16 [M, N];  mode 1: y float32 [M, N];  mode 2: y bf16 = GELU_tanh(.) */

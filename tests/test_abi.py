@@ -101,7 +101,7 @@ def test_invalid_arguments_enqueue_nothing(W):
                               None) == -1
     assert L.wan_dit_step_cached_fwd(C.byref(c), dummy, dummy, 2, 3, 7, 12, dummy, 1 << 30,
                                      C.byref(mw), dummy, dummy, 1 << 40, None) == -2   # odd H8
-    assert L.wan_attention_fwd(dummy, 100, dummy, 256, dummy, 64, 64, dummy, 256, 1, 2, 4, 4,
+    assert L.wan_attention_fwd(dummy, 100, dummy, 256, dummy, 64, 64, dummy, 256, 1, 2, 4, 4, 0,
                                None) == -2                                          # ldq < H*128
     assert L.wan_linear_fwd(dummy, dummy, None, dummy, 4, 4, 100, 0, None) == -2   # K % 64
 

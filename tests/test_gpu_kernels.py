@@ -10,7 +10,10 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def _attn_gpu(q, k, v, H):
+C_LOG2 = np.log2(np.e) / np.sqrt(128.0)   # the pre-scaled query's factor
+
+
+def _attn_gpu(q, k, v, H, q_scaled=False):
     import video_diffusion_transformer_block_amd as W
     from tests.gpu_util import DEV
     B, Lq, D = q.shape
@@ -23,7 +26,7 @@ def _attn_gpu(q, k, v, H):
     tk = torch.from_numpy(k.reshape(B * Lk, D)).to(torch.bfloat16).to(DEV)
     tv = torch.from_numpy(vt).to(torch.bfloat16).to(DEV)
     to = torch.empty((B * Lq, D), dtype=torch.bfloat16, device=DEV)
-    W.attention_fwd(tq, D, tk, D, tv, B * Lkp, Lkp, to, D, B, H, Lq, Lk)
+    W.attention_fwd(tq, D, tk, D, tv, B * Lkp, Lkp, to, D, B, H, Lq, Lk, q_scaled=q_scaled)
     torch.cuda.synchronize()
     return to.float().cpu().numpy().reshape(B, Lq, D)
 
@@ -56,6 +59,48 @@ def test_attention_rows_sum_to_one():
     q, k, v = synth.attention_inputs(2, 1, 2, 300, 500, qk_std=3.0)
     g = _attn_gpu(q, k, np.ones_like(v), 2)
     assert np.max(np.abs(g - 1.0)) <= 4e-3
+
+
+# a block of keys whose logits jump far above everything before it, so that
+# the running max must be raised mid-stream (the kernel takes the first
+# tile's max and raises it only when a probability passes 2^16): in the 2nd
+# tile, in the steady-state loop, in the last ragged tile, and in the first
+# tile (later tiles then sit far below the max)
+OUTLIER_CASES = [  # Lq, Lk, first outlier key, last outlier key + 1
+    (200, 150, 64, 100), (300, 600, 300, 340), (130, 600, 580, 600), (100, 500, 0, 20),
+]
+
+
+@pytest.mark.parametrize("q_scaled", [False, True])
+@pytest.mark.parametrize("Lq,Lk,k0,k1", OUTLIER_CASES)
+def test_attention_raises_running_max(Lq, Lk, k0, k1, q_scaled):
+    print(f"attention outlier keys {k0}..{k1} of {Lk}, Lq={Lq}, q_scaled={q_scaled}", flush=True)
+    from tests.gpu_util import assert_parity
+    q, k, v = synth.attention_inputs(3, 1, 2, Lq, Lk)
+    k[:, k0:k1] *= 4.0     # logits x4 (std 16): far past 2^16 in probability
+    if q_scaled:           # the kernel reads q' = bf16(q c); the exact answer is that of q' / c
+        q = synth.bf16_round(q * np.float32(C_LOG2))
+        qo = q.astype(np.float64) / C_LOG2
+    else:
+        qo = q
+    g = _attn_gpu(q, k, v, 2, q_scaled)
+    o = _attn_oracle(qo, k, v, 2)
+    assert_parity(g, o, 3e-2, 1e-2, f"attention outliers {k0}..{k1}")
+    g1 = _attn_gpu(q, k, np.ones_like(v), 2, q_scaled)
+    assert np.max(np.abs(g1 - 1.0)) <= 4e-3
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk", [(2, 2, 300, 100), (1, 1, 1000, 1000), (1, 2, 100, 250)])
+def test_attention_prescaled_query(B, H, Lq, Lk):
+    """q_scaled = 1: the query holds q log2(e)/sqrt(128), as the block's
+    query projections write it."""
+    print(f"attention pre-scaled q B={B} H={H} Lq={Lq} Lk={Lk}", flush=True)
+    from tests.gpu_util import assert_parity
+    q, k, v = synth.attention_inputs(4, B, H, Lq, Lk)
+    qs = synth.bf16_round(q * np.float32(C_LOG2))
+    g = _attn_gpu(qs, k, v, H, True)
+    o = _attn_oracle(qs.astype(np.float64) / C_LOG2, k, v, H)
+    assert_parity(g, o, 3e-2, 1e-2, f"attention pre-scaled {B},{H},{Lq},{Lk}")
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (300, 256, 192), (513, 320, 64), (257, 512, 1280)])

@@ -82,7 +82,7 @@ def lib() -> C.CDLL:
         L.wan_dit_step_fwd.argtypes = [C.POINTER(Cfg), vp, vp, i, i, i, i, vp, vp, C.POINTER(ModelW),
                                        vp, vp, sz, vp]
         L.wan_i2v_mask.argtypes = [vp, i, i, i, i, vp]
-        L.wan_attention_fwd.argtypes = [vp, i, vp, i, vp, i, i, vp, i, i, i, i, i, vp]
+        L.wan_attention_fwd.argtypes = [vp, i, vp, i, vp, i, i, vp, i, i, i, i, i, i, vp]
         L.wan_linear_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
         L.wan_kv_cache_bytes.argtypes = [C.POINTER(Cfg), i]
         L.wan_kv_cache_bytes.restype = sz
@@ -188,10 +188,11 @@ def dit_step_fwd(cfg: Cfg, latent: torch.Tensor, t: torch.Tensor, ctx: torch.Ten
                                   _stream(stream)))
 
 
-def attention_fwd(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk, stream=None):
+def attention_fwd(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk, stream=None,
+                  q_scaled=False):
     _check("wan_attention_fwd",
            lib().wan_attention_fwd(_p(q), ldq, _p(k), ldk, _p(vt), ldv, vt_bstride, _p(o), ldo,
-                                   B, H, Lq, Lk, _stream(stream)))
+                                   B, H, Lq, Lk, int(bool(q_scaled)), _stream(stream)))
 
 
 def linear_fwd(x, w, b, y, M, N, K, mode, stream=None):

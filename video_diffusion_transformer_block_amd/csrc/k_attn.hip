@@ -20,11 +20,11 @@
 //  * K and V^T tiles of 64 keys go global -> LDS directly (buffer_load ...
 //    lds), double-buffered, with XOR swizzles that keep every 16-lane group of
 //    a 16-byte read on distinct banks; K runs one tile ahead of V;
-//  * Q arrives pre-scaled by log2(e)/sqrt(hd) (the block's Q projections
-//    write it so; for other callers the fragments are scaled on load), and
-//    the score MFMAs start from an accumulator holding -m (m the running max
-//    in log2 units), so a score register already holds s - m and a
-//    probability is one v_exp_f32 of it;
+//  * the score MFMAs start from an accumulator holding -m (m the running
+//    max), so a score register already holds s - m.  The block's Q
+//    projections write Q times log2(e)/sqrt(hd) (one rounding, in their
+//    epilogue): a probability is then one v_exp_f32 of the register; for a
+//    plain Q it is one multiply and one v_exp_f32;
 //  * no row max in the steady state: the max is taken once, from the first
 //    tile, and raised only when a tile's probabilities overflow 2^16 (seen in
 //    the per-lane row sum); then that tile's max is taken, the accumulators
@@ -61,6 +61,9 @@ WAN_DEV int vswz(int row) { return (row >> 1) & 7; }   // 16-byte chunk XOR for 
 // SIMD to itself (512 registers; the accumulators of O fit in AGPRs).
 constexpr int QB = WAN_ATTN_QB;
 static_assert(QB == 1 || QB == 2, "one or two 32-query blocks per wavefront");
+// QS: q arrives multiplied by scale * log2(e) (a score is then already in
+// log2 units); otherwise every score is multiplied by it before the exp2.
+template <bool QS>
 __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
   constexpr int NW = 8 / QB;          // wavefronts per workgroup
   constexpr int KBW = 16 / NW;        // 1-KB blocks of a K (or V^T) tile each wavefront loads
@@ -102,10 +105,8 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
 
   // ---- Q fragments (B operand of S^T = K Q^T): for query block qb the lane
   // holds Q[q][st*16 + g*8 .. +8] of query q = qrow[qb]
-  // times c = scale * log2 e, so that scores come out in log2 units: done by
-  // the producer when q_scaled (one rounding), else here (a second bf16
-  // rounding of q)
-  const float c = a.scale * 1.4426950408889634f;
+  // log2 units per score unit: 1 for a pre-scaled q, else scale * log2(e)
+  const float c = QS ? 1.0f : a.scale * 1.4426950408889634f;
   int qrow[QB];
   bf16x8 qf[QB][8];
 #pragma unroll
@@ -116,12 +117,7 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       uint4 v = ok ? ld16(qp + st * 16) : make_uint4(0, 0, 0, 0);
-      bf16x8 f = *reinterpret_cast<bf16x8 *>(&v);
-      if (!a.q_scaled) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = f2bf(bf2f(f[e]) * c);
-      }
-      qf[qb][st] = f;
+      qf[qb][st] = *reinterpret_cast<bf16x8 *>(&v);
     }
   }
 
@@ -132,7 +128,8 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[t][qb][r] = 0.f;
-  // nm[qb]: -m in all 16 entries (the score MFMAs' initial accumulator)
+  // nm[qb]: -m in all 16 entries (the score MFMAs' initial accumulator); m
+  // is the running max in score units (log2 units when QS)
   f32x16 nm[QB];
   float l[QB];
 #pragma unroll
@@ -256,7 +253,8 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            pb[qb][kb][hf][e] = f2bf(__builtin_amdgcn_exp2f(s[kb][qb][hf * 8 + e]));
+            pb[qb][kb][hf][e] = f2bf(__builtin_amdgcn_exp2f(QS ? s[kb][qb][hf * 8 + e]
+                                                               : s[kb][qb][hf * 8 + e] * c));
           const bf16x2 *pp = reinterpret_cast<const bf16x2 *>(&pb[qb][kb][hf]);
           ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[0], one, ls0, false);
           ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[1], one, ls1, false);
@@ -289,7 +287,7 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       dm[qb] = fmaxf(mx[qb], 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-dm[qb]);
+      const float alpha = __builtin_amdgcn_exp2f(-dm[qb] * c);
       l[qb] *= alpha;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -508,7 +506,8 @@ hipError_t launch_attention(const AttnDesc &a, hipStream_t s) {
   if ((long)a.H * a.hd * a.ldv * 2 >= (1L << 31)) return hipErrorInvalidValue;
   if (a.vt_bstride < (a.Lk + AK - 1) / AK * AK) return hipErrorInvalidValue;
   const int nqt = (a.Lq + AQ - 1) / AQ;
-  k_attn_bf16<<<a.B * a.H * nqt, 512 / QB, 0, s>>>(a);
+  if (a.q_scaled) k_attn_bf16<true><<<a.B * a.H * nqt, 512 / QB, 0, s>>>(a);
+  else k_attn_bf16<false><<<a.B * a.H * nqt, 512 / QB, 0, s>>>(a);
   return hipGetLastError();
 }
 

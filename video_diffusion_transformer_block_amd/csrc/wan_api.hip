@@ -654,7 +654,7 @@ int wan_i2v_mask(const uint8_t *frame_mask, int n_frames, int lat_f, int H8, int
 }
 
 int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv,
-                      int vt_bstride, void *o, int ldo, int B, int H, int Lq, int Lk,
+                      int vt_bstride, void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled,
                       void *stream) {
   if (!q || !k || !vt || !o) return WAN_ERR_NULL;
   if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return WAN_ERR_SHAPE;
@@ -662,7 +662,7 @@ int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void
     return WAN_ERR_SHAPE;
   if (ldv % 8 || vt_bstride % 8 || vt_bstride < rup(Lk, 64) || (long)ldv < (long)B * vt_bstride)
     return WAN_ERR_SHAPE;
-  AttnDesc a = attn(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk, 128, 0);
+  AttnDesc a = attn(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk, 128, 0, q_scaled != 0);
   WAN_TRY(launch_attention(a, S(stream)));
   return WAN_OK;
 }
