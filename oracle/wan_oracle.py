@@ -76,6 +76,10 @@ READINGS = {
                            "(the pages run the model in bf16 and quantise for the GEMM); it is "
                            "rounded to bf16 (nearest even) before its per-token quantisation, so "
                            "the E4M3 code is decided from a bf16 value on both sides",
+    "R24 FP8 layers": "the FP8 block runs its six Linear layers on the token stream in FP8 (QKV "
+                      "quantised as one [3d, d] tensor, SA out, CA query, CA out, FFN up, FFN "
+                      "down); text / image K/V, LayerNorm, attention, GELU and the residual "
+                      "stay exact",
 }
 
 
@@ -269,7 +273,7 @@ def block(x, m, wts: Dict[str, np.ndarray], ctx, heads: int, eps: float = 1e-6,
     With ``rows`` only those token rows of the output are computed (self-
     attention still reads all tokens' keys and values).  ``fp8``: the six
     Linear layers (QKV, SA out, CA query, CA out, FFN up, FFN down) in FP8
-    with per-token activation and per-tensor weight scales (R22)
+    with per-token activation and per-tensor weight scales (R22 - R24)
     [Note, Infra / 推理优化: FP8 GEMM]."""
     x = _f(x)
     mod = block_modulation(m, wts["mod_bias"])
