@@ -16,8 +16,10 @@
 // K tiles ahead are issued (two LDS stages, one barrier per K tile).  Tail rows / columns
 // load a clamped (in-bounds) row and are never stored.  Tiles are visited in
 // groups of 8 M-tiles so that the 32 workgroups an XCD runs at once share A
-// and B slices in that XCD's L2.  The epilogue goes through LDS so every
-// lane stores 16 contiguous bytes of one output row.
+// and B slices in that XCD's L2.  For float32 outputs the MFMAs compute the
+// tile transposed (operands swapped), so each lane holds runs of 4
+// consecutive columns of one output row and the epilogue works straight from
+// the accumulators; bf16 outputs are staged through LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -132,6 +134,106 @@ WAN_DEV void epi8(const GemmDesc &g, int m, int n, float *v) {
   }
 }
 
+// Epilogue on 4 consecutive columns n..n+3 (n % 4 == 0) of row m, or
+// element-wise for a ragged column tail; columns N .. npad-1 of a bf16 output
+// are written as zeros.
+template <int KIND, bool BROWS, bool SCALED>
+WAN_DEV void epi4(const GemmDesc &g, int m, int n, float *v) {
+  const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
+  const bool full = n + 4 <= g.N;
+  if (SCALED) {   // FP8 dequantisation: row scale (per token or per tensor) times column scale
+    const float sa = g.a_scale[g.a_per_row ? m : 0];
+    if (g.b_per_col) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] *= sa * g.b_scale[n + i < g.N ? n + i : g.N - 1];
+    } else {
+      const float sc = sa * g.b_scale[0];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] *= sc;
+    }
+  }
+  if (bias) {
+    if (BROWS) {
+      const float bb = (float)bias[m];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += bb;
+    } else if (full) {
+      const uint2 u = *reinterpret_cast<const uint2 *>(bias + n);
+      const bf16 *e = reinterpret_cast<const bf16 *>(&u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += (float)e[i];
+    } else {
+      for (int i = 0; i < 4 && n + i < g.N; ++i) v[i] += (float)bias[n + i];
+    }
+  }
+  if (KIND == OUT_GELU) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = gelu_tanh(v[i]);
+  }
+  if (KIND == OUT_BF16 && n < g.scale_cols) {   // scale_cols % 8 == 0: whole groups
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] *= g.col_scale;
+  }
+  if (KIND == OUT_BF16 || KIND == OUT_GELU) {
+    bf16 *c = reinterpret_cast<bf16 *>(g.C) + (long)m * g.ldc + n;
+    if (full) {
+      bf16x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = f2bf(v[i]);
+      *reinterpret_cast<bf16x4 *>(c) = o;
+    } else {
+      const int lim = g.npad > g.N ? g.npad : g.N;
+      for (int i = 0; i < 4 && n + i < lim; ++i) c[i] = n + i < g.N ? f2bf(v[i]) : f2bf(0.f);
+    }
+  } else if (KIND == OUT_F32) {
+    float *c = reinterpret_cast<float *>(g.C) + (long)m * g.ldc + n;
+    if (full) *reinterpret_cast<float4 *>(c) = make_float4(v[0], v[1], v[2], v[3]);
+    else
+      for (int i = 0; i < 4 && n + i < g.N; ++i) c[i] = v[i];
+  } else {  // OUT_RESID: x += gate * v
+    float *xp = g.X + (long)m * g.ldx + n;
+    const float *gp = g.gate ? g.gate + (long)(m / g.rows_per_batch) * g.gate_bstride + n : nullptr;
+    if (full) {
+      float4 x = *reinterpret_cast<float4 *>(xp);
+      if (gp) {
+        const float4 gg = *reinterpret_cast<const float4 *>(gp);
+        x.x += gg.x * v[0]; x.y += gg.y * v[1]; x.z += gg.z * v[2]; x.w += gg.w * v[3];
+      } else {
+        x.x += v[0]; x.y += v[1]; x.z += v[2]; x.w += v[3];
+      }
+      *reinterpret_cast<float4 *>(xp) = x;
+    } else {
+      for (int i = 0; i < 4 && n + i < g.N; ++i) xp[i] += (gp ? gp[i] : 1.0f) * v[i];
+    }
+  }
+}
+
+// Epilogue straight from the accumulators, no LDS: the tile is computed with
+// the MFMA operands swapped (C^T = B A^T), so lane l of block (i, j) of
+// wavefront (wm, wn) holds C[m][n .. n+3] in registers 4q .. 4q+3, with
+// m = m0 + wm*128 + i*32 + l%32 and n = n0 + wn*64 + j*32 + 8q + 4(l/32).
+template <int KIND, bool BROWS, bool SCALED>
+WAN_DEV void epilogue_regs(const GemmDesc &g, const f32x16 (&acc)[4][2], int lane, int m0, int n0,
+                           int wm, int wn) {
+  const int half = lane >> 5, l32 = lane & 31;
+  const int lim = g.npad > g.N ? g.npad : g.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 128 + i * 32 + l32;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 64 + j * 32 + q * 8 + half * 4;
+        if (n < lim) {
+          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          epi4<KIND, BROWS, SCALED>(g, m, n, v);
+        }
+      }
+  }
+}
+
 // Epilogue through LDS: per wave 4 slabs of 32 rows x 64 columns (fp32,
 // padded rows), so every lane handles 8 contiguous columns of one row.  The
 // caller has synchronised the workgroup (the LDS tiles are free).
@@ -172,6 +274,13 @@ WAN_DEV void epilogue(const GemmDesc &g, const f32x16 (&acc)[4][2], float *lds, 
     __builtin_amdgcn_wave_barrier();
   }
 }
+
+// Float32 outputs (plain and the residual update of the float32 stream) are
+// written from the registers of a transposed tile: 16-byte runs per lane,
+// no LDS round trip, and the residual's read-modify-write of x overlaps
+// across the whole tile.  bf16 outputs go through LDS, where every lane
+// stores 16 contiguous bytes.
+template <int KIND> constexpr bool epi_from_regs() { return KIND == OUT_F32 || KIND == OUT_RESID; }
 
 template <int KIND, bool BROWS>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
@@ -261,7 +370,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+        if constexpr (epi_from_regs<KIND>())
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
   };
   // scheduling hint: one MFMA, one LDS read, alternately (6 reads), then 2 MFMAs
   auto interleave = [&]() {
@@ -317,8 +429,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
   if (kt < KT) tile(kt, 0);
   if (kt + 1 < KT) tile(kt + 1, 1);
 
-  __syncthreads();
-  epilogue<KIND, BROWS, false>(g, acc, reinterpret_cast<float *>(smem), w, lane, m0, n0, wm, wn);
+  if constexpr (epi_from_regs<KIND>()) {
+    epilogue_regs<KIND, BROWS, false>(g, acc, lane, m0, n0, wm, wn);
+  } else {
+    __syncthreads();
+    epilogue<KIND, BROWS, false>(g, acc, reinterpret_cast<float *>(smem), w, lane, m0, n0, wm, wn);
+  }
 }
 
 // FP8 operands (OCP E4M3; "Wan: Open and Advanced Large-Scale Video Generative
@@ -332,7 +448,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
 // in the same k order, which is all the dot product needs.  Per tile: the
 // loads of tile kt+2 start, the 8 MFMAs of tile kt run from registers, one
 // barrier, then the fragments of tile kt+1 are read into the same registers
-// while those MFMAs execute.  The epilogue scales by a_scale[m] * b_scale[0].
+// while those MFMAs execute.  The epilogue (registers or LDS, as for bf16
+// operands) scales by the row scale times the column scale.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 template <int KIND, bool BROWS>
@@ -451,8 +568,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(GemmDesc g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fa[i], fb[j], acc[i][j], 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+        if constexpr (epi_from_regs<KIND>())
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0,
+                                                                      0x7F7F7F7F, 0, 0x7F7F7F7F);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0,
+                                                                      0x7F7F7F7F, 0, 0x7F7F7F7F);
   };
 
   const int KT = g.K / GBK8;
@@ -489,9 +610,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(GemmDesc g) {
   for (; kt < KT; ++kt)             // the last 1 .. 3 tiles: one generic copy with run-time flags
     tile(kt, kt & 1, kt + 2 < KT, kt + 1 < KT);
 
-  // the epilogue stages 8 wavefronts x 32 rows x 68 floats through its own LDS buffer
-  __shared__ __attribute__((aligned(16))) float sEp[GW * 32 * 68];
-  epilogue<KIND, BROWS, true>(g, acc, sEp, w, lane, m0, n0, wm, wn);
+  if constexpr (epi_from_regs<KIND>()) {
+    epilogue_regs<KIND, BROWS, true>(g, acc, lane, m0, n0, wm, wn);
+  } else {
+    // 8 wavefronts x 32 rows x 68 floats staged through an LDS buffer of its own
+    __shared__ __attribute__((aligned(16))) float sEp[GW * 32 * 68];
+    epilogue<KIND, BROWS, true>(g, acc, sEp, w, lane, m0, n0, wm, wn);
+  }
 }
 
 // per-element epilogue (float32 path)
