@@ -42,98 +42,6 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 // have landed and every LDS read of this wavefront has returned
 template <int N> WAN_DEV void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0070 | N); }
 
-template <typename T> struct Vec8;
-template <> struct Vec8<bf16> {
-  static WAN_DEV void load(const bf16 *p, float *v) {
-    uint4 u = ld16(p);
-    const bf16 *e = reinterpret_cast<const bf16 *>(&u);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (float)e[i];
-  }
-  static WAN_DEV void store(bf16 *p, const float *v) {
-    bf16x8 o;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = f2bf(v[i]);
-    *reinterpret_cast<bf16x8 *>(p) = o;
-  }
-};
-
-// Epilogue on 8 consecutive columns n..n+7 of row m (n + 8 <= N and 16-byte
-// aligned rows), or element-wise for a ragged column tail.
-template <int KIND, bool BROWS, bool SCALED = false>
-WAN_DEV void epi8(const GemmDesc &g, int m, int n, float *v) {
-  const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
-  const bool full = n + 8 <= g.N;
-  if (SCALED) {   // FP8 dequantisation: row scale (per token or per tensor) times column scale
-    const float sa = g.a_scale[g.a_per_row ? m : 0];
-    if (g.b_per_col) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] *= sa * g.b_scale[n + i < g.N ? n + i : g.N - 1];
-    } else {
-      const float sc = sa * g.b_scale[0];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] *= sc;
-    }
-  }
-  if (bias) {
-    if (BROWS) {
-      const float bb = (float)bias[m];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] += bb;
-    } else if (full) {
-      float bv[8];
-      Vec8<bf16>::load(bias + n, bv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] += bv[i];
-    } else {
-      for (int i = 0; i < 8 && n + i < g.N; ++i) v[i] += (float)bias[n + i];
-    }
-  }
-  if (KIND == OUT_GELU) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = gelu_tanh(v[i]);
-  }
-  if (KIND == OUT_BF16 && n < g.scale_cols) {   // scale_cols % 8 == 0: whole chunks
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] *= g.col_scale;
-  }
-  if (KIND == OUT_BF16 || KIND == OUT_GELU) {
-    bf16 *c = reinterpret_cast<bf16 *>(g.C) + (long)m * g.ldc + n;
-    if (full) {
-      Vec8<bf16>::store(c, v);
-    } else {
-      const int lim = g.npad > g.N ? g.npad : g.N;
-      for (int i = 0; i < 8 && n + i < lim; ++i) c[i] = n + i < g.N ? f2bf(v[i]) : f2bf(0.f);
-    }
-  } else if (KIND == OUT_F32) {
-    float *c = reinterpret_cast<float *>(g.C) + (long)m * g.ldc + n;
-    if (full) {
-      *reinterpret_cast<float4 *>(c) = make_float4(v[0], v[1], v[2], v[3]);
-      *reinterpret_cast<float4 *>(c + 4) = make_float4(v[4], v[5], v[6], v[7]);
-    } else {
-      for (int i = 0; i < 8 && n + i < g.N; ++i) c[i] = v[i];
-    }
-  } else {  // OUT_RESID: x += gate * v
-    float *xp = g.X + (long)m * g.ldx + n;
-    const float *gp = g.gate ? g.gate + (long)(m / g.rows_per_batch) * g.gate_bstride + n : nullptr;
-    if (full) {
-      float4 x0 = *reinterpret_cast<float4 *>(xp), x1 = *reinterpret_cast<float4 *>(xp + 4);
-      if (gp) {
-        float4 g0 = *reinterpret_cast<const float4 *>(gp), g1 = *reinterpret_cast<const float4 *>(gp + 4);
-        x0.x += g0.x * v[0]; x0.y += g0.y * v[1]; x0.z += g0.z * v[2]; x0.w += g0.w * v[3];
-        x1.x += g1.x * v[4]; x1.y += g1.y * v[5]; x1.z += g1.z * v[6]; x1.w += g1.w * v[7];
-      } else {
-        x0.x += v[0]; x0.y += v[1]; x0.z += v[2]; x0.w += v[3];
-        x1.x += v[4]; x1.y += v[5]; x1.z += v[6]; x1.w += v[7];
-      }
-      *reinterpret_cast<float4 *>(xp) = x0;
-      *reinterpret_cast<float4 *>(xp + 4) = x1;
-    } else {
-      for (int i = 0; i < 8 && n + i < g.N; ++i) xp[i] += (gp ? gp[i] : 1.0f) * v[i];
-    }
-  }
-}
-
 // Epilogue on 4 consecutive columns n..n+3 (n % 4 == 0) of row m, or
 // element-wise for a ragged column tail; columns N .. npad-1 of a bf16 output
 // are written as zeros.
@@ -234,39 +142,88 @@ WAN_DEV void epilogue_regs(const GemmDesc &g, const f32x16 (&acc)[4][2], int lan
   }
 }
 
-// Epilogue through LDS: per wave 4 slabs of 32 rows x 64 columns (fp32,
-// padded rows), so every lane handles 8 contiguous columns of one row.  The
-// caller has synchronised the workgroup (the LDS tiles are free).
+// Epilogue of bf16 outputs through LDS: per wave 4 slabs of 32 rows x 64
+// columns (fp32, padded rows), so every lane finishes 8 contiguous columns
+// (cb + 8q, q = 0..3) of one row and stores 16 bytes.  Everything it reads
+// from global memory (bias, FP8 scales) is loaded before its first store: the
+// memory counter retires in issue order, so a load issued after a store would
+// wait for that store.  The caller has synchronised the workgroup.
 template <int KIND, bool BROWS, bool SCALED>
 WAN_DEV void epilogue(const GemmDesc &g, const f32x16 (&acc)[4][2], float *lds, int w, int lane,
                       int m0, int n0, int wm, int wn) {
+  static_assert(KIND == OUT_BF16 || KIND == OUT_GELU, "bf16 outputs only");
   const int half = lane >> 5, l32 = lane & 31;
   constexpr int EP = 68;
   float *ep = lds + w * 32 * EP;
+  const int row = lane >> 1, cb = (lane & 1) * 32;
+  const int nb = n0 + wn * 64 + cb;          // column of q = 0
+  const int mb = m0 + wm * 128 + row;        // row of slab 0
+  const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
+  // column terms of the lane's 32 columns (a bias per column, or an FP8
+  // scale per column when the columns are tokens: the bias-rows GEMMs), row
+  // terms of its 4 rows (indices clamped into the matrix; clamped values are
+  // never stored)
+  constexpr bool CADD = !BROWS, CMUL = SCALED && BROWS;
+  bf16x8 cadd[4];   // kept as bf16: 4 registers per 8 columns
+  float cmul[4][8], radd[4], rmul[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int n = nb + q * 8;
+    if (CADD && bias && n + 8 <= g.N) {
+      const uint4 u = ld16(bias + n);
+      cadd[q] = *reinterpret_cast<const bf16x8 *>(&u);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        cadd[q][k] = CADD && bias ? bias[n + k < g.N ? n + k : g.N - 1] : (bf16)0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      cmul[q][k] = CMUL ? g.b_scale[g.b_per_col ? (n + k < g.N ? n + k : g.N - 1) : 0] : 1.f;
+  }
+  const float csc = SCALED && !CMUL ? g.b_scale[0] : 1.f;   // a per-tensor column scale
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int mc = min(mb + i * 32, g.M - 1);
+    radd[i] = bias && BROWS ? (float)bias[mc] : 0.f;
+    rmul[i] = SCALED ? g.a_scale[g.a_per_row ? mc : 0] * csc : 1.f;
+  }
+  const int lim = g.npad > g.N ? g.npad : g.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = (r >> 2) * 8 + half * 4 + (r & 3);
-        ep[row * EP + jj * 32 + l32] = acc[i][jj][r];
+        const int rr = (r >> 2) * 8 + half * 4 + (r & 3);
+        ep[rr * EP + jj * 32 + l32] = acc[i][jj][r];
       }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
-    const int row = lane >> 1, cb = (lane & 1) * 32;
-    const int m = m0 + wm * 128 + i * 32 + row;
+    const int m = mb + i * 32;
     if (m < g.M) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 64 + cb + q * 8;
-        if (n < g.N || n < g.npad) {
-          float v[8];
+        const int n = nb + q * 8;
+        if (n < lim) {
           const float4 u0 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8);
           const float4 u1 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8 + 4);
-          v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
-          v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
-          epi8<KIND, BROWS, SCALED>(g, m, n, v);
+          float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            v[k] = v[k] * rmul[i] * (CMUL ? cmul[q][k] : 1.f) + radd[i] + (CADD ? (float)cadd[q][k] : 0.f);
+            if (KIND == OUT_GELU) v[k] = gelu_tanh(v[k]);
+            if (KIND == OUT_BF16 && n < g.scale_cols) v[k] *= g.col_scale;
+          }
+          bf16 *c = reinterpret_cast<bf16 *>(g.C) + (long)m * g.ldc + n;
+          if (n + 8 <= g.N) {
+            bf16x8 o;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[k] = f2bf(v[k]);
+            *reinterpret_cast<bf16x8 *>(c) = o;
+          } else {
+            for (int k = 0; k < 8 && n + k < lim; ++k) c[k] = n + k < g.N ? f2bf(v[k]) : f2bf(0.f);
+          }
         }
       }
     }
@@ -694,6 +651,7 @@ hipError_t launch_gemm(const GemmDesc &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.fp8) {
     if (g.K % 64 || !g.a_scale || !g.b_scale || g.f32) return hipErrorInvalidValue;
+    if (g.b_per_col && !g.bias_rows) return hipErrorInvalidValue;   // per-column scales: token columns only
     if ((long)g.M * g.lda >= (1L << 31) || (long)g.N * g.ldb >= (1L << 31)) return hipErrorInvalidValue;
     const int blocks = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
     if (g.bias_rows) {
