@@ -301,6 +301,39 @@ def fp8_block_bench(steps: int, warmup: int):
           flush=True)
 
 
+def fp8_block_leg(W, cfg, work, bwd, mod, ctx, stream, steps, warmup, bf16_ms, tmlp):
+    """Time the step with wan_dit_block_fp8_fwd in place of the bf16 block (the
+    same t-MLP call first; weights quantised once beforehand; the per-token
+    activation quantisation is inside the timed region), on its own copy of
+    the residual stream."""
+    import torch
+    desc = W.block_weights(bwd)
+    qbuf = torch.empty(W.block_fp8_bytes(cfg), dtype=torch.uint8, device="cuda")
+    W.quantize_block_fp8(cfg, desc, qbuf, stream)
+    ws = torch.empty(W.block_fp8_workspace_bytes(cfg, work.batch, work.lat_f, work.Hp, work.Wp),
+                     dtype=torch.uint8, device="cuda")
+    x = torch.randn((work.batch, work.L, cfg.dim), generator=torch.Generator().manual_seed(3)).cuda()
+    geo = (work.batch, work.lat_f, work.Hp, work.Wp)
+    def step8():
+        tmlp()
+        W.dit_block_fp8_fwd(cfg, x, *geo, mod, desc, qbuf, ctx, None, ws, stream)
+
+    for _ in range(max(1, warmup)):
+        step8()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step8()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms8 = e0.elapsed_time(e1) / steps
+    if not bool(torch.isfinite(x).all()):
+        raise RuntimeError("non-finite FP8 block output")
+    return {"ms_per_step": round(ms8, 4), "tokens_per_s": round(work.batch * work.L / (ms8 * 1e-3), 1),
+            "speedup_vs_bf16": round(bf16_ms / ms8, 4), "dtype": "fp8 e4m3 Linear layers, bf16 attention"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -451,6 +484,9 @@ def main():
                      "flop_per_launch": sa_f},
         "wall_s_timed": round(t_wall, 3),
     }
+    if m.dtype == "bf16":   # the same block with its six Linear layers in FP8 (E4M3), same inputs
+        out["fp8_block"] = fp8_block_leg(W, cfg, work, bwd, mod, ctx, stream, args.steps, args.warmup, ms,
+                                         lambda: W.tmlp_fwd(cfg, t, tws_c, mod, tws, stream))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work, inp, tw, bw)
     print(json.dumps(out), flush=True)
