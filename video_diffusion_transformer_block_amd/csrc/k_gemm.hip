@@ -42,30 +42,22 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 // have landed and every LDS read of this wavefront has returned
 template <int N> WAN_DEV void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0070 | N); }
 
-// Epilogue on 4 consecutive columns n..n+3 (n % 4 == 0) of row m, or
-// element-wise for a ragged column tail; columns N .. npad-1 of a bf16 output
-// are written as zeros.
+// Epilogue of a float32 output on 4 consecutive columns n..n+3 (n % 4 == 0)
+// of row m, or element-wise for a ragged column tail: a plain store, or the
+// gated residual x += gate * v into the float32 stream.
 template <int KIND, bool BROWS, bool SCALED>
 WAN_DEV void epi4(const GemmDesc &g, int m, int n, float *v) {
+  static_assert(KIND == OUT_F32 || KIND == OUT_RESID, "float32 outputs only");
+  static_assert(!BROWS, "bias along rows: bf16 outputs only");
   const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
   const bool full = n + 4 <= g.N;
-  if (SCALED) {   // FP8 dequantisation: row scale (per token or per tensor) times column scale
-    const float sa = g.a_scale[g.a_per_row ? m : 0];
-    if (g.b_per_col) {
+  if (SCALED) {   // FP8 dequantisation: row scale (per token or per tensor) times the tensor's
+    const float sc = g.a_scale[g.a_per_row ? m : 0] * g.b_scale[0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] *= sa * g.b_scale[n + i < g.N ? n + i : g.N - 1];
-    } else {
-      const float sc = sa * g.b_scale[0];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] *= sc;
-    }
+    for (int i = 0; i < 4; ++i) v[i] *= sc;
   }
   if (bias) {
-    if (BROWS) {
-      const float bb = (float)bias[m];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] += bb;
-    } else if (full) {
+    if (full) {
       const uint2 u = *reinterpret_cast<const uint2 *>(bias + n);
       const bf16 *e = reinterpret_cast<const bf16 *>(&u);
 #pragma unroll
@@ -74,26 +66,7 @@ WAN_DEV void epi4(const GemmDesc &g, int m, int n, float *v) {
       for (int i = 0; i < 4 && n + i < g.N; ++i) v[i] += (float)bias[n + i];
     }
   }
-  if (KIND == OUT_GELU) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = gelu_tanh(v[i]);
-  }
-  if (KIND == OUT_BF16 && n < g.scale_cols) {   // scale_cols % 8 == 0: whole groups
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] *= g.col_scale;
-  }
-  if (KIND == OUT_BF16 || KIND == OUT_GELU) {
-    bf16 *c = reinterpret_cast<bf16 *>(g.C) + (long)m * g.ldc + n;
-    if (full) {
-      bf16x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = f2bf(v[i]);
-      *reinterpret_cast<bf16x4 *>(c) = o;
-    } else {
-      const int lim = g.npad > g.N ? g.npad : g.N;
-      for (int i = 0; i < 4 && n + i < lim; ++i) c[i] = n + i < g.N ? f2bf(v[i]) : f2bf(0.f);
-    }
-  } else if (KIND == OUT_F32) {
+  if (KIND == OUT_F32) {
     float *c = reinterpret_cast<float *>(g.C) + (long)m * g.ldc + n;
     if (full) *reinterpret_cast<float4 *>(c) = make_float4(v[0], v[1], v[2], v[3]);
     else
@@ -124,7 +97,6 @@ template <int KIND, bool BROWS, bool SCALED>
 WAN_DEV void epilogue_regs(const GemmDesc &g, const f32x16 (&acc)[4][2], int lane, int m0, int n0,
                            int wm, int wn) {
   const int half = lane >> 5, l32 = lane & 31;
-  const int lim = g.npad > g.N ? g.npad : g.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + wm * 128 + i * 32 + l32;
@@ -134,7 +106,7 @@ WAN_DEV void epilogue_regs(const GemmDesc &g, const f32x16 (&acc)[4][2], int lan
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + wn * 64 + j * 32 + q * 8 + half * 4;
-        if (n < lim) {
+        if (n < g.N) {
           float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
           epi4<KIND, BROWS, SCALED>(g, m, n, v);
         }
@@ -669,6 +641,7 @@ hipError_t launch_gemm(const GemmDesc &g, hipStream_t s) {
     return hipGetLastError();
   }
   if (!g.f32 && (g.K % GBK)) return hipErrorInvalidValue;
+  if (g.bias_rows && g.kind != OUT_BF16) return hipErrorInvalidValue;   // bias along rows: bf16 outputs
   // the bf16 kernel addresses A and B with 32-bit byte offsets
   if (!g.f32 && ((long)g.M * g.lda * 2 >= (1L << 31) || (long)g.N * g.ldb * 2 >= (1L << 31)))
     return hipErrorInvalidValue;
