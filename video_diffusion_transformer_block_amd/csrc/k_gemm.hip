@@ -16,10 +16,10 @@
 // K tiles ahead are issued (two LDS stages, one barrier per K tile).  Tail rows / columns
 // load a clamped (in-bounds) row and are never stored.  Tiles are visited in
 // groups of 8 M-tiles so that the 32 workgroups an XCD runs at once share A
-// and B slices in that XCD's L2.  For float32 outputs the MFMAs compute the
-// tile transposed (operands swapped), so each lane holds runs of 4
-// consecutive columns of one output row and the epilogue works straight from
-// the accumulators; bf16 outputs are staged through LDS.
+// and B slices in that XCD's L2.  The MFMAs compute the tile transposed
+// (operands swapped), so each lane holds runs of 4 consecutive columns of one
+// output row: float32 outputs are written straight from the accumulators,
+// bf16 outputs are staged through LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -115,7 +115,8 @@ WAN_DEV void epilogue_regs(const GemmDesc &g, const f32x16 (&acc)[4][2], int lan
 }
 
 // Epilogue of bf16 outputs through LDS: per wave 4 slabs of 32 rows x 64
-// columns (fp32, padded rows), so every lane finishes 8 contiguous columns
+// columns (fp32, padded rows), written from the transposed tile's runs of 4
+// columns, read back so that every lane finishes 8 contiguous columns
 // (cb + 8q, q = 0..3) of one row and stores 16 bytes.  Everything it reads
 // from global memory (bias, FP8 scales) is loaded before its first store: the
 // memory counter retires in issue order, so a load issued after a store would
@@ -163,13 +164,14 @@ WAN_DEV void epilogue(const GemmDesc &g, const f32x16 (&acc)[4][2], float *lds, 
   const int lim = g.npad > g.N ? g.npad : g.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    // the transposed tile: lane l holds row l%32, columns 8q + 4(l/32) .. +3
+    // of each 32-column block jj -- one 16-byte LDS write per run
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = (r >> 2) * 8 + half * 4 + (r & 3);
-        ep[rr * EP + jj * 32 + l32] = acc[i][jj][r];
-      }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(ep + l32 * EP + jj * 32 + q * 8 + half * 4) =
+            make_float4(acc[i][jj][4 * q], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2], acc[i][jj][4 * q + 3]);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
     const int m = mb + i * 32;
@@ -204,11 +206,12 @@ WAN_DEV void epilogue(const GemmDesc &g, const f32x16 (&acc)[4][2], float *lds, 
   }
 }
 
-// Float32 outputs (plain and the residual update of the float32 stream) are
-// written from the registers of a transposed tile: 16-byte runs per lane,
-// no LDS round trip, and the residual's read-modify-write of x overlaps
-// across the whole tile.  bf16 outputs go through LDS, where every lane
-// stores 16 contiguous bytes.
+// Every tile is computed transposed (C^T = B A^T: MFMA operands swapped), so
+// a lane holds runs of 4 consecutive columns of one output row.  Float32
+// outputs (plain and the residual update of the float32 stream) are written
+// straight from those registers: 16-byte runs per lane, no LDS round trip.
+// bf16 outputs are staged through LDS (one 16-byte write per run), so that
+// every lane then stores 16 contiguous bytes of bf16.
 template <int KIND> constexpr bool epi_from_regs() { return KIND == OUT_F32 || KIND == OUT_RESID; }
 
 template <int KIND, bool BROWS>
@@ -299,10 +302,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        if constexpr (epi_from_regs<KIND>())
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
   };
   // scheduling hint: one MFMA, one LDS read, alternately (6 reads), then 2 MFMAs
   auto interleave = [&]() {
@@ -497,12 +497,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(GemmDesc g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        if constexpr (epi_from_regs<KIND>())
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0,
-                                                                      0x7F7F7F7F, 0, 0x7F7F7F7F);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0,
-                                                                      0x7F7F7F7F, 0, 0x7F7F7F7F);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0,
+                                                                    0x7F7F7F7F, 0, 0x7F7F7F7F);
   };
 
   const int KT = g.K / GBK8;
