@@ -360,12 +360,14 @@ def image_context(clip, w1, b1, w2, b2, w3, b3):
 
 def step(latent, t, ctx, mw: Dict[str, object], heads: int, eps: float = 1e-6,
          clip=None, blocks: Optional[List[Dict[str, np.ndarray]]] = None,
-         return_hidden: bool = False):
+         return_hidden: bool = False, fp8: bool = False):
     """patchify -> shared t-MLP -> N blocks -> head -> unpatchify.
     latent [B, Cin, F, H8, W8]; t [B]; ctx [B, Lc, d]; clip [B, Li, 1280] or None.
     Returns the predicted velocity [B, 16, F, H8, W8] (the flow-matching
     target of [Note, 训练方法]).  ``blocks`` may be an iterable that yields the
-    block weights one at a time (to bound host memory)."""
+    block weights one at a time (to bound host memory).  ``fp8``: every block
+    with its six Linear layers in FP8 (R22 - R24); patchify, t-MLP, image MLP
+    and head stay exact."""
     lat = _f(latent)
     B, Cin, F, H8, W8 = lat.shape
     Hp, Wp = H8 // 2, W8 // 2
@@ -378,7 +380,7 @@ def step(latent, t, ctx, mw: Dict[str, object], heads: int, eps: float = 1e-6,
         img = np.stack([image_context(clip[b], iw["w1"], iw["b1"], iw["w2"], iw["b2"],
                                       iw["w3"], iw["b3"]) for b in range(B)])
     for wts in (blocks if blocks is not None else mw["blocks"]):
-        x = block(x, m, wts, ctx, heads, eps, img=img)
+        x = block(x, m, wts, ctx, heads, eps, img=img, fp8=fp8)
     out = head_unpatchify(x, mw["head_w"], mw["head_b"], F, Hp, Wp, 16)
     return (out, x) if return_hidden else out
 

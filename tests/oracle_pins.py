@@ -573,3 +573,46 @@ def pin_bf16_round(O):
     x32 = x.astype(np.float32).astype(np.float64)
     assert np.all(np.abs(got - x32) <= np.abs(x32) * 2.0 ** -8)
 
+
+def pin_fp8_step(O):
+    """The step's FP8 switch reaches every block and nothing else: with the
+    quantisers replaced by the identity it equals the exact step bit for bit,
+    and the weight quantiser sees each block's six weights (two blocks)."""
+    r = _rng(53)
+    d, F, H, Lc, nb = 64, 128, 2, 5, 2
+    def blk():
+        return {"sa_wqkv": r.standard_normal((3 * d, d)) * 0.1, "sa_bqkv": r.standard_normal(3 * d) * 0.02,
+                "sa_wo": r.standard_normal((d, d)) * 0.1, "sa_bo": r.standard_normal(d) * 0.02,
+                "ca_wq": r.standard_normal((d, d)) * 0.1, "ca_bq": r.standard_normal(d) * 0.02,
+                "ca_wkv": r.standard_normal((2 * d, d)) * 0.1, "ca_bkv": r.standard_normal(2 * d) * 0.02,
+                "ca_wo": r.standard_normal((d, d)) * 0.1, "ca_bo": r.standard_normal(d) * 0.02,
+                "ffn_w1": r.standard_normal((F, d)) * 0.1, "ffn_b1": r.standard_normal(F) * 0.02,
+                "ffn_w2": r.standard_normal((d, F)) * 0.1, "ffn_b2": r.standard_normal(d) * 0.02,
+                "mod_bias": r.standard_normal(6 * d) * 0.02}
+    mw = {"patch_w": r.standard_normal((d, 64)) * 0.1, "patch_b": r.standard_normal(d) * 0.02,
+          "tmlp": {"w1": r.standard_normal((d, 256)) * 0.05, "b1": r.standard_normal(d) * 0.02,
+                   "w2": r.standard_normal((6 * d, d)) * 0.05, "b2": r.standard_normal(6 * d) * 0.02},
+          "head_w": r.standard_normal((64, d)) * 0.1, "head_b": r.standard_normal(64) * 0.02,
+          "blocks": [blk() for _ in range(nb)]}
+    lat = r.standard_normal((1, 16, 2, 4, 6))
+    t = np.array([500.0])
+    ctx = r.standard_normal((1, Lc, d))
+    exact = O.step(lat, t, ctx, mw, H)
+    qr, qt, br = O.quantize_rows_fp8, O.quantize_tensor_fp8, O.bf16_round
+    seen = []
+    try:
+        O.quantize_rows_fp8 = lambda a: (np.asarray(a, np.float64), np.ones(np.shape(a)[0]))
+
+        def fake_tensor(a):
+            seen.append(np.shape(a))
+            return np.asarray(a, np.float64), 1.0
+        O.quantize_tensor_fp8 = fake_tensor
+        O.bf16_round = lambda a: np.asarray(a, np.float64)
+        same = O.step(lat, t, ctx, mw, H, fp8=True)
+    finally:
+        O.quantize_rows_fp8, O.quantize_tensor_fp8, O.bf16_round = qr, qt, br
+    assert np.array_equal(same, exact), "fp8 step switch changed more than the blocks' Linear layers"
+    assert len(seen) == 6 * nb, seen
+    q8 = O.step(lat, t, ctx, mw, H, fp8=True)
+    assert not np.array_equal(q8, exact)
+

@@ -59,6 +59,8 @@ MUTATIONS = {
                                 "return linear(gelu_tanh(lin(hmod, w1, b1)), w2, b2)"),
     "fp8 flag dropped for CA": ("wkv_img=wts.get(\"ca_wkv_img\"), bkv_img=wts.get(\"ca_bkv_img\"),\n                             fp8=fp8)",
                                 "wkv_img=wts.get(\"ca_wkv_img\"), bkv_img=wts.get(\"ca_bkv_img\"))"),
+    "fp8 flag not passed to the blocks": ("x = block(x, m, wts, ctx, heads, eps, img=img, fp8=fp8)",
+                                          "x = block(x, m, wts, ctx, heads, eps, img=img)"),
     "head split strided": ("k[:, h * hd:(h + 1) * hd],\n                                     v[:, h * hd:(h + 1) * hd])",
                            "k[:, h::heads],\n                                     v[:, h::heads])"),
 }
