@@ -303,6 +303,39 @@ int wan_dit_block_fp8_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int 
                           const void *ctx, const void *img_ctx, void *ws, size_t ws_bytes,
                           void *stream);
 
+/* ---- FP8 step and sampler -------------------------------------------------- */
+/* The step and the sampler of the bf16 model with every block in FP8 as in
+ * wan_dit_block_fp8_fwd (patchify, t-MLP, image MLP, cross-attention K/V,
+ * attention and head unchanged).  bf16 configurations only. */
+
+/* Bytes of a model's packed FP8 block weights: n_blocks regions of
+ * wan_block_fp8_bytes each (0 for an invalid or float32 cfg). */
+size_t wan_model_fp8_bytes(const wan_cfg_t *cfg);
+
+/* Quantise every block of w (bf16, device) into qbuf (device, 256-byte aligned,
+ * at least wan_model_fp8_bytes; block i at i * wan_block_fp8_bytes). */
+int wan_quantize_model_fp8(const wan_cfg_t *cfg, const wan_model_weights_t *w, void *qbuf,
+                           size_t qbuf_bytes, void *stream);
+
+/* Workspace of wan_dit_step_fp8_fwd (sampler = 0) or wan_sample_fp8_fwd
+ * (sampler = 1); 0 for an invalid cfg / shape. */
+size_t wan_fp8_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, int W8, int sampler);
+
+/* wan_dit_step_fwd with FP8 blocks: arguments as there, plus qbuf from
+ * wan_quantize_model_fp8 for the same w (the blocks' six quantised weight
+ * pointers are not read and may be NULL).  B * L * max(d, ffn) < 2^31. */
+int wan_dit_step_fp8_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, int B,
+                         int lat_f, int H8, int W8, const void *ctx, const void *clip_feat,
+                         const wan_model_weights_t *w, const void *qbuf, float *out, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* wan_sample_fwd with FP8 blocks (cross-attention K/V from the bf16 cache of
+ * wan_kv_cache_fwd): arguments as there, plus qbuf as above. */
+int wan_sample_fp8_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, int H8, int W8,
+                       int n_steps, int guided, float scale, const void *kv_cache, size_t cache_bytes,
+                       const wan_model_weights_t *w, const void *qbuf, void *ws, size_t ws_bytes,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

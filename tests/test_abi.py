@@ -136,3 +136,26 @@ def test_fp8_block_invalid_arguments(W):
                                    None) == -2                                     # qbuf misaligned
     assert L.wan_dit_block_fp8_fwd(C.byref(c), *args, dummy, dummy, None, dummy, 1 << 40, None) == -1
 
+
+
+def test_fp8_model_sizes_and_invalid_arguments(W):
+    c = _cfg(W)   # 3 blocks
+    assert W.model_fp8_bytes(c) == 3 * W.block_fp8_bytes(c)
+    assert W.model_fp8_bytes(_cfg(W, dtype="f32", heads=4)) == 0
+    step = W.fp8_workspace_bytes(c, 2, 3, 8, 12)
+    samp = W.fp8_workspace_bytes(c, 2, 3, 8, 12, True)
+    assert step > W.workspace_bytes(c, 2, 3, 8, 12) and samp > step
+    assert W.fp8_workspace_bytes(c, 2, 3, 7, 12) == 0                 # odd H8
+    L = W.lib()
+    cf = _cfg(W, dtype="f32", heads=4)
+    dummy = C.c_void_p(256)   # never dereferenced: every call below fails validation first
+    mw, keep = W.model_weights({"patch_w": None, "patch_b": None, "tmlp": {"w1": None, "b1": None,
+                                "w2": None, "b2": None}, "head_w": None, "head_b": None}, [])
+    assert L.wan_quantize_model_fp8(C.byref(cf), C.byref(mw), dummy, 1 << 30, None) == -3
+    assert L.wan_quantize_model_fp8(C.byref(c), C.byref(mw), dummy, 1 << 30, None) == -1
+    assert L.wan_dit_step_fp8_fwd(C.byref(cf), dummy, dummy, 2, 3, 8, 12, dummy, None, C.byref(mw),
+                                  dummy, dummy, dummy, 1 << 40, None) == -3
+    assert L.wan_dit_step_fp8_fwd(C.byref(c), dummy, dummy, 2, 3, 8, 12, dummy, None, C.byref(mw),
+                                  None, dummy, dummy, 1 << 40, None) == -1
+    assert L.wan_sample_fp8_fwd(C.byref(c), dummy, 2, 3, 8, 12, 0, 1, 5.0, dummy, 1 << 30,
+                                C.byref(mw), dummy, dummy, 1 << 40, None) == -2   # zero steps

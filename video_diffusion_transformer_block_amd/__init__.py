@@ -8,6 +8,8 @@ video_diffusion_transformer_block_amd.build`` (or ``__graft_entry__.build()``).
 from . import binding  # noqa: F401
 from .binding import (Cfg, WanError, attention_fwd, block_fp8_bytes, block_fp8_workspace_bytes,  # noqa: F401
                       block_weights, dit_block_fp8_fwd, dit_block_fwd, quantize_block_fp8,
+                      model_fp8_bytes, fp8_workspace_bytes, quantize_model_fp8, dit_step_fp8_fwd,
+                      sample_fp8_fwd,
                       dit_step_cached_fwd, dit_step_fwd, euler_fwd, i2v_mask, kv_cache_bytes,
                       kv_cache_fwd, lib, linear_fp8_fwd, linear_fwd, make_cfg, model_weights, sample_fwd,
                       quantize_rows_fp8, quantize_tensor_fp8, sample_workspace_bytes, status_str,

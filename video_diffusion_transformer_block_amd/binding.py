@@ -24,9 +24,12 @@ EXPORTS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_by
            "wan_i2v_mask", "wan_attention_fwd", "wan_linear_fwd", "wan_kv_cache_fwd",
            "wan_dit_step_cached_fwd", "wan_euler_fwd", "wan_sample_fwd", "wan_quantize_rows_fp8",
            "wan_quantize_tensor_fp8", "wan_linear_fp8_fwd", "wan_block_fp8_bytes",
-           "wan_quantize_block_fp8", "wan_block_fp8_workspace_bytes", "wan_dit_block_fp8_fwd")
+           "wan_quantize_block_fp8", "wan_block_fp8_workspace_bytes", "wan_dit_block_fp8_fwd",
+           "wan_model_fp8_bytes", "wan_quantize_model_fp8", "wan_fp8_workspace_bytes",
+           "wan_dit_step_fp8_fwd", "wan_sample_fp8_fwd")
 _SIZE_FNS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
-             "wan_block_fp8_bytes", "wan_block_fp8_workspace_bytes")
+             "wan_block_fp8_bytes", "wan_block_fp8_workspace_bytes", "wan_model_fp8_bytes",
+             "wan_fp8_workspace_bytes")
 
 
 class WanError(RuntimeError):
@@ -102,6 +105,13 @@ def lib() -> C.CDLL:
         L.wan_block_fp8_workspace_bytes.argtypes = [C.POINTER(Cfg), i, i, i, i]
         L.wan_dit_block_fp8_fwd.argtypes = [C.POINTER(Cfg), vp, i, i, i, i, vp, C.POINTER(BlockW), vp,
                                             vp, vp, vp, sz, vp]
+        L.wan_model_fp8_bytes.argtypes = [C.POINTER(Cfg)]
+        L.wan_quantize_model_fp8.argtypes = [C.POINTER(Cfg), C.POINTER(ModelW), vp, sz, vp]
+        L.wan_fp8_workspace_bytes.argtypes = [C.POINTER(Cfg), i, i, i, i, i]
+        L.wan_dit_step_fp8_fwd.argtypes = [C.POINTER(Cfg), vp, vp, i, i, i, i, vp, vp, C.POINTER(ModelW),
+                                           vp, vp, vp, sz, vp]
+        L.wan_sample_fp8_fwd.argtypes = [C.POINTER(Cfg), vp, i, i, i, i, i, i, C.c_float, vp, sz,
+                                         C.POINTER(ModelW), vp, vp, sz, vp]
         for n in EXPORTS:
             if n in _SIZE_FNS:
                 getattr(L, n).restype = sz
@@ -298,3 +308,36 @@ def dit_block_fp8_fwd(cfg: Cfg, x: torch.Tensor, B: int, lat_f: int, Hp: int, Wp
            lib().wan_dit_block_fp8_fwd(C.byref(cfg), _p(x), B, lat_f, Hp, Wp, _p(mod), C.byref(bw),
                                        _p(qbuf), _p(ctx), _p(img_ctx), _p(ws), _nbytes(ws),
                                        _stream(stream)))
+
+
+def model_fp8_bytes(cfg: Cfg) -> int:
+    return int(lib().wan_model_fp8_bytes(C.byref(cfg)))
+
+
+def fp8_workspace_bytes(cfg: Cfg, B: int, lat_f: int, H8: int, W8: int, sampler: bool = False) -> int:
+    return int(lib().wan_fp8_workspace_bytes(C.byref(cfg), B, lat_f, H8, W8, int(bool(sampler))))
+
+
+def quantize_model_fp8(cfg: Cfg, mw: ModelW, qbuf: torch.Tensor, stream=None):
+    _check("wan_quantize_model_fp8", lib().wan_quantize_model_fp8(C.byref(cfg), C.byref(mw), _p(qbuf),
+                                                                  _nbytes(qbuf), _stream(stream)))
+
+
+def dit_step_fp8_fwd(cfg: Cfg, latent: torch.Tensor, t: torch.Tensor, ctx: torch.Tensor,
+                     clip: Optional[torch.Tensor], mw: ModelW, qbuf: torch.Tensor, out: torch.Tensor,
+                     ws: torch.Tensor, stream=None):
+    B, _, F, H8, W8 = latent.shape
+    _check("wan_dit_step_fp8_fwd",
+           lib().wan_dit_step_fp8_fwd(C.byref(cfg), _p(latent), _p(t), B, F, H8, W8, _p(ctx), _p(clip),
+                                      C.byref(mw), _p(qbuf), _p(out), _p(ws), _nbytes(ws),
+                                      _stream(stream)))
+
+
+def sample_fp8_fwd(cfg: Cfg, latent: torch.Tensor, n_steps: int, cache: torch.Tensor, mw: ModelW,
+                   qbuf: torch.Tensor, ws: torch.Tensor, guided: bool = False, scale: float = 1.0,
+                   stream=None):
+    B, _, F, H8, W8 = latent.shape
+    _check("wan_sample_fp8_fwd",
+           lib().wan_sample_fp8_fwd(C.byref(cfg), _p(latent), B, F, H8, W8, n_steps, int(bool(guided)),
+                                    float(scale), _p(cache), _nbytes(cache), C.byref(mw), _p(qbuf),
+                                    _p(ws), _nbytes(ws), _stream(stream)))

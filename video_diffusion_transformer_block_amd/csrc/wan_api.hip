@@ -385,8 +385,10 @@ int image_context(const wan_cfg_t &c, int B, const void *clip, const wan_model_w
   return WAN_OK;
 }
 
-// every weight the step reads (image MLP only when `need_img`)
-int check_model_weights(const wan_cfg_t &c, const wan_model_weights_t *w, bool need_img) {
+// every weight the step reads (image MLP only when `need_img`; with fp8 the
+// blocks' six quantised weights are not read)
+int check_model_weights(const wan_cfg_t &c, const wan_model_weights_t *w, bool need_img,
+                        bool fp8 = false) {
   if (!w) return WAN_ERR_NULL;
   if (!w->patch_w || !w->patch_b || !w->head_w || !w->head_b || !w->tmlp.w1 || !w->tmlp.b1 ||
       !w->tmlp.w2 || !w->tmlp.b2)
@@ -394,17 +396,32 @@ int check_model_weights(const wan_cfg_t &c, const wan_model_weights_t *w, bool n
   if (c.n_blocks > 0 && !w->blocks) return WAN_ERR_NULL;
   int st;
   for (int i = 0; i < c.n_blocks; ++i)
-    if ((st = check_block_weights(c, &w->blocks[i]))) return st;
+    if ((st = check_block_weights(c, &w->blocks[i], fp8))) return st;
   if (need_img && (!w->img_w1 || !w->img_b1 || !w->img_w2 || !w->img_b2 || !w->img_w3 || !w->img_b3))
     return WAN_ERR_CONFIG;
   return WAN_OK;
 }
 
+// the FP8 operands of block i of a model's packed weights (n_blocks regions)
+Fp8Ptrs fp8_block_ptrs(const wan_cfg_t &c, const char *qbuf, int i, char *ws, const Layout &y) {
+  const Fp8Layout ql = fp8_layout(c);
+  const char *qb = qbuf + (size_t)i * ql.total;
+  Fp8Ptrs q8;
+  for (int k = 0; k < 6; ++k) q8.w[k] = (const uint8_t *)(qb + ql.w[k]);
+  q8.sc = (const float *)(qb + ql.sc);
+  q8.aq = (uint8_t *)ws + y.aq;
+  q8.as = (float *)(ws + y.as);
+  return q8;
+}
+
 // patchify -> t-MLP -> (image context) -> blocks -> head + unpatchify.  With
-// `cache` the blocks read their cross-attention K/V from it (ctx / clip unused).
+// `cache` the blocks read their cross-attention K/V from it (ctx / clip unused);
+// with `q8buf` (a model's packed FP8 weights) every block runs its Linear
+// layers in FP8.
 int step_run(const wan_cfg_t &c, const float *latent, const float *t, int B, int lat_f, int H8,
              int W8, const void *ctx, const void *clip, const char *cache,
-             const wan_model_weights_t &w, float *out, char *wsb, const Layout &y, hipStream_t s) {
+             const wan_model_weights_t &w, float *out, char *wsb, const Layout &y, hipStream_t s,
+             const char *q8buf = nullptr) {
   const int d = c.dim, f32 = c.dtype == WAN_F32;
   const int Hp = H8 / 2, Wp = W8 / 2;
   const long L = (long)lat_f * Hp * Wp;
@@ -434,7 +451,9 @@ int step_run(const wan_cfg_t &c, const float *latent, const float *t, int B, int
       kp = {base + kl.kc, base + kl.vtc, base + kl.ki, base + kl.vti};
       pk = &kp;
     }
-    st = block_run(c, x, B, L, mod, w.blocks[i], ctx, img, pk, wsb, y, s);
+    Fp8Ptrs q8;
+    if (q8buf) q8 = fp8_block_ptrs(c, q8buf, i, wsb, y);
+    st = block_run(c, x, B, L, mod, w.blocks[i], ctx, img, pk, wsb, y, s, q8buf ? &q8 : nullptr);
     if (st) return st;
   }
   WAN_TRY(launch_head_unpatchify(x, B, lat_f, Hp, Wp, d, w.head_w, w.head_b, c.out_ch, out, f32, s));
@@ -451,6 +470,26 @@ size_t sample_extra(int B, int out_ch, long plane, size_t *t_off, size_t *v_off,
   *t_off = base;
   *v_off = *t_off + up((size_t)B * 4, ALIGN);
   return *v_off + up((size_t)B * out_ch * plane * 4, ALIGN);
+}
+
+// n_steps Euler steps of the cached step (see wan_sample_fwd); q8buf: FP8 blocks
+int sample_run(const wan_cfg_t &c, float *latent, int B, int lat_f, int H8, int W8, int n_steps,
+               int guided, float scale, const char *kv_cache, const wan_model_weights_t &w, char *wsb,
+               const Layout &y, size_t t_off, size_t v_off, hipStream_t s, const char *q8buf = nullptr) {
+  float *tb = reinterpret_cast<float *>(wsb + t_off);
+  float *vel = reinterpret_cast<float *>(wsb + v_off);
+  const long plane = (long)lat_f * H8 * W8;
+  // flow time tau_k = k / n from noise (0) to data (1); the model's timestep
+  // input is 1000 tau_k; one Euler step of length 1/n per evaluation
+  const float dt = (float)(1.0 / n_steps);
+  for (int k = 0; k < n_steps; ++k) {
+    WAN_TRY(launch_fill(tb, B, (float)(1000.0 * k / n_steps), s));
+    int st = step_run(c, latent, tb, B, lat_f, H8, W8, nullptr, nullptr, kv_cache, w, vel, wsb, y, s,
+                      q8buf);
+    if (st) return st;
+    WAN_TRY(launch_euler(latent, vel, B, c.in_ch, c.out_ch, plane, dt, guided, scale, s));
+  }
+  return WAN_OK;
 }
 
 }  // namespace
@@ -619,21 +658,8 @@ int wan_sample_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, int H8
   Layout y = make_layout(*cfg, B, L, true);
   size_t t_off, v_off;
   if (ws_bytes < sample_extra(B, cfg->out_ch, plane, &t_off, &v_off, y.total)) return WAN_ERR_WORKSPACE;
-  hipStream_t s = S(stream);
-  char *wsb = (char *)ws;
-  float *tb = reinterpret_cast<float *>(wsb + t_off);
-  float *vel = reinterpret_cast<float *>(wsb + v_off);
-  // flow time tau_k = k / n from noise (0) to data (1); the model's timestep
-  // input is 1000 tau_k; one Euler step of length 1/n per evaluation
-  const float dt = (float)(1.0 / n_steps);
-  for (int k = 0; k < n_steps; ++k) {
-    WAN_TRY(launch_fill(tb, B, (float)(1000.0 * k / n_steps), s));
-    st = step_run(*cfg, latent, tb, B, lat_f, H8, W8, nullptr, nullptr, (const char *)kv_cache, *w,
-                  vel, wsb, y, s);
-    if (st) return st;
-    WAN_TRY(launch_euler(latent, vel, B, cfg->in_ch, cfg->out_ch, plane, dt, guided, scale, s));
-  }
-  return WAN_OK;
+  return sample_run(*cfg, latent, B, lat_f, H8, W8, n_steps, guided, scale, (const char *)kv_cache, *w,
+                    (char *)ws, y, t_off, v_off, S(stream));
 }
 
 int wan_i2v_mask(const uint8_t *frame_mask, int n_frames, int lat_f, int H8, int W8, float *out) {
@@ -755,6 +781,80 @@ int wan_dit_block_fp8_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int 
   q8.aq = (uint8_t *)ws + y.aq;
   q8.as = (float *)((char *)ws + y.as);
   return block_run(*cfg, x, B, L, mod, *w, ctx, img_ctx, nullptr, (char *)ws, y, S(stream), &q8);
+}
+
+size_t wan_model_fp8_bytes(const wan_cfg_t *cfg) {
+  if (check_cfg(cfg) != WAN_OK || cfg->dtype != WAN_BF16) return 0;
+  return fp8_layout(*cfg).total * (size_t)cfg->n_blocks;
+}
+
+int wan_quantize_model_fp8(const wan_cfg_t *cfg, const wan_model_weights_t *w, void *qbuf,
+                           size_t qbuf_bytes, void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (cfg->dtype != WAN_BF16) return WAN_ERR_DTYPE;
+  if (!w || (!qbuf && cfg->n_blocks > 0) || (cfg->n_blocks > 0 && !w->blocks)) return WAN_ERR_NULL;
+  const size_t per = fp8_layout(*cfg).total;
+  if (qbuf_bytes < per * (size_t)cfg->n_blocks) return WAN_ERR_WORKSPACE;
+  for (int i = 0; i < cfg->n_blocks; ++i)
+    if ((st = wan_quantize_block_fp8(cfg, &w->blocks[i], (char *)qbuf + (size_t)i * per, per, stream)))
+      return st;
+  return WAN_OK;
+}
+
+size_t wan_fp8_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, int W8, int sampler) {
+  if (check_cfg(cfg) != WAN_OK || cfg->dtype != WAN_BF16) return 0;
+  if (check_step_dims(B, lat_f, H8, W8) != WAN_OK) return 0;
+  const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
+  const size_t base = make_layout(*cfg, B, L, true, true).total;
+  if (!sampler) return base;
+  size_t t_off, v_off;
+  return sample_extra(B, cfg->out_ch, (long)lat_f * H8 * W8, &t_off, &v_off, base);
+}
+
+int wan_dit_step_fp8_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, int B, int lat_f,
+                         int H8, int W8, const void *ctx, const void *clip_feat,
+                         const wan_model_weights_t *w, const void *qbuf, float *out, void *ws,
+                         size_t ws_bytes, void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (cfg->dtype != WAN_BF16) return WAN_ERR_DTYPE;
+  if (!latent || !t || !ctx || !w || !out || !ws || (!qbuf && cfg->n_blocks > 0)) return WAN_ERR_NULL;
+  if ((uintptr_t)qbuf % ALIGN) return WAN_ERR_SHAPE;
+  if ((st = check_step_dims(B, lat_f, H8, W8))) return st;
+  const bool i2v = cfg->img_len > 0;
+  if ((st = check_model_weights(*cfg, w, i2v, true))) return st;
+  if (i2v != (clip_feat != nullptr)) return WAN_ERR_CONFIG;
+  const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
+  if ((long)B * L * (cfg->ffn > cfg->dim ? cfg->ffn : cfg->dim) >= (1L << 31)) return WAN_ERR_SHAPE;
+  Layout y = make_layout(*cfg, B, L, true, true);
+  if (ws_bytes < y.total) return WAN_ERR_WORKSPACE;
+  return step_run(*cfg, latent, t, B, lat_f, H8, W8, ctx, clip_feat, nullptr, *w, out, (char *)ws, y,
+                  S(stream), (const char *)qbuf);
+}
+
+int wan_sample_fp8_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, int H8, int W8,
+                       int n_steps, int guided, float scale, const void *kv_cache, size_t cache_bytes,
+                       const wan_model_weights_t *w, const void *qbuf, void *ws, size_t ws_bytes,
+                       void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (cfg->dtype != WAN_BF16) return WAN_ERR_DTYPE;
+  if (!latent || !w || !ws || ((!kv_cache || !qbuf) && cfg->n_blocks > 0)) return WAN_ERR_NULL;
+  if ((uintptr_t)qbuf % ALIGN) return WAN_ERR_SHAPE;
+  if ((st = check_step_dims(B, lat_f, H8, W8))) return st;
+  if (n_steps <= 0 || (guided && B != 2) || !isfinite(scale)) return WAN_ERR_SHAPE;
+  if (cfg->in_ch < cfg->out_ch) return WAN_ERR_SHAPE;
+  if ((st = check_model_weights(*cfg, w, false, true))) return st;
+  if (cache_bytes < kv_layout(*cfg, B).per_block * (size_t)cfg->n_blocks) return WAN_ERR_WORKSPACE;
+  const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
+  if ((long)B * L * (cfg->ffn > cfg->dim ? cfg->ffn : cfg->dim) >= (1L << 31)) return WAN_ERR_SHAPE;
+  const long plane = (long)lat_f * H8 * W8;
+  Layout y = make_layout(*cfg, B, L, true, true);
+  size_t t_off, v_off;
+  if (ws_bytes < sample_extra(B, cfg->out_ch, plane, &t_off, &v_off, y.total)) return WAN_ERR_WORKSPACE;
+  return sample_run(*cfg, latent, B, lat_f, H8, W8, n_steps, guided, scale, (const char *)kv_cache, *w,
+                    (char *)ws, y, t_off, v_off, S(stream), (const char *)qbuf);
 }
 
 int wan_linear_fwd(const void *x, const void *w, const void *b, void *y, int M, int N, int K,
