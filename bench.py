@@ -176,7 +176,18 @@ def sampler_bench(n_steps: int, warmup: int):
     plain_ms = timed(plain)
     if not bool(torch.isfinite(lat).all()):
         raise RuntimeError("non-finite sample")
-    per_c, per_p = cached_ms / n_steps, plain_ms / n_steps
+    # the same cached sampler with every block in FP8 (weights quantised once, outside the timing)
+    qbuf = torch.empty(W.model_fp8_bytes(cfg), dtype=torch.uint8, device="cuda")
+    quant_ms = timed(lambda: W.quantize_model_fp8(cfg, mws, qbuf, stream))
+    ws8 = torch.empty(W.fp8_workspace_bytes(cfg, B, work.lat_f, work.lat_h, work.lat_w, True),
+                      dtype=torch.uint8, device="cuda")
+    lat = lat0.clone()
+    W.sample_fp8_fwd(cfg, lat, warmup, cache, mws, qbuf, ws8, True, 5.0, stream)
+    lat = lat0.clone()
+    fp8_ms = timed(lambda: W.sample_fp8_fwd(cfg, lat, n_steps, cache, mws, qbuf, ws8, True, 5.0, stream))
+    if not bool(torch.isfinite(lat).all()):
+        raise RuntimeError("non-finite FP8 sample")
+    per_c, per_p, per_8 = cached_ms / n_steps, plain_ms / n_steps, fp8_ms / n_steps
     print(json.dumps({
         "sampler": "wan1.3b-480p guidance pair (30 blocks, B=2, L=32760, 512 text tokens)",
         "steps": n_steps, "guidance": 5.0,
@@ -184,7 +195,10 @@ def sampler_bench(n_steps: int, warmup: int):
         "kv_cache_fill_ms": round(fill_ms, 3),
         "saving_per_step_ms": round(per_p - per_c, 3),
         "latent_tokens_per_s_cached": round(B * L / (per_c * 1e-3), 1),
-        "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latent and text)",
+        "ms_per_step_cached_fp8_blocks": round(per_8, 3), "fp8_speedup": round(per_c / per_8, 4),
+        "fp8_weight_quantisation_ms": round(quant_ms, 3),
+        "dtype": "bf16 (and fp8 e4m3 block Linear layers)",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latent and text)",
     }), flush=True)
 
 
