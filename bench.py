@@ -53,6 +53,8 @@ def attn_sources_sha256() -> str:
 
 
 def attn_traffic_bytes():
+    """Calibrated HBM bytes of one self-attention launch of the 1.3B 480P
+    workload (the counters were taken on that shape only), or None."""
     t = ATTN_TRAFFIC
     if attn_sources_sha256() != t["sources_sha256"]:
         return None
@@ -471,7 +473,8 @@ def main():
     tokens_s = B * L / (ms * 1e-3)
 
     out = {
-        "metric": "DiT block tokens/s + attn TFLOP/s (% bf16 MFMA peak), 1.3B @ 480P L=32760",
+        "metric": "DiT block tokens/s + attn TFLOP/s (% bf16 MFMA peak), 1.3B @ 480P L=32760"
+                  if args.config == 2 else f"DiT block tokens/s + attn TFLOP/s (% bf16 MFMA peak), {work.name}",
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -491,7 +494,7 @@ def main():
         "block_frac_of_peak": round(block_tf / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "k_attn_bf16", "achieved": round(attn_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic_bytes(),
+                     "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic_bytes() if args.config == 2 else None,
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 counters, copy-calibrated)",
                      "algorithmic_bytes": 4 * B * L * d * 2,
                      "launch_ms": round(attn_ms, 4),
