@@ -47,11 +47,20 @@ __global__ __launch_bounds__(256) void k_gemv(const T *__restrict__ W, const T *
 #pragma unroll
       for (int u = 0; u < VW; ++u) wv[u] = k0 + u < K ? wr[k0 + u] : from_f<T>(0.f);
     }
+    const bool full = k0 + VW <= K && (K & 3) == 0;
     for (int b = 0; b < B; ++b) {
       const float *xb = x + (long)b * K + k0;
+      float xv[VW];
+      if (full) {   // x rows are 16-byte aligned (K % 4 == 0): vector loads
+#pragma unroll
+        for (int u = 0; u < VW; u += 4) *reinterpret_cast<float4 *>(xv + u) = *reinterpret_cast<const float4 *>(xb + u);
+      } else {
+#pragma unroll
+        for (int u = 0; u < VW; ++u) xv[u] = k0 + u < K ? xb[u] : 0.f;
+      }
       float s = 0.f;
 #pragma unroll
-      for (int u = 0; u < VW; ++u) s = fmaf(to_f<T>(wv[u]), k0 + u < K ? xb[u] : 0.f, s);
+      for (int u = 0; u < VW; ++u) s = fmaf(to_f<T>(wv[u]), xv[u], s);
       acc[b] += s;
     }
   }
