@@ -80,6 +80,19 @@ READINGS = {
                       "quantised as one [3d, d] tensor, SA out, CA query, CA out, FFN up, FFN "
                       "down); text / image K/V, LayerNorm, attention, GELU and the residual "
                       "stay exact",
+    "R25 8-bit attention": "[Note, Infra / 推理优化: 8-bit FlashAttention, Int8 for S = QK^T, FP8 "
+                           "for O = PV, FP32 accumulation across key blocks]: per (batch, head) "
+                           "q is quantised per token (its hd features) and k per block of 64 keys "
+                           "(block b = keys 64b .. 64b+63, the last block ragged) to symmetric "
+                           "Int8: inv = 127 / amax (float32 division), code = round-half-even of "
+                           "clamp(x * inv (float32), +-127), scale = amax / 127, an all-zero group "
+                           "scale 1; v is quantised per channel (one feature over the Lk keys) to "
+                           "E4M3 by R22's rule; S = (q8 . k8) sq sk (exact integer dot product); "
+                           "the probabilities are scaled so that the row max maps to 2^7 and "
+                           "rounded to E4M3 (nearest even); O = sv * (sum_j P8_j v8_j) / sum_j "
+                           "P8_j: the normaliser adds the rounded probabilities, so O is a convex "
+                           "combination of the dequantised values; inputs are the bf16 q, k, v "
+                           "the block holds",
 }
 
 
@@ -537,3 +550,93 @@ def linear_fp8(x, w, b=None):
     qw, sw = quantize_tensor_fp8(w)
     return linear_fp8_q(x, qw, sw, b)
 
+
+# ---------------------------------------------------------------------------
+# 8-bit attention (R25)  [Note, Infra / 推理优化: 8-bit FlashAttention -- Int8
+# for S = QK^T, FP8 for O = PV, FP32 accumulation across blocks]
+
+I8_MAX = 127.0
+ATTN8_KBLOCK = 64        # keys per K quantisation block
+ATTN8_PSCALE = 128.0     # the row max of the probabilities maps to 2^7 before rounding
+
+
+def _i8_scale_f32(amax):
+    """(inv, scale) in float32: inv = 127 / amax, scale = amax / 127; amax = 0
+    gives (1, 1)."""
+    amax = np.float32(amax)
+    if amax == 0:
+        return np.float32(1.0), np.float32(1.0)
+    return np.float32(I8_MAX) / amax, amax / np.float32(I8_MAX)
+
+
+def quantize_int8(x):
+    """Symmetric Int8 quantisation of x as one group (R25): (codes, scale) with
+    x ~= codes * scale; the code is decided in float32 (x * inv, clamp to
+    +-127, round half to even)."""
+    x32 = np.asarray(x, np.float32)
+    inv, s = _i8_scale_f32(np.max(np.abs(x32)) if x32.size else 0.0)
+    v = np.clip(x32 * np.float32(inv), np.float32(-I8_MAX), np.float32(I8_MAX))
+    return np.rint(v.astype(F64)), F64(s)
+
+
+def quantize_q_int8(q):
+    """Per-token Int8 quantisation of one head's q [L, hd] (R25): (codes [L, hd],
+    scale [L])."""
+    q = np.asarray(q, np.float32)
+    codes = np.empty(q.shape, F64)
+    sc = np.empty(q.shape[0], F64)
+    for i in range(q.shape[0]):
+        codes[i], sc[i] = quantize_int8(q[i])
+    return codes, sc
+
+
+def quantize_k_int8(k, block: int = ATTN8_KBLOCK):
+    """Per-block Int8 quantisation of one head's k [L, hd] (R25): blocks of
+    ``block`` consecutive keys share a scale.  Returns (codes [L, hd], scale
+    of each block [ceil(L / block)])."""
+    k = np.asarray(k, np.float32)
+    nb = (k.shape[0] + block - 1) // block
+    codes = np.empty(k.shape, F64)
+    sc = np.empty(nb, F64)
+    for bi in range(nb):
+        codes[bi * block:(bi + 1) * block], sc[bi] = quantize_int8(k[bi * block:(bi + 1) * block])
+    return codes, sc
+
+
+def quantize_v_fp8(v):
+    """Per-channel E4M3 quantisation of one head's v [L, hd] (R25 with R22's
+    rule): each feature column gets its own scale.  Returns (codes [L, hd],
+    scale [hd])."""
+    q, sc = quantize_rows_fp8(np.asarray(v, np.float32).T)
+    return q.T, sc
+
+
+def attention_8bit(q, k, v, q_scaled: bool = False):
+    """One head of the 8-bit attention (R25).  q [Lq, hd], k / v [Lk, hd] hold
+    bf16 values.  q_scaled: q was multiplied by log2(e)/sqrt(hd) beforehand
+    (the score is then in log2 units) -- the same attention of the unscaled q.
+    Steps: quantise q per token, k per 64-key block (Int8) and v per channel
+    (E4M3); integer scores times the two scales; probabilities relative to the
+    row max, times 2^7, rounded to E4M3; PV on the rounded values, normalised
+    by their sum, times the channel scales."""
+    q8, sq = quantize_q_int8(q)
+    k8, sk = quantize_k_int8(k)
+    v8, sv = quantize_v_fp8(v)
+    skey = np.repeat(sk, ATTN8_KBLOCK)[:k8.shape[0]]
+    S = (q8 @ k8.T) * sq[:, None] * skey[None, :]
+    if q_scaled:
+        P = ATTN8_PSCALE * np.exp2(S - S.max(axis=1, keepdims=True))
+    else:
+        S = S / math.sqrt(q8.shape[1])
+        P = ATTN8_PSCALE * np.exp(S - S.max(axis=1, keepdims=True))
+    P8 = e4m3_round(P)
+    return (P8 @ v8) * sv[None, :] / P8.sum(axis=1, keepdims=True)
+
+
+def multihead_8bit(q, k, v, heads: int, q_scaled: bool = False):
+    """attention_8bit per head (head h = columns h*hd .. (h+1)*hd) of one
+    batch sample, concatenated."""
+    hd = q.shape[1] // heads
+    return np.concatenate([attention_8bit(q[:, h * hd:(h + 1) * hd], k[:, h * hd:(h + 1) * hd],
+                                          v[:, h * hd:(h + 1) * hd], q_scaled)
+                           for h in range(heads)], axis=1)

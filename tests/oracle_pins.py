@@ -616,3 +616,128 @@ def pin_fp8_step(O):
     q8 = O.step(lat, t, ctx, mw, H, fp8=True)
     assert not np.array_equal(q8, exact)
 
+
+
+# ---------------------------------------------------------------- 8-bit attention
+def pin_int8_quant(O):
+    """Symmetric Int8 quantisation: hand-computed codes (ties to even), the
+    group max mapping to +-127, the half-step error bound, the all-zero group,
+    and the block / channel groupings of K and V (distinct magnitudes per
+    block or channel, a ragged last K block)."""
+    x = np.array([127.0, 0.5, 1.5, 2.5, -3.5, 126.5, -127.0, 63.25], np.float32)
+    q, s = O.quantize_int8(x)                       # amax 127: inv = scale = 1
+    _close(q, [127, 0, 2, 2, -4, 126, -127, 63], 0, "Int8 codes, ties to even")
+    assert s == 1.0
+    q, s = O.quantize_int8(np.zeros(5, np.float32))
+    assert s == 1.0 and not q.any(), "zero group"
+    r = _rng(60)
+    for mag in (1e-3, 1.0, 37.0, 3e4):
+        x = (r.standard_normal(500) * mag).astype(np.float32)
+        q, s = O.quantize_int8(x)
+        assert np.max(np.abs(q)) == 127 and np.all(q == np.round(q))
+        assert np.isclose(s, np.max(np.abs(x)) / 127.0, rtol=1e-6)
+        assert np.all(np.abs(x / s - q) <= 0.5 + 1e-5), ("half-step bound", mag)
+    # per-token q
+    qm = (r.standard_normal((4, 16)) * np.array([[1e-2], [1.0], [50.0], [0.0]])).astype(np.float32)
+    qc, qs = O.quantize_q_int8(qm)
+    for i in range(3):
+        assert np.isclose(qs[i], np.max(np.abs(qm[i])) / 127.0, rtol=1e-6) and np.max(np.abs(qc[i])) == 127
+    assert qs[3] == 1.0 and not qc[3].any()
+    # per-64-key-block k: block b has magnitude 10^b; key 149 (ragged block 2) is the largest
+    k = np.concatenate([r.standard_normal((64, 16)), r.standard_normal((64, 16)) * 10,
+                        r.standard_normal((22, 16)) * 100]).astype(np.float32)
+    k[149, 3] = 1e4
+    kc, ks = O.quantize_k_int8(k)
+    assert ks.shape == (3,)
+    for b, (lo, hi) in enumerate([(0, 64), (64, 128), (128, 150)]):
+        assert np.isclose(ks[b], np.max(np.abs(k[lo:hi])) / 127.0, rtol=1e-6), ("block scale", b)
+        assert np.max(np.abs(kc[lo:hi])) == 127
+    assert kc[149, 3] == 127
+    # per-channel v: column c has magnitude 4^c
+    v = (r.standard_normal((90, 6)) * 4.0 ** np.arange(6)).astype(np.float32)
+    vc, vs = O.quantize_v_fp8(v)
+    assert vc.shape == v.shape and vs.shape == (6,)
+    for c in range(6):
+        assert np.isclose(vs[c], np.max(np.abs(v[:, c])) / 448.0, rtol=1e-6) and np.max(np.abs(vc[:, c])) == 448
+
+
+def _brute_attention_8bit(q, k, v, q_scaled):
+    """The 8-bit attention written out with loops: Int8 by Python's round
+    (half to even) of float32 products, E4M3 by torch's float8_e4m3fn."""
+    f32 = np.float32
+    Lq, hd = q.shape
+    Lk = k.shape[0]
+
+    def i8(vals):
+        amax = max(abs(float(t)) for t in vals)
+        if amax == 0:
+            return [0] * len(vals), 1.0
+        inv, s = f32(127) / f32(amax), f32(amax) / f32(127)
+        return [round(float(min(max(f32(t) * inv, f32(-127)), f32(127)))) for t in vals], float(s)
+
+    def e4m3(t):
+        return float(torch.tensor([float(t)], dtype=torch.float64).to(torch.float8_e4m3fn).to(torch.float64)[0])
+
+    qc, qs = [], []
+    for i in range(Lq):
+        c, s = i8(list(q[i]))
+        qc.append(c)
+        qs.append(s)
+    kc, ks = [None] * Lk, [0.0] * Lk
+    for b0 in range(0, Lk, 64):
+        rows = list(range(b0, min(b0 + 64, Lk)))
+        c, s = i8([k[j][d] for j in rows for d in range(hd)])
+        for n, j in enumerate(rows):
+            kc[j], ks[j] = c[n * hd:(n + 1) * hd], s
+    vc, vs = [[0.0] * hd for _ in range(Lk)], [0.0] * hd
+    for d in range(hd):
+        amax = max(abs(float(v[j][d])) for j in range(Lk))
+        inv, s = (f32(448) / f32(amax), f32(amax) / f32(448)) if amax else (f32(1), f32(1))
+        for j in range(Lk):
+            vc[j][d] = e4m3(min(max(f32(v[j][d]) * inv, f32(-448)), f32(448)))
+        vs[d] = float(s)
+    out = np.zeros((Lq, hd))
+    for i in range(Lq):
+        S = [sum(qc[i][d] * kc[j][d] for d in range(hd)) * qs[i] * ks[j] for j in range(Lk)]
+        mx = max(S)
+        if q_scaled:
+            p = [e4m3(128.0 * 2.0 ** (t - mx)) for t in S]
+        else:
+            p = [e4m3(128.0 * math.exp((t - mx) / math.sqrt(hd))) for t in S]
+        tot = sum(p)
+        for d in range(hd):
+            out[i, d] = vs[d] * sum(p[j] * vc[j][d] for j in range(Lk)) / tot
+    return out
+
+
+def pin_attention_8bit(O):
+    """8-bit attention against the loop version above (two K blocks, the
+    second ragged; plain and pre-scaled q), and two closed forms: equal keys
+    give the mean of v; one key far above the rest gives that key's v (the
+    others' probabilities round to zero).  Inputs on the Int8 / E4M3 grids
+    with scale 1 make both closed forms exact."""
+    r = _rng(61)
+    for q_scaled, mag in ((False, 1.0), (True, 0.3)):
+        q = O.bf16_round(r.standard_normal((3, 16)) * 2.0)
+        k = O.bf16_round(r.standard_normal((70, 16)) * np.where(np.arange(70) < 64, 1.0, 3.0)[:, None])
+        v = O.bf16_round(r.standard_normal((70, 16)))
+        q = O.bf16_round(q * mag)
+        _close(O.attention_8bit(q, k, v, q_scaled), _brute_attention_8bit(q, k, v, q_scaled), 1e-12,
+               f"8-bit attention vs loops (q_scaled={q_scaled})")
+    vals = O.e4m3_values()
+    v = vals[r.integers(0, 127, (40, 8))] * np.sign(r.standard_normal((40, 8)))
+    v[5] = 448.0                                          # every channel's max is 448: scale 1
+    q = np.round(r.standard_normal((4, 8)) * 40)
+    q[:, 0] = 127.0                                       # per-token scale 1
+    k = np.tile(np.round(r.standard_normal((1, 8)) * 40), (40, 1))
+    k[:, 1] = 127.0                                       # equal keys, block scale 1
+    for q_scaled in (False, True):
+        _close(O.attention_8bit(q, k, v, q_scaled), np.tile(v.mean(axis=0), (4, 1)), 1e-12,
+               "equal keys: mean of v")
+    k = np.zeros((40, 8))
+    k[:, 0] = -127.0
+    k[17, 0] = 127.0                                      # key 17 scores 2 * 127^2 above the rest
+    for q_scaled in (False, True):
+        q1 = np.zeros((4, 8))
+        q1[:, 0] = 127.0
+        _close(O.attention_8bit(q1, k, v, q_scaled), np.tile(v[17], (4, 1)), 0, "one dominant key")

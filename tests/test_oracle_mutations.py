@@ -61,6 +61,21 @@ MUTATIONS = {
                                 "wkv_img=wts.get(\"ca_wkv_img\"), bkv_img=wts.get(\"ca_bkv_img\"))"),
     "fp8 flag not passed to the blocks": ("x = block(x, m, wts, ctx, heads, eps, img=img, fp8=fp8)",
                                           "x = block(x, m, wts, ctx, heads, eps, img=img)"),
+    "attn8 K scales tiled, not repeated": ("skey = np.repeat(sk, ATTN8_KBLOCK)[:k8.shape[0]]",
+                                           "skey = np.resize(sk, k8.shape[0])"),
+    "attn8 K block of 32": ("def quantize_k_int8(k, block: int = ATTN8_KBLOCK):",
+                            "def quantize_k_int8(k, block: int = 32):"),
+    "attn8 normaliser unrounded": ("return (P8 @ v8) * sv[None, :] / P8.sum(axis=1, keepdims=True)",
+                                   "return (P8 @ v8) * sv[None, :] / P.sum(axis=1, keepdims=True)"),
+    "attn8 probabilities not scaled": ("P = ATTN8_PSCALE * np.exp(S - S.max(axis=1, keepdims=True))",
+                                       "P = np.exp(S - S.max(axis=1, keepdims=True))"),
+    "attn8 V scale per token": ("q, sc = quantize_rows_fp8(np.asarray(v, np.float32).T)\n    return q.T, sc",
+                                "q, sc = quantize_rows_fp8(np.asarray(v, np.float32))\n    return q, sc[:q.shape[1]]"),
+    "attn8 Int8 truncates": ("return np.rint(v.astype(F64)), F64(s)", "return np.trunc(v.astype(F64)), F64(s)"),
+    "attn8 Int8 scale 128": ("return np.float32(I8_MAX) / amax, amax / np.float32(I8_MAX)",
+                             "return np.float32(128.0) / amax, amax / np.float32(128.0)"),
+    "attn8 pre-scaled q scaled again": ("        S = S / math.sqrt(q8.shape[1])\n        P = ATTN8_PSCALE * np.exp(",
+                                        "        S = S / math.sqrt(q8.shape[1])\n        P = ATTN8_PSCALE * np.exp2("),
     "head split strided": ("k[:, h * hd:(h + 1) * hd],\n                                     v[:, h * hd:(h + 1) * hd])",
                            "k[:, h::heads],\n                                     v[:, h::heads])"),
 }
