@@ -238,6 +238,49 @@ int wan_sample_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, int H8
 int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv, int vt_bstride,
                       void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled, void *stream);
 
+/* ---- 8-bit attention ([Note] Infra / 推理优化: 8-bit FlashAttention, Int8 for
+ * S = QK^T, FP8 for O = PV, FP32 accumulation across key blocks) -----------
+ * Quantised copies, hd = 128, all device:
+ *   q8  [B*Lq, H*128] Int8 codes, qs [B*Lq, H] float32: q per token and head
+ *   k8  [B*Lk, H*128] Int8 codes, ks [B, H, ceil(Lk/64)] float32: k per block
+ *       of 64 keys and head (block b = keys 64b .. 64b+63, the last ragged)
+ *   v8t [H*128, B*Lkp] E4M3 bytes, Lkp = round_up(Lk, 64), batch b at column
+ *       b*Lkp (columns Lk .. Lkp-1 of a segment are zero), vs [B, H*128]
+ *       float32: V per channel (one head feature over the Lk keys)
+ * Int8: inv = 127 / amax (float32 division), code = round-half-even(
+ * clamp(x * inv, +-127)), scale = amax / 127.  E4M3: the FP8 GEMM's rule
+ * with 448.  An all-zero group gets scale 1.  The attention scores with the
+ * integer dot products times qs ks, scales its probabilities so the row max
+ * maps to at most 448 (2^7 where the running max is set), rounds them to
+ * E4M3, and divides sum_j P_j v8_j vs by sum_j P_j (float32 accumulation).
+ * Limits: Lk*H*128 and H*128*B*Lkp below 2^31 (WAN_ERR_SHAPE beyond). */
+
+/* Workspace bytes of wan_attention_8bit_fwd (the six copies, each 256-byte
+ * aligned); 0 for invalid or too large sizes. */
+size_t wan_attention_8bit_workspace_bytes(int B, int H, int Lq, int Lk);
+
+/* The quantisers: q, k, vt as in wan_attention_fwd (bf16; vt's padding
+ * columns Lk .. round_up(Lk, 64)-1 must be readable, their values are
+ * ignored) -> the six copies above, caller-allocated. */
+int wan_attention_8bit_quantize(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv,
+                                int vt_bstride, int B, int H, int Lq, int Lk, void *q8, float *qs, void *k8,
+                                float *ks, void *v8t, float *vs, void *stream);
+
+/* The 8-bit attention on quantised copies (layouts above).  q_scaled as in
+ * wan_attention_fwd: 1 when the q that was quantised had been multiplied by
+ * log2(e)/sqrt(128).  o [B, Lq, H*128] bf16, row stride ldo (>= H*128, % 4). */
+int wan_attention_8bit_q_fwd(const void *q8, const float *qs, const void *k8, const float *ks, const void *v8t,
+                             const float *vs, void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled,
+                             void *stream);
+
+/* Both: arguments as wan_attention_fwd plus ws (device, at least
+ * wan_attention_8bit_workspace_bytes, else WAN_ERR_WORKSPACE) holding the
+ * copies.  The result approximates wan_attention_fwd's within the 8-bit
+ * rounding (a few percent of |O|). */
+int wan_attention_8bit_fwd(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv,
+                           int vt_bstride, void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled,
+                           void *ws, size_t ws_bytes, void *stream);
+
 /* y = x W^T + b for a bf16 x [M, K], W [N, K], b [N] (device), K % 64 == 0.
  * mode 0: y bf16 [M, N];  mode 1: y float32 [M, N];  mode 2: y bf16 = GELU_tanh(.) */
 int wan_linear_fwd(const void *x, const void *w, const void *b, void *y, int M, int N, int K,

@@ -159,3 +159,28 @@ def test_fp8_model_sizes_and_invalid_arguments(W):
                                   None, dummy, dummy, 1 << 40, None) == -1
     assert L.wan_sample_fp8_fwd(C.byref(c), dummy, 2, 3, 8, 12, 0, 1, 5.0, dummy, 1 << 30,
                                 C.byref(mw), dummy, dummy, 1 << 40, None) == -2   # zero steps
+
+
+def test_attn8_sizes_and_invalid_arguments(W):
+    # six copies, each 256-aligned: q8, qs, k8, ks, v8t, vs
+    B, H, Lq, Lk = 2, 3, 100, 70
+    d, Lkp = H * 128, 128
+    parts = [B * Lq * d, B * Lq * H * 4, B * Lk * d, B * H * 2 * 4, d * B * Lkp, B * d * 4]
+    assert W.attention_8bit_workspace_bytes(B, H, Lq, Lk) == sum((p + 255) // 256 * 256 for p in parts)
+    assert W.attention_8bit_workspace_bytes(0, H, Lq, Lk) == 0
+    assert W.attention_8bit_workspace_bytes(1, 40, 10, 500000) == 0          # beyond 32-bit offsets
+    L = W.lib()
+    dummy = C.c_void_p(256)   # never dereferenced: every call below fails validation first
+    ws = 1 << 40
+    assert L.wan_attention_8bit_fwd(dummy, 384, dummy, 384, dummy, 256, 128, dummy, 384, 2, 3, 100, 70, 0,
+                                    None, ws, None) == -1
+    assert L.wan_attention_8bit_fwd(dummy, 100, dummy, 384, dummy, 256, 128, dummy, 384, 2, 3, 100, 70, 0,
+                                    dummy, ws, None) == -2                  # ldq < H*128
+    assert L.wan_attention_8bit_fwd(dummy, 384, dummy, 384, dummy, 256, 64, dummy, 384, 2, 3, 100, 70, 0,
+                                    dummy, ws, None) == -2                  # vt_bstride < round_up(Lk, 64)
+    assert L.wan_attention_8bit_fwd(dummy, 384, dummy, 384, dummy, 256, 128, dummy, 384, 2, 3, 100, 70, 0,
+                                    dummy, 1024, None) == -4                # short workspace
+    assert L.wan_attention_8bit_quantize(dummy, 384, dummy, 384, dummy, 256, 128, 2, 3, 100, 70, dummy, None,
+                                         dummy, dummy, dummy, dummy, None) == -1
+    assert L.wan_attention_8bit_q_fwd(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 100, 2, 3, 100, 70, 0,
+                                      None) == -2                           # ldo < H*128

@@ -6,7 +6,9 @@ into that ABI.  Build the library with ``python -m
 video_diffusion_transformer_block_amd.build`` (or ``__graft_entry__.build()``).
 """
 from . import binding  # noqa: F401
-from .binding import (Cfg, WanError, attention_fwd, block_fp8_bytes, block_fp8_workspace_bytes,  # noqa: F401
+from .binding import (Cfg, WanError, attention_fwd, attention_8bit_fwd, attention_8bit_q_fwd,  # noqa: F401
+                      attention_8bit_quantize, attention_8bit_workspace_bytes, block_fp8_bytes,
+                      block_fp8_workspace_bytes,
                       block_weights, dit_block_fp8_fwd, dit_block_fwd, quantize_block_fp8,
                       model_fp8_bytes, fp8_workspace_bytes, quantize_model_fp8, dit_step_fp8_fwd,
                       sample_fp8_fwd,

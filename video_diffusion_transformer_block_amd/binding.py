@@ -26,10 +26,11 @@ EXPORTS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_by
            "wan_quantize_tensor_fp8", "wan_linear_fp8_fwd", "wan_block_fp8_bytes",
            "wan_quantize_block_fp8", "wan_block_fp8_workspace_bytes", "wan_dit_block_fp8_fwd",
            "wan_model_fp8_bytes", "wan_quantize_model_fp8", "wan_fp8_workspace_bytes",
-           "wan_dit_step_fp8_fwd", "wan_sample_fp8_fwd")
+           "wan_dit_step_fp8_fwd", "wan_sample_fp8_fwd", "wan_attention_8bit_workspace_bytes",
+           "wan_attention_8bit_quantize", "wan_attention_8bit_q_fwd", "wan_attention_8bit_fwd")
 _SIZE_FNS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
              "wan_block_fp8_bytes", "wan_block_fp8_workspace_bytes", "wan_model_fp8_bytes",
-             "wan_fp8_workspace_bytes")
+             "wan_fp8_workspace_bytes", "wan_attention_8bit_workspace_bytes")
 
 
 class WanError(RuntimeError):
@@ -112,6 +113,11 @@ def lib() -> C.CDLL:
                                            vp, vp, vp, sz, vp]
         L.wan_sample_fp8_fwd.argtypes = [C.POINTER(Cfg), vp, i, i, i, i, i, i, C.c_float, vp, sz,
                                          C.POINTER(ModelW), vp, vp, sz, vp]
+        L.wan_attention_8bit_workspace_bytes.argtypes = [i, i, i, i]
+        L.wan_attention_8bit_quantize.argtypes = [vp, i, vp, i, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp,
+                                                  vp]
+        L.wan_attention_8bit_q_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.wan_attention_8bit_fwd.argtypes = [vp, i, vp, i, vp, i, i, vp, i, i, i, i, i, i, vp, sz, vp]
         for n in EXPORTS:
             if n in _SIZE_FNS:
                 getattr(L, n).restype = sz
@@ -203,6 +209,31 @@ def attention_fwd(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk, str
     _check("wan_attention_fwd",
            lib().wan_attention_fwd(_p(q), ldq, _p(k), ldk, _p(vt), ldv, vt_bstride, _p(o), ldo,
                                    B, H, Lq, Lk, int(bool(q_scaled)), _stream(stream)))
+
+
+def attention_8bit_workspace_bytes(B, H, Lq, Lk) -> int:
+    return int(lib().wan_attention_8bit_workspace_bytes(B, H, Lq, Lk))
+
+
+def attention_8bit_quantize(q, ldq, k, ldk, vt, ldv, vt_bstride, B, H, Lq, Lk, q8, qs, k8, ks, v8t, vs,
+                            stream=None):
+    _check("wan_attention_8bit_quantize",
+           lib().wan_attention_8bit_quantize(_p(q), ldq, _p(k), ldk, _p(vt), ldv, vt_bstride, B, H, Lq, Lk,
+                                             _p(q8), _p(qs), _p(k8), _p(ks), _p(v8t), _p(vs), _stream(stream)))
+
+
+def attention_8bit_q_fwd(q8, qs, k8, ks, v8t, vs, o, ldo, B, H, Lq, Lk, q_scaled=False, stream=None):
+    _check("wan_attention_8bit_q_fwd",
+           lib().wan_attention_8bit_q_fwd(_p(q8), _p(qs), _p(k8), _p(ks), _p(v8t), _p(vs), _p(o), ldo, B, H,
+                                          Lq, Lk, int(bool(q_scaled)), _stream(stream)))
+
+
+def attention_8bit_fwd(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk, ws, q_scaled=False,
+                       stream=None):
+    _check("wan_attention_8bit_fwd",
+           lib().wan_attention_8bit_fwd(_p(q), ldq, _p(k), ldk, _p(vt), ldv, vt_bstride, _p(o), ldo, B, H,
+                                        Lq, Lk, int(bool(q_scaled)), _p(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def linear_fwd(x, w, b, y, M, N, K, mode, stream=None):

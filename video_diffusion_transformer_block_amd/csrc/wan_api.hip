@@ -18,6 +18,7 @@
 #include <string.h>
 
 #include "../../include/wan_dit.h"
+#include "attn8.hpp"
 #include "kernels.hpp"
 
 using namespace wan;
@@ -690,6 +691,113 @@ int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void
     return WAN_ERR_SHAPE;
   AttnDesc a = attn(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk, 128, 0, q_scaled != 0);
   WAN_TRY(launch_attention(a, S(stream)));
+  return WAN_OK;
+}
+
+// ---- 8-bit attention: Int8 / E4M3 copies of q, k, V^T and the attention on them
+
+namespace {
+
+// byte offsets of the quantised copies in a workspace: q8, qs, k8, ks, v8t, vs, end
+void attn8_offsets(int B, int H, int Lq, int Lk, size_t off[7]) {
+  const size_t d = (size_t)H * 128, Lkp = (size_t)rup(Lk, 64), nkb = Lkp / 64;
+  const size_t sz[6] = {(size_t)B * Lq * d, (size_t)B * Lq * H * 4, (size_t)B * Lk * d,
+                        (size_t)B * H * nkb * 4, d * B * Lkp, (size_t)B * d * 4};
+  size_t o = 0;
+  for (int i = 0; i < 6; ++i) {
+    off[i] = o;
+    o += up(sz[i], ALIGN);
+  }
+  off[6] = o;
+}
+
+// sizes the 8-bit kernels address with 32-bit buffer offsets
+bool attn8_fits(int B, int H, int Lq, int Lk) {
+  const long d = (long)H * 128;
+  return (long)Lk * d < (1L << 31) && d * B * rup(Lk, 64) < (1L << 31) && (long)B * Lq < (1L << 31) / d;
+}
+
+Attn8Desc attn8_desc(const void *q8, const float *qs, const void *k8, const float *ks, const void *v8t,
+                     const float *vs, void *o, int ldo, int B, int H, int Lq, int Lk, bool q_scaled) {
+  Attn8Desc a;
+  a.q8 = static_cast<const int8_t *>(q8); a.ldq8 = (long)H * 128; a.qs = qs;
+  a.k8 = static_cast<const int8_t *>(k8); a.ldk8 = (long)H * 128; a.ks = ks;
+  a.v8t = static_cast<const uint8_t *>(v8t); a.v8_bstride = rup(Lk, 64); a.ldv8 = (long)B * a.v8_bstride;
+  a.vs = vs;
+  a.o = o; a.ldo = ldo;
+  a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk;
+  a.alpha = q_scaled ? 1.0f : 1.4426950408889634f / sqrtf(128.0f);
+  return a;
+}
+
+Attn8Quant attn8_quant(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv, int vt_bstride,
+                       int B, int H, int Lq, int Lk, void *q8, float *qs, void *k8, float *ks, void *v8t,
+                       float *vs) {
+  Attn8Quant z;
+  z.q = q; z.ldq = ldq; z.k = k; z.ldk = ldk; z.vt = vt; z.ldv = ldv; z.vt_bstride = vt_bstride;
+  z.B = B; z.H = H; z.Lq = Lq; z.Lk = Lk;
+  z.q8 = q8; z.ldq8 = (long)H * 128; z.qs = qs;
+  z.k8 = k8; z.ldk8 = (long)H * 128; z.ks = ks;
+  z.v8t = v8t; z.v8_bstride = rup(Lk, 64); z.ldv8 = (long)B * z.v8_bstride; z.vs = vs;
+  return z;
+}
+
+// argument checks shared by the 8-bit entry points taking bf16 q, k, V^T
+int attn8_check_inputs(int ldq, int ldk, int ldv, int vt_bstride, int B, int H, int Lq, int Lk) {
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return WAN_ERR_SHAPE;
+  if (ldq < H * 128 || ldk < H * 128 || ldq % 8 || ldk % 8) return WAN_ERR_SHAPE;
+  if (ldv % 8 || vt_bstride % 8 || vt_bstride < rup(Lk, 64) || (long)ldv < (long)B * vt_bstride)
+    return WAN_ERR_SHAPE;
+  if (!attn8_fits(B, H, Lq, Lk)) return WAN_ERR_SHAPE;
+  return WAN_OK;
+}
+
+}  // namespace
+
+size_t wan_attention_8bit_workspace_bytes(int B, int H, int Lq, int Lk) {
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || !attn8_fits(B, H, Lq, Lk)) return 0;
+  size_t off[7];
+  attn8_offsets(B, H, Lq, Lk, off);
+  return off[6];
+}
+
+int wan_attention_8bit_quantize(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv,
+                                int vt_bstride, int B, int H, int Lq, int Lk, void *q8, float *qs, void *k8,
+                                float *ks, void *v8t, float *vs, void *stream) {
+  if (!q || !k || !vt || !q8 || !qs || !k8 || !ks || !v8t || !vs) return WAN_ERR_NULL;
+  const int st = attn8_check_inputs(ldq, ldk, ldv, vt_bstride, B, H, Lq, Lk);
+  if (st != WAN_OK) return st;
+  WAN_TRY(launch_quant_attn8(attn8_quant(q, ldq, k, ldk, vt, ldv, vt_bstride, B, H, Lq, Lk, q8, qs, k8, ks,
+                                         v8t, vs), S(stream)));
+  return WAN_OK;
+}
+
+int wan_attention_8bit_q_fwd(const void *q8, const float *qs, const void *k8, const float *ks, const void *v8t,
+                             const float *vs, void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled,
+                             void *stream) {
+  if (!q8 || !qs || !k8 || !ks || !v8t || !vs || !o) return WAN_ERR_NULL;
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || ldo < H * 128 || ldo % 4) return WAN_ERR_SHAPE;
+  if (!attn8_fits(B, H, Lq, Lk)) return WAN_ERR_SHAPE;
+  WAN_TRY(launch_attention8(attn8_desc(q8, qs, k8, ks, v8t, vs, o, ldo, B, H, Lq, Lk, q_scaled != 0), S(stream)));
+  return WAN_OK;
+}
+
+int wan_attention_8bit_fwd(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv,
+                           int vt_bstride, void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled,
+                           void *ws, size_t ws_bytes, void *stream) {
+  if (!q || !k || !vt || !o || !ws) return WAN_ERR_NULL;
+  int st = attn8_check_inputs(ldq, ldk, ldv, vt_bstride, B, H, Lq, Lk);
+  if (st != WAN_OK) return st;
+  if (ldo < H * 128 || ldo % 4) return WAN_ERR_SHAPE;
+  size_t off[7];
+  attn8_offsets(B, H, Lq, Lk, off);
+  if (ws_bytes < off[6]) return WAN_ERR_WORKSPACE;
+  char *w = static_cast<char *>(ws);
+  float *qs = (float *)(w + off[1]), *ks = (float *)(w + off[3]), *vs = (float *)(w + off[5]);
+  WAN_TRY(launch_quant_attn8(attn8_quant(q, ldq, k, ldk, vt, ldv, vt_bstride, B, H, Lq, Lk, w + off[0], qs,
+                                         w + off[2], ks, w + off[4], vs), S(stream)));
+  WAN_TRY(launch_attention8(attn8_desc(w + off[0], qs, w + off[2], ks, w + off[4], vs, o, ldo, B, H, Lq, Lk,
+                                       q_scaled != 0), S(stream)));
   return WAN_OK;
 }
 
