@@ -369,13 +369,29 @@ __global__ __launch_bounds__(512, 1) void k_attn_i8f8(Attn8Desc a) {
                   const i32x8 &pprev, bool has_next, bool load_k2, bool do_pv, bool ragged) {
     const auto Q = other(P);
     if (load_k2) gloadK(j + 2, P);      // stage of K(j), read in iteration j-1
+    gloadV(j, P);                        // stage of V(j-2), read in iteration j-1
     const float c = cq * ksp[j];
     const float bb = -fmaf(K0F, c, m);
-    if (has_next) qk(kbuf(Q), snxt);
+    // region 1 -- matrix unit: PV of tile j-1; vector unit: the exponents of
+    // tile j and their lane max
     if (do_pv) pv(vbuf(Q), pprev);
     float x[2][16];
     expo(scur, c, bb, ragged, j, x);
     const float lm = lanemax(x);
+    if (do_pv) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // V fragments of the first two MFMAs
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // the fragment two MFMAs ahead
+        __builtin_amdgcn_sched_group_barrier(0x402, 10, 0);  // 10 VALU
+      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 10, 0);
+      }
+    }
     if (__builtin_amdgcn_ballot_w64(lm > XMAX8) != 0) {
       // raise the running max to this tile's (so its largest probability is
       // 2^7); the accumulators (including PV(j-1), of the old max) follow
@@ -393,9 +409,24 @@ __global__ __launch_bounds__(512, 1) void k_attn_i8f8(Attn8Desc a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[kb][r] -= dm;
     }
+    // region 2 -- matrix unit: the scores of tile j+1; vector unit: the
+    // probabilities of tile j
+    if (has_next) qk(kbuf(Q), snxt);
     probs(x, pcur);
-    __builtin_amdgcn_sched_barrier(0);
-    gloadV(j, P);                        // stage of V(j-2), read in iteration j-1
+    if (has_next) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // K fragments of the first two MFMAs
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the fragment two MFMAs ahead
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);   // 6 VALU
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0x0070);  // K(j+2), V(j) landed; LDS reads done
     __syncthreads();
   };
