@@ -20,17 +20,25 @@
 //    FMA, f * c + bb with c = sq sk log2(e)/sqrt(hd) and bb = -(1.5 * 2^23 c
 //    + m), gives the score in log2 units minus the running max m;
 //  * probabilities p = exp2 of that: 2^7 at a freshly set max.  The max is
-//    taken from the first tile and raised only when a probability of a tile
-//    would pass 448, E4M3's largest value (a lane max of the exponents per
-//    tile); the accumulators are then rescaled and the tile recomputed;
+//    taken from the first tile and raised, by a whole number of log2 units,
+//    only when a probability of a tile would pass 448, E4M3's largest value
+//    (a lane max of the tile's scores, checked before the exponentials).
+//    The accumulators are not rescaled: O and the row sums stay referred to
+//    the first max, 2^64 below it, and each tile's probabilities enter them
+//    times 2^E, E the total rise so far, through the E8M0 scale of the B
+//    operand of the MFMAs.  Should E pass 150 the accumulated terms weigh
+//    less than 2^-130 against the new ones and are cleared;
 //  * P^T in E4M3 is the B operand of O^T += V^T P^T
 //    (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales).  The rows of a K
 //    tile sit in LDS in a permuted order (ksig8) that makes a lane's 32 score
 //    registers the probabilities of 32 consecutive keys, so a V^T fragment is
 //    32 consecutive bytes of a V^T row;
-//  * the row sums come from one more MFMA of the same P^T with an all-ones A
-//    operand: the normaliser adds exactly the rounded probabilities the PV
-//    MFMAs weight V with, in float32;
+//  * the row sums come from one more MFMA of the same P^T registers, a
+//    16x16x128 one whose A operand holds ones and zeros per lane: it adds a
+//    query's 64 probabilities (with unit scales -- a K block of that MFMA
+//    mixes two queries, whose E may differ), and the lane adds it times 2^E
+//    to its float32 sum: the normaliser is exactly the sum of the rounded
+//    weights the PV MFMAs use;
 //  * software pipeline: iteration j runs the score MFMAs of tile j+1 and the
 //    PV MFMAs of tile j-1 while the vector unit turns the scores of tile j
 //    into probabilities; K and V^T tiles of 64 keys go global -> LDS directly
@@ -270,14 +278,24 @@ __global__ __launch_bounds__(512, 1) void k_attn_i8f8(Attn8Desc a) {
   i32x16 kinit;
 #pragma unroll
   for (int r = 0; r < 16; ++r) kinit[r] = K0I;
+  // A operand of the row-sum MFMA (16x16x128): lane l holds row l%16, key
+  // group l/16 of the B operand -- the P^T registers read as 16 columns x 4
+  // groups of 32 keys: group 0 = query c, keys 0-31; 1 = query c+16, keys
+  // 0-31; 2 = query c, keys 32-63; 3 = query c+16, keys 32-63 (c = l%16).
+  // Rows r with (r/4) even sum groups 0 and 2 (query c), the others groups 1
+  // and 3 (query c+16); result row 4(l/16) + i then holds the row sum of
+  // query l%32 in every lane.  E4M3 1.0 is 0x38.
   i32x8 ones;
+  {
+    const int sel = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) ones[r] = 0x38383838;   // E4M3 1.0 in every byte
+    for (int r = 0; r < 8; ++r) ones[r] = sel;
+  }
 
-  f32x16 o[4], lacc;
+  f32x16 o[4];
+  float lsum = 0.f;   // row sum of this lane's query, same reference as O
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    lacc[r] = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) o[t][r] = 0.f;
   }
@@ -306,6 +324,19 @@ __global__ __launch_bounds__(512, 1) void k_attn_i8f8(Attn8Desc a) {
           if (j * KT8 + 32 * g + 16 * kb + r >= Lk) x[kb][r] = -INFINITY;
     }
   };
+  // lane max of a tile's biased integer scores read as floats (positive,
+  // ordered like the scores); keys past Lk count as the lowest score
+  auto rawmax = [&](const i32x16 (&s)[2], bool ragged, int j) {
+    float mx = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool dead = ragged && j * KT8 + 32 * g + 16 * kb + r >= Lk;
+        mx = fmaxf(mx, dead ? 0.f : __int_as_float(s[kb][r]));
+      }
+    return mx;
+  };
   auto lanemax = [&](const float (&x)[2][16]) {
     float m = x[0][0];
 #pragma unroll
@@ -314,21 +345,27 @@ __global__ __launch_bounds__(512, 1) void k_attn_i8f8(Attn8Desc a) {
       for (int r = 0; r < 16; ++r) m = fmaxf(m, x[kb][r]);
     return m;
   };
-  // E4M3 probabilities in the B-operand layout: byte 16 kb + r = key 32 g + 16 kb + r
+  // E4M3 probabilities in the B-operand layout: byte 16 kb + r = key 32 g + 16
+  // kb + r.  The two packs of a dword write its low and its high half, so the
+  // first starts from the register's old contents (no zeroing move).
   auto probs = [&](const float (&x)[2][16], i32x8 &p) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         int d = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(x[kb][4 * q]),
-                                                __builtin_amdgcn_exp2f(x[kb][4 * q + 1]), 0, false);
+                                                __builtin_amdgcn_exp2f(x[kb][4 * q + 1]), p[kb * 4 + q], false);
         d = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(x[kb][4 * q + 2]),
                                             __builtin_amdgcn_exp2f(x[kb][4 * q + 3]), d, true);
         p[kb * 4 + q] = d;
       }
   };
-  // O^T += V^T P^T and the row sums += 1^T P^T
-  auto pv = [&](const uint8_t *sv, const i32x8 &p) {
+  // O^T += V^T P^T, the products times 2^(E-64) (E8M0 scale ebits of the B
+  // operand: for output column j it is read from lanes j and j+32, both this
+  // query's), and the row sum += 2^(E-64) 1^T P^T
+  auto pv = [&](const uint8_t *sv, const i32x8 &p, int ebits) {
+    const f32x4 lt = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, p, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                      0x7F7F7F7F, 0, 0x7F7F7F7F);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint4 lo = *reinterpret_cast<const uint4 *>(sv + t * 32 * KT8 + voff[0]);
@@ -336,9 +373,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_i8f8(Attn8Desc a) {
       i32x8 va;
       va[0] = lo.x; va[1] = lo.y; va[2] = lo.z; va[3] = lo.w;
       va[4] = hi.x; va[5] = hi.y; va[6] = hi.z; va[7] = hi.w;
-      o[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, p, o[t], 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+      o[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, p, o[t], 0, 0, 0, 0x7F7F7F7F, 0, ebits);
     }
-    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, p, lacc, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+    lsum = fmaf(lt[0], __int_as_float((ebits & 0xFF) << 23), lsum);   // 2^(byte - 127)
   };
 
   constexpr std::integral_constant<int, 0> P0{};
@@ -352,6 +389,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_i8f8(Attn8Desc a) {
   i32x16 sa[2], sb[2];
   qk(sK0, sa);
   float m;   // running max, log2 units, minus XTOP8
+  int E = 0;  // its rise since the first tile (whole log2 units)
   {
     float x[2][16];
     const float c = cq * ksp[0];
@@ -366,52 +404,52 @@ __global__ __launch_bounds__(512, 1) void k_attn_i8f8(Attn8Desc a) {
   // j+1 exists; load_k2: tile j+2 exists; do_pv: j >= 1; ragged: tile j is
   // the last, ragged tile.
   auto step = [&](auto P, int j, const i32x16 (&scur)[2], i32x16 (&snxt)[2], i32x8 &pcur,
-                  const i32x8 &pprev, bool has_next, bool load_k2, bool do_pv, bool ragged) {
+                  const i32x8 &pprev, int &ecur, int eprev, bool has_next, bool load_k2, bool do_pv,
+                  bool ragged) {
     const auto Q = other(P);
     if (load_k2) gloadK(j + 2, P);      // stage of K(j), read in iteration j-1
     gloadV(j, P);                        // stage of V(j-2), read in iteration j-1
     const float c = cq * ksp[j];
-    const float bb = -fmaf(K0F, c, m);
-    // region 1 -- matrix unit: PV of tile j-1; vector unit: the exponents of
-    // tile j and their lane max
-    if (do_pv) pv(vbuf(Q), pprev);
-    float x[2][16];
-    expo(scur, c, bb, ragged, j, x);
-    const float lm = lanemax(x);
+    // region 1 -- matrix unit: PV of tile j-1; vector unit: the lane max of
+    // tile j's biased scores (as floats 1.5 * 2^23 + S, ordered like S)
+    if (do_pv) pv(vbuf(Q), pprev, eprev);
+    const float lx = fmaf(rawmax(scur, ragged, j), c, -fmaf(K0F, c, m));
     if (do_pv) {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // V fragments of the first two MFMAs
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // the fragment two MFMAs ahead
-        __builtin_amdgcn_sched_group_barrier(0x402, 10, 0);  // 10 VALU
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);   // 4 VALU
       }
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
       }
     }
-    if (__builtin_amdgcn_ballot_w64(lm > XMAX8) != 0) {
-      // raise the running max to this tile's (so its largest probability is
-      // 2^7); the accumulators (including PV(j-1), of the old max) follow
-      const float dm = fmaxf(fmaxf(lm, half_swap(lm)) - XTOP8, 0.f);
-      const float al = __builtin_amdgcn_exp2f(-dm);
+    if (__builtin_amdgcn_ballot_w64(lx > XMAX8) != 0) {
+      // raise the running max by whole log2 units, so that this tile's
+      // largest probability lands in (2^6, 2^7]
+      const float dm = ceilf(fmaxf(fmaxf(lx, half_swap(lx)) - XTOP8, 0.f));
       m += dm;
+      E += (int)dm;
+      if (E > 150) {
+        // the terms accumulated so far are below 2^-130 of the new ones
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        lacc[r] *= al;
+        for (int r = 0; r < 16; ++r)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) o[t][r] *= al;
+          for (int t = 0; t < 4; ++t) o[t][r] = 0.f;
+        lsum = 0.f;
+        E = 0;
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[kb][r] -= dm;
     }
+    ecur = (63 + E) * 0x01010101;   // E8M0 of 2^(E-64) in every byte: this tile's scale
     // region 2 -- matrix unit: the scores of tile j+1; vector unit: the
-    // probabilities of tile j
+    // exponents and probabilities of tile j
     if (has_next) qk(kbuf(Q), snxt);
+    float x[2][16];
+    expo(scur, c, -fmaf(K0F, c, m), ragged, j, x);
     probs(x, pcur);
     if (has_next) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // K fragments of the first two MFMAs
@@ -419,12 +457,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_i8f8(Attn8Desc a) {
       for (int i = 0; i < 6; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the fragment two MFMAs ahead
-        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);   // 6 VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // 6 VALU (FMA, E4M3 packing)
+        __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);   // 4 exponentials
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0070);  // K(j+2), V(j) landed; LDS reads done
@@ -432,31 +472,34 @@ __global__ __launch_bounds__(512, 1) void k_attn_i8f8(Attn8Desc a) {
   };
 
   i32x8 pa, pb;
+  int ea = 63 * 0x01010101, eb = 63 * 0x01010101;
 #pragma unroll
   for (int r = 0; r < 8; ++r) pa[r] = pb[r] = 0;
-  step(P0, 0, sa, sb, pa, pb, ntiles > 1, ntiles > 2, false, ntiles == 1 && ragged_last);
+  step(P0, 0, sa, sb, pa, pb, ea, eb, ntiles > 1, ntiles > 2, false, ntiles == 1 && ragged_last);
   int j = 1;
   for (; j + 3 < ntiles; j += 2) {
-    step(P1, j, sb, sa, pb, pa, true, true, true, false);
-    step(P0, j + 1, sa, sb, pa, pb, true, true, true, false);
+    step(P1, j, sb, sa, pb, pa, eb, ea, true, true, true, false);
+    step(P0, j + 1, sa, sb, pa, pb, ea, eb, true, true, true, false);
   }
   // the last tiles with run-time stages; scores of tile j in sb, P(j-1) in pa
   for (; j < ntiles; ++j) {
-    step(j & 1, j, sb, sa, pb, pa, j + 1 < ntiles, j + 2 < ntiles, true, j == ntiles - 1 && ragged_last);
+    step(j & 1, j, sb, sa, pb, pa, eb, ea, j + 1 < ntiles, j + 2 < ntiles, true,
+         j == ntiles - 1 && ragged_last);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) sb[kb] = sa[kb];
     pa = pb;
+    ea = eb;
   }
-  pv(vbuf((ntiles - 1) & 1), pa);
+  pv(vbuf((ntiles - 1) & 1), pa, ea);
   // the MFMAs read operands across the whole wavefront: keep the last ones
   // (and their LDS reads) out of the row-guarded store below, where the
   // compiler would otherwise sink them under a partial EXEC mask
-  asm volatile("" ::"v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(lacc));
+  asm volatile("" ::"v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(lsum));
 
   // ---- normalise, undo the V channel scales, store: lane holds
   // O^T[hd = t*32 + (r/4)*8 + g*4 + r%4][query qrow]
   if (!qok) return;
-  const float inv = 1.0f / lacc[0];
+  const float inv = 1.0f / lsum;
   const float *vsp = a.vs + (long)b * (H * HD8) + h * HD8;
   const long orow = (long)(b * Lq + qrow);
 #pragma unroll
