@@ -93,6 +93,10 @@ READINGS = {
                            "P8_j: the normaliser adds the rounded probabilities, so O is a convex "
                            "combination of the dequantised values; inputs are the bf16 q, k, v "
                            "the block holds",
+    "R26 8-bit attention in the block": "only the self-attention runs in 8 bits (R25), on the bf16-"
+                                        "rounded q, k, v of the block's projections (bf16 or FP8 "
+                                        "Linear layers); the cross-attention to the short text / "
+                                        "image contexts stays exact",
 }
 
 
@@ -214,12 +218,13 @@ def multihead(q, k, v, heads: int):
 
 
 def self_attention(hmod, wqkv, bqkv, wo, bo, heads: int, rows: Optional[np.ndarray] = None,
-                   fp8: bool = False):
+                   fp8: bool = False, attn8: bool = False):
     """Self-attention of one sample: qkv = h Wqkv^T + b (q | k | v blocks of d
     rows in Wqkv), o = MHA(q, k, v), y = o Wo^T + bo.  ``rows`` restricts the
     query side (and the returned rows) to a subset of tokens; keys and values
     always cover all tokens.  ``fp8``: both projections in FP8 (R22), the
-    stored Wqkv quantised as one tensor."""
+    stored Wqkv quantised as one tensor.  ``attn8``: the attention in 8 bits
+    on the bf16-rounded q, k, v (R25, R26)."""
     hmod = _f(hmod)
     d = hmod.shape[1]
     wqkv, bqkv = _f(wqkv), _f(bqkv)
@@ -234,7 +239,10 @@ def self_attention(hmod, wqkv, bqkv, wo, bo, heads: int, rows: Optional[np.ndarr
     v = lin(hmod, slice(2 * d, 3 * d), bqkv[2 * d:])
     hq = hmod if rows is None else hmod[rows]
     q = lin(hq, slice(0, d), bqkv[:d])
-    o = multihead(q, k, v, heads)
+    if attn8:
+        o = multihead_8bit(bf16_round(q), bf16_round(k), bf16_round(v), heads)
+    else:
+        o = multihead(q, k, v, heads)
     return lin_o(o, wo, bo)
 
 
@@ -273,7 +281,7 @@ def ffn(hmod, w1, b1, w2, b2, fp8: bool = False):
 
 def block(x, m, wts: Dict[str, np.ndarray], ctx, heads: int, eps: float = 1e-6,
           img=None, rows: Optional[np.ndarray] = None, return_parts: bool = False,
-          fp8: bool = False):
+          fp8: bool = False, attn8: bool = False):
     """One block for a batch.  x [B, L, d]; m [B, 6d] (shared t-MLP output);
     ctx [B, Lc, d]; img [B, Li, d] or None.
 
@@ -287,7 +295,8 @@ def block(x, m, wts: Dict[str, np.ndarray], ctx, heads: int, eps: float = 1e-6,
     attention still reads all tokens' keys and values).  ``fp8``: the six
     Linear layers (QKV, SA out, CA query, CA out, FFN up, FFN down) in FP8
     with per-token activation and per-tensor weight scales (R22 - R24)
-    [Note, Infra / 推理优化: FP8 GEMM]."""
+    [Note, Infra / 推理优化: FP8 GEMM].  ``attn8``: the self-attention in 8 bits
+    (R25, R26) [Note, Infra / 推理优化: 8-bit FlashAttention]."""
     x = _f(x)
     mod = block_modulation(m, wts["mod_bias"])
     outs, parts = [], []
@@ -295,7 +304,7 @@ def block(x, m, wts: Dict[str, np.ndarray], ctx, heads: int, eps: float = 1e-6,
         xb = x[b]
         h1 = modulate(layer_norm(xb, eps), mod["shift1"][b], mod["scale1"][b])
         sa = self_attention(h1, wts["sa_wqkv"], wts["sa_bqkv"], wts["sa_wo"], wts["sa_bo"],
-                            heads, rows=rows, fp8=fp8)
+                            heads, rows=rows, fp8=fp8, attn8=attn8)
         xr = xb if rows is None else xb[rows]
         x1 = xr + mod["gate1"][b] * sa
         ca = cross_attention(x1, _f(ctx[b]), wts["ca_wq"], wts["ca_bq"], wts["ca_wkv"],
@@ -373,14 +382,15 @@ def image_context(clip, w1, b1, w2, b2, w3, b3):
 
 def step(latent, t, ctx, mw: Dict[str, object], heads: int, eps: float = 1e-6,
          clip=None, blocks: Optional[List[Dict[str, np.ndarray]]] = None,
-         return_hidden: bool = False, fp8: bool = False):
+         return_hidden: bool = False, fp8: bool = False, attn8: bool = False):
     """patchify -> shared t-MLP -> N blocks -> head -> unpatchify.
     latent [B, Cin, F, H8, W8]; t [B]; ctx [B, Lc, d]; clip [B, Li, 1280] or None.
     Returns the predicted velocity [B, 16, F, H8, W8] (the flow-matching
     target of [Note, 训练方法]).  ``blocks`` may be an iterable that yields the
     block weights one at a time (to bound host memory).  ``fp8``: every block
     with its six Linear layers in FP8 (R22 - R24); patchify, t-MLP, image MLP
-    and head stay exact."""
+    and head stay exact.  ``attn8``: every block's self-attention in 8 bits
+    (R25, R26)."""
     lat = _f(latent)
     B, Cin, F, H8, W8 = lat.shape
     Hp, Wp = H8 // 2, W8 // 2
@@ -393,7 +403,7 @@ def step(latent, t, ctx, mw: Dict[str, object], heads: int, eps: float = 1e-6,
         img = np.stack([image_context(clip[b], iw["w1"], iw["b1"], iw["w2"], iw["b2"],
                                       iw["w3"], iw["b3"]) for b in range(B)])
     for wts in (blocks if blocks is not None else mw["blocks"]):
-        x = block(x, m, wts, ctx, heads, eps, img=img, fp8=fp8)
+        x = block(x, m, wts, ctx, heads, eps, img=img, fp8=fp8, attn8=attn8)
     out = head_unpatchify(x, mw["head_w"], mw["head_b"], F, Hp, Wp, 16)
     return (out, x) if return_hidden else out
 

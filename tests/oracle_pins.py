@@ -741,3 +741,100 @@ def pin_attention_8bit(O):
         q1 = np.zeros((4, 8))
         q1[:, 0] = 127.0
         _close(O.attention_8bit(q1, k, v, q_scaled), np.tile(v[17], (4, 1)), 0, "one dominant key")
+
+
+def pin_attn8_block(O):
+    """The block's 8-bit attention switch touches only the self-attention:
+    with the 8-bit attention replaced by the exact one (and the bf16 rounding
+    by the identity) the block equals the exact block bit for bit, with one
+    call per sample (also with FP8 Linear layers).  The real 8-bit block
+    update stays within a few percent of the exact one."""
+    r = _rng(62)
+    d, F, H, L, Lc = 256, 128, 2, 70, 6
+    w = {"sa_wqkv": r.standard_normal((3 * d, d)) * 0.06, "sa_bqkv": r.standard_normal(3 * d) * 0.02,
+         "sa_wo": r.standard_normal((d, d)) * 0.06, "sa_bo": r.standard_normal(d) * 0.02,
+         "ca_wq": r.standard_normal((d, d)) * 0.06, "ca_bq": r.standard_normal(d) * 0.02,
+         "ca_wkv": r.standard_normal((2 * d, d)) * 0.06, "ca_bkv": r.standard_normal(2 * d) * 0.02,
+         "ca_wo": r.standard_normal((d, d)) * 0.06, "ca_bo": r.standard_normal(d) * 0.02,
+         "ffn_w1": r.standard_normal((F, d)) * 0.06, "ffn_b1": r.standard_normal(F) * 0.02,
+         "ffn_w2": r.standard_normal((d, F)) * 0.06, "ffn_b2": r.standard_normal(d) * 0.02,
+         "mod_bias": r.standard_normal(6 * d) * 0.02}
+    x, m, ctx = r.standard_normal((2, L, d)), r.standard_normal((2, 6 * d)) * 0.3, r.standard_normal((2, Lc, d))
+    exact = O.block(x, m, w, ctx, H)
+    mh8, br = O.multihead_8bit, O.bf16_round
+    calls = []
+
+    def fake(q, k, v, heads, q_scaled=False):
+        calls.append((np.shape(q), np.shape(k)))
+        return O.multihead(q, k, v, heads)
+    try:
+        O.multihead_8bit = fake
+        O.bf16_round = lambda a: np.asarray(a, np.float64)
+        same = O.block(x, m, w, ctx, H, attn8=True)
+    finally:
+        O.multihead_8bit, O.bf16_round = mh8, br
+    assert np.array_equal(same, exact), "attn8 switch changed more than the self-attention"
+    assert len(calls) == 2 and calls[0] == ((L, d), (L, d)), calls
+    # what reaches the 8-bit attention holds bf16 values (R26)
+    seen = []
+    try:
+        def spy(q, k, v, heads, q_scaled=False):
+            seen.append(all(np.array_equal(br(a), np.asarray(a, np.float64)) for a in (q, k, v)))
+            return mh8(q, k, v, heads, q_scaled)
+        O.multihead_8bit = spy
+        O.block(x[:1], m[:1], w, ctx[:1], H, attn8=True)
+    finally:
+        O.multihead_8bit = mh8
+    assert seen == [True], seen
+    # with FP8 Linear layers the switch reaches the self-attention too
+    calls.clear()
+    try:
+        O.multihead_8bit = fake
+        O.block(x, m, w, ctx, H, fp8=True, attn8=True)
+    finally:
+        O.multihead_8bit = mh8
+    assert len(calls) == 2, calls
+    q8 = O.block(x, m, w, ctx, H, attn8=True)
+    upd, upd8 = exact - x, q8 - x
+    rel = np.abs(upd8 - upd).sum() / np.abs(upd).sum()
+    assert 1e-4 < rel < 0.06, rel
+
+
+def pin_attn8_step(O):
+    """The step's 8-bit attention switch reaches the self-attention of every
+    block (two blocks, one sample) and nothing else: with the 8-bit attention
+    replaced by the exact one the step equals the exact step bit for bit."""
+    r = _rng(63)
+    d, F, H, Lc, nb = 64, 128, 2, 5, 2
+
+    def blk():
+        return {"sa_wqkv": r.standard_normal((3 * d, d)) * 0.1, "sa_bqkv": r.standard_normal(3 * d) * 0.02,
+                "sa_wo": r.standard_normal((d, d)) * 0.1, "sa_bo": r.standard_normal(d) * 0.02,
+                "ca_wq": r.standard_normal((d, d)) * 0.1, "ca_bq": r.standard_normal(d) * 0.02,
+                "ca_wkv": r.standard_normal((2 * d, d)) * 0.1, "ca_bkv": r.standard_normal(2 * d) * 0.02,
+                "ca_wo": r.standard_normal((d, d)) * 0.1, "ca_bo": r.standard_normal(d) * 0.02,
+                "ffn_w1": r.standard_normal((F, d)) * 0.1, "ffn_b1": r.standard_normal(F) * 0.02,
+                "ffn_w2": r.standard_normal((d, F)) * 0.1, "ffn_b2": r.standard_normal(d) * 0.02,
+                "mod_bias": r.standard_normal(6 * d) * 0.02}
+    mw = {"patch_w": r.standard_normal((d, 64)) * 0.1, "patch_b": r.standard_normal(d) * 0.02,
+          "tmlp": {"w1": r.standard_normal((d, 256)) * 0.05, "b1": r.standard_normal(d) * 0.02,
+                   "w2": r.standard_normal((6 * d, d)) * 0.05, "b2": r.standard_normal(6 * d) * 0.02},
+          "head_w": r.standard_normal((64, d)) * 0.1, "head_b": r.standard_normal(64) * 0.02,
+          "blocks": [blk() for _ in range(nb)]}
+    lat = r.standard_normal((1, 16, 2, 4, 6))
+    t = np.array([500.0])
+    ctx = r.standard_normal((1, Lc, d))
+    exact = O.step(lat, t, ctx, mw, H)
+    mh8, br = O.multihead_8bit, O.bf16_round
+    calls = []
+    try:
+        def fake(q, k, v, heads, q_scaled=False):
+            calls.append(np.shape(q))
+            return O.multihead(q, k, v, heads)
+        O.multihead_8bit = fake
+        O.bf16_round = lambda a: np.asarray(a, np.float64)
+        same = O.step(lat, t, ctx, mw, H, attn8=True)
+    finally:
+        O.multihead_8bit, O.bf16_round = mh8, br
+    assert np.array_equal(same, exact), "attn8 step switch changed more than the self-attention"
+    assert len(calls) == nb, calls

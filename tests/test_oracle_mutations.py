@@ -59,8 +59,10 @@ MUTATIONS = {
                                 "return linear(gelu_tanh(lin(hmod, w1, b1)), w2, b2)"),
     "fp8 flag dropped for CA": ("wkv_img=wts.get(\"ca_wkv_img\"), bkv_img=wts.get(\"ca_bkv_img\"),\n                             fp8=fp8)",
                                 "wkv_img=wts.get(\"ca_wkv_img\"), bkv_img=wts.get(\"ca_bkv_img\"))"),
-    "fp8 flag not passed to the blocks": ("x = block(x, m, wts, ctx, heads, eps, img=img, fp8=fp8)",
-                                          "x = block(x, m, wts, ctx, heads, eps, img=img)"),
+    "fp8 flag not passed to the blocks": ("x = block(x, m, wts, ctx, heads, eps, img=img, fp8=fp8, attn8=attn8)",
+                                          "x = block(x, m, wts, ctx, heads, eps, img=img, attn8=attn8)"),
+    "attn8 flag not passed to the blocks": ("x = block(x, m, wts, ctx, heads, eps, img=img, fp8=fp8, attn8=attn8)",
+                                            "x = block(x, m, wts, ctx, heads, eps, img=img, fp8=fp8)"),
     "attn8 K scales tiled, not repeated": ("skey = np.repeat(sk, ATTN8_KBLOCK)[:k8.shape[0]]",
                                            "skey = np.resize(sk, k8.shape[0])"),
     "attn8 K block of 32": ("def quantize_k_int8(k, block: int = ATTN8_KBLOCK):",
@@ -76,6 +78,10 @@ MUTATIONS = {
                              "return np.float32(128.0) / amax, amax / np.float32(128.0)"),
     "attn8 pre-scaled q scaled again": ("        S = S / math.sqrt(q8.shape[1])\n        P = ATTN8_PSCALE * np.exp(",
                                         "        S = S / math.sqrt(q8.shape[1])\n        P = ATTN8_PSCALE * np.exp2("),
+    "attn8 switch ignored": ("    if attn8:\n        o = multihead_8bit(", "    if False:\n        o = multihead_8bit("),
+    "attn8 inputs not rounded to bf16": ("o = multihead_8bit(bf16_round(q), bf16_round(k), bf16_round(v), heads)",
+                                         "o = multihead_8bit(q, k, v, heads)"),
+    "attn8 flag not passed to the SA": ("heads, rows=rows, fp8=fp8, attn8=attn8)", "heads, rows=rows, fp8=fp8)"),
     "head split strided": ("k[:, h * hd:(h + 1) * hd],\n                                     v[:, h * hd:(h + 1) * hd])",
                            "k[:, h::heads],\n                                     v[:, h::heads])"),
 }
