@@ -44,9 +44,10 @@ extern "C" {
 #define WAN_ERR_SHAPE     -2  /* sizes inconsistent: odd H/8 or W/8, dim != heads*head_dim,
                                  unsupported head_dim, empty sequence, ...          */
 #define WAN_ERR_DTYPE     -3  /* cfg->dtype is neither WAN_F32 nor WAN_BF16, or is
-                                 WAN_F32 for an FP8 entry point                     */
+                                 WAN_F32 for an FP8 entry point or with cfg->attn8  */
 #define WAN_ERR_WORKSPACE -4  /* ws_bytes smaller than wan_workspace_bytes()         */
-#define WAN_ERR_CONFIG    -5  /* I2V pointers inconsistent with in_ch / img_len      */
+#define WAN_ERR_CONFIG    -5  /* I2V pointers inconsistent with in_ch / img_len, or
+                                 cfg->attn8 neither 0 nor 1                         */
 #define WAN_ERR_HIP       -6  /* a HIP launch failed                                 */
 
 /* operand dtypes */
@@ -69,6 +70,11 @@ typedef struct {
     int img_feat;   /* CLIP feature width (1280), I2V only                    */
     float eps;      /* LayerNorm epsilon (1e-6)                               */
     int dtype;      /* WAN_F32 or WAN_BF16                                    */
+    int attn8;      /* 1: every block's self-attention in 8 bits (Int8 Q K^T, E4M3 P V,
+                       the 8-bit attention below) with bf16 or FP8 Linear layers, the
+                       cross-attention unchanged ([Note] Infra / 推理优化: 8-bit
+                       FlashAttention); WAN_BF16 only (else WAN_ERR_DTYPE).  0: bf16
+                       self-attention.  Other values: WAN_ERR_CONFIG               */
 } wan_cfg_t;
 
 /* Shared timestep MLP ([Note] Diffusion Transformer; [News] 核心创新二):

@@ -184,3 +184,16 @@ def test_attn8_sizes_and_invalid_arguments(W):
                                          dummy, dummy, dummy, dummy, None) == -1
     assert L.wan_attention_8bit_q_fwd(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 100, 2, 3, 100, 70, 0,
                                       None) == -2                           # ldo < H*128
+
+
+def test_attn8_cfg_checks(W):
+    """cfg attn8: bf16 only, 0 or 1, and the block workspace grows by the
+    8-bit copies of q, k, V^T."""
+    c = W.make_cfg(dim=128, heads=2, ffn=256, dtype="f32", attn8=True)
+    assert W.workspace_bytes(c, 1, 2, 4, 4) == 0
+    c = W.make_cfg(dim=256, heads=2, ffn=256, attn8=True)
+    c.attn8 = 2
+    assert W.workspace_bytes(c, 1, 2, 4, 4) == 0
+    c.attn8 = 1
+    base = W.workspace_bytes(W.make_cfg(dim=256, heads=2, ffn=256), 1, 2, 4, 4)
+    assert W.workspace_bytes(c, 1, 2, 4, 4) == base + W.attention_8bit_workspace_bytes(1, 2, 8, 8)

@@ -42,7 +42,7 @@ class WanError(RuntimeError):
 class Cfg(C.Structure):
     _fields_ = [(n, C.c_int) for n in ("dim", "heads", "head_dim", "ffn", "n_blocks", "in_ch",
                                          "out_ch", "freq_dim", "text_len", "img_len", "img_feat")] \
-        + [("eps", C.c_float), ("dtype", C.c_int)]
+        + [("eps", C.c_float), ("dtype", C.c_int), ("attn8", C.c_int)]
 
 
 class TmlpW(C.Structure):
@@ -151,9 +151,9 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_cfg(*, dim, heads, ffn, n_blocks=1, in_ch=16, out_ch=16, freq_dim=256, text_len=512,
-             img_len=0, img_feat=1280, eps=1e-6, dtype="bf16") -> Cfg:
+             img_len=0, img_feat=1280, eps=1e-6, dtype="bf16", attn8=False) -> Cfg:
     return Cfg(dim, heads, dim // heads, ffn, n_blocks, in_ch, out_ch, freq_dim, text_len,
-               img_len, img_feat, eps, WAN_BF16 if dtype == "bf16" else WAN_F32)
+               img_len, img_feat, eps, WAN_BF16 if dtype == "bf16" else WAN_F32, int(bool(attn8)))
 
 
 def workspace_bytes(cfg: Cfg, B: int, lat_f: int, H8: int, W8: int) -> int:

@@ -29,10 +29,68 @@ constexpr size_t ALIGN = 256;
 size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 long rup(long v, long a) { return (v + a - 1) / a * a; }
 
+// ---- 8-bit attention: Int8 / E4M3 copies of q, k, V^T and the attention on them
+
+// byte offsets of the quantised copies in a workspace: q8, qs, k8, ks, v8t, vs, end
+void attn8_offsets(int B, int H, int Lq, int Lk, size_t off[7]) {
+  const size_t d = (size_t)H * 128, Lkp = (size_t)rup(Lk, 64), nkb = Lkp / 64;
+  const size_t sz[6] = {(size_t)B * Lq * d, (size_t)B * Lq * H * 4, (size_t)B * Lk * d,
+                        (size_t)B * H * nkb * 4, d * B * Lkp, (size_t)B * d * 4};
+  size_t o = 0;
+  for (int i = 0; i < 6; ++i) {
+    off[i] = o;
+    o += up(sz[i], ALIGN);
+  }
+  off[6] = o;
+}
+
+// sizes the 8-bit kernels address with 32-bit buffer offsets
+bool attn8_fits(int B, int H, int Lq, int Lk) {
+  const long d = (long)H * 128;
+  return (long)Lk * d < (1L << 31) && d * B * rup(Lk, 64) < (1L << 31) && (long)B * Lq < (1L << 31) / d;
+}
+
+Attn8Desc attn8_desc(const void *q8, const float *qs, const void *k8, const float *ks, const void *v8t,
+                     const float *vs, void *o, int ldo, int B, int H, int Lq, int Lk, bool q_scaled) {
+  Attn8Desc a;
+  a.q8 = static_cast<const int8_t *>(q8); a.ldq8 = (long)H * 128; a.qs = qs;
+  a.k8 = static_cast<const int8_t *>(k8); a.ldk8 = (long)H * 128; a.ks = ks;
+  a.v8t = static_cast<const uint8_t *>(v8t); a.v8_bstride = rup(Lk, 64); a.ldv8 = (long)B * a.v8_bstride;
+  a.vs = vs;
+  a.o = o; a.ldo = ldo;
+  a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk;
+  a.alpha = q_scaled ? 1.0f : 1.4426950408889634f / sqrtf(128.0f);
+  return a;
+}
+
+Attn8Quant attn8_quant(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv, int vt_bstride,
+                       int B, int H, int Lq, int Lk, void *q8, float *qs, void *k8, float *ks, void *v8t,
+                       float *vs) {
+  Attn8Quant z;
+  z.q = q; z.ldq = ldq; z.k = k; z.ldk = ldk; z.vt = vt; z.ldv = ldv; z.vt_bstride = vt_bstride;
+  z.B = B; z.H = H; z.Lq = Lq; z.Lk = Lk;
+  z.q8 = q8; z.ldq8 = (long)H * 128; z.qs = qs;
+  z.k8 = k8; z.ldk8 = (long)H * 128; z.ks = ks;
+  z.v8t = v8t; z.v8_bstride = rup(Lk, 64); z.ldv8 = (long)B * z.v8_bstride; z.vs = vs;
+  return z;
+}
+
+// argument checks shared by the 8-bit entry points taking bf16 q, k, V^T
+int attn8_check_inputs(int ldq, int ldk, int ldv, int vt_bstride, int B, int H, int Lq, int Lk) {
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return WAN_ERR_SHAPE;
+  if (ldq < H * 128 || ldk < H * 128 || ldq % 8 || ldk % 8) return WAN_ERR_SHAPE;
+  if (ldv % 8 || vt_bstride % 8 || vt_bstride < rup(Lk, 64) || (long)ldv < (long)B * vt_bstride)
+    return WAN_ERR_SHAPE;
+  if (!attn8_fits(B, H, Lq, Lk)) return WAN_ERR_SHAPE;
+  return WAN_OK;
+}
+
+
 struct Layout {
   size_t modb, hid, h, qk, vt, o, qc, kc, vtc, ki, vti, acc32, u;   // block
   size_t mod, x, P, pw, img1, img2, imgc;                           // step
   size_t aq, as;                                                    // FP8 activations
+  size_t a8;                                                        // 8-bit attention copies
   size_t total;
   long Lp, Lcp, Lip;
   int Kp;
@@ -75,6 +133,11 @@ Layout make_layout(const wan_cfg_t &c, int B, long L, bool step, bool fp8 = fals
   if (fp8) {   // E4M3 codes of one activation (the widest: FFN hidden) + per-token scales
     y.aq = take(B * L * (F > d ? F : d));
     y.as = take(B * L * 4);
+  }
+  if (c.attn8) {   // Int8 q, k and E4M3 V^T of the self-attention, with their scales
+    size_t o8[7];
+    attn8_offsets(B, c.heads, (int)L, (int)L, o8);
+    y.a8 = take(o8[6]);
   }
   y.total = off;
   return y;
@@ -147,6 +210,8 @@ int check_cfg(const wan_cfg_t *c) {
   if (c->heads * c->head_dim != c->dim) return WAN_ERR_SHAPE;
   if (c->freq_dim % 2) return WAN_ERR_SHAPE;
   if (!(c->eps > 0.f) || !isfinite(c->eps)) return WAN_ERR_SHAPE;
+  if (c->attn8 != 0 && c->attn8 != 1) return WAN_ERR_CONFIG;
+  if (c->attn8 && c->dtype != WAN_BF16) return WAN_ERR_DTYPE;
   if (c->dtype == WAN_BF16) {
     // MFMA tiles: K of every GEMM a multiple of 64; attention head dim 128
     if (c->head_dim != 128 || c->ffn % 64 || c->freq_dim % 8) return WAN_ERR_SHAPE;
@@ -159,10 +224,11 @@ int check_cfg(const wan_cfg_t *c) {
   return WAN_OK;
 }
 
-int check_dims(int B, int lat_f, int Hp, int Wp) {
+int check_dims(const wan_cfg_t &c, int B, int lat_f, int Hp, int Wp) {
   if (B <= 0 || B > 8 || lat_f <= 0 || Hp <= 0 || Wp <= 0) return WAN_ERR_SHAPE;
   const long L = (long)lat_f * Hp * Wp;
   if ((long)B * L > (1L << 30)) return WAN_ERR_SHAPE;
+  if (c.attn8 && !attn8_fits(B, c.heads, (int)L, (int)L)) return WAN_ERR_SHAPE;
   return WAN_OK;
 }
 
@@ -282,6 +348,25 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
     return launch_gemm(fp8(g, q8->as, 1, q8->sc + wi, 0), s);
   };
 
+  // self-attention of the bf16 paths on q | k in qk and V^T in vt: bf16 with
+  // the pre-scaled query, or (cfg attn8) quantised to Int8 / E4M3 and run by
+  // the 8-bit kernel ([Note] Infra / 推理优化: 8-bit FlashAttention)
+  auto self_attn = [&]() -> hipError_t {
+    if (!c.attn8)
+      return launch_attention(attn(qk, 2 * d, off(qk, d, es), 2 * d, vt, (long)B * y.Lp, y.Lp, o, d, B, H,
+                                   (int)L, (int)L, hd, 0, 1), s);
+    char *a8 = ws + y.a8;
+    size_t o8[7];
+    attn8_offsets(B, H, (int)L, (int)L, o8);
+    float *qs8 = (float *)(a8 + o8[1]), *ks8 = (float *)(a8 + o8[3]), *vs8 = (float *)(a8 + o8[5]);
+    hipError_t e = launch_quant_attn8(attn8_quant(qk, 2 * d, off(qk, d, es), 2 * d, vt, (int)((long)B * y.Lp),
+                                                  (int)y.Lp, B, H, (int)L, (int)L, a8 + o8[0], qs8,
+                                                  a8 + o8[2], ks8, a8 + o8[4], vs8), s);
+    if (e != hipSuccess) return e;
+    return launch_attention8(attn8_desc(a8 + o8[0], qs8, a8 + o8[2], ks8, a8 + o8[4], vs8, o, d, B, H,
+                                        (int)L, (int)L, false), s);
+  };
+
   WAN_TRY(launch_mod_combine(mod, w.mod_bias, modb, B, 6 * d, s));
   // ---- self-attention branch
   WAN_TRY(ln(0, d, 1));
@@ -290,9 +375,9 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
     WAN_TRY(launch_attention(attn(qk, 3 * d, off(qk, d, es), 3 * d, off(qk, 2 * d, es), 3 * d, 0,
                                   o, d, B, H, (int)L, (int)L, hd, 1), s));
   } else if (q8) {
-    WAN_TRY(launch_gemm(fp8(qscaled(gemm(q8->aq, d, q8->w[0], d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk,
-                                         2 * d, 0), d, hd),
-                            q8->as, 1, q8->sc + 0, 0), s));
+    // with the 8-bit attention the query stays unscaled (it is quantised per token)
+    GemmDesc gqk = gemm(q8->aq, d, q8->w[0], d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0);
+    WAN_TRY(launch_gemm(fp8(c.attn8 ? gqk : qscaled(gqk, d, hd), q8->as, 1, q8->sc + 0, 0), s));
     for (int b = 0; b < B; ++b) {   // V^T = Wv h_b^T: weight scale per tensor, token scale per column
       GemmDesc g = gemm(q8->w[0] + 2L * d * d, d, q8->aq + (long)b * L * d, d, d, (int)L, d,
                         off(w.sa_bqkv, 2 * d, es), OUT_BF16, vt + b * y.Lp * es, (long)B * y.Lp, 0);
@@ -300,11 +385,10 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
       g.npad = (int)y.Lp;
       WAN_TRY(launch_gemm(fp8(g, q8->sc + 0, 0, q8->as + (long)b * L, 1), s));
     }
-    WAN_TRY(launch_attention(attn(qk, 2 * d, off(qk, d, es), 2 * d, vt, (long)B * y.Lp, y.Lp, o,
-                                  d, B, H, (int)L, (int)L, hd, 0, 1), s));
+    WAN_TRY(self_attn());
   } else {
-    WAN_TRY(launch_gemm(qscaled(gemm(h, d, w.sa_wqkv, d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0),
-                                d, hd), s));
+    GemmDesc gqk = gemm(h, d, w.sa_wqkv, d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0);
+    WAN_TRY(launch_gemm(c.attn8 ? gqk : qscaled(gqk, d, hd), s));
     for (int b = 0; b < B; ++b) {
       GemmDesc g = gemm(off(w.sa_wqkv, 2L * d * d, es), d, off(h, (long)b * L * d, es), d, d,
                         (int)L, d, off(w.sa_bqkv, 2 * d, es), OUT_BF16, vt + b * y.Lp * es,
@@ -313,8 +397,7 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
       g.npad = (int)y.Lp;   // keys L .. Lp-1 of this batch segment are zero
       WAN_TRY(launch_gemm(g, s));
     }
-    WAN_TRY(launch_attention(attn(qk, 2 * d, off(qk, d, es), 2 * d, vt, (long)B * y.Lp, y.Lp, o,
-                                  d, B, H, (int)L, (int)L, hd, 0, 1), s));
+    WAN_TRY(self_attn());
   }
   WAN_TRY(linear(resid(o, d, w.sa_wo, M, d, d, w.sa_bo, x, modb + 2 * d, 6 * d, (int)L, f32), 1,
                  false));
@@ -462,9 +545,9 @@ int step_run(const wan_cfg_t &c, const float *latent, const float *t, int B, int
 }
 
 // latent geometry of a step
-int check_step_dims(int B, int lat_f, int H8, int W8) {
+int check_step_dims(const wan_cfg_t &c, int B, int lat_f, int H8, int W8) {
   if (H8 <= 0 || W8 <= 0 || H8 % 2 || W8 % 2) return WAN_ERR_SHAPE;
-  return check_dims(B, lat_f, H8 / 2, W8 / 2);
+  return check_dims(c, B, lat_f, H8 / 2, W8 / 2);
 }
 
 size_t sample_extra(int B, int out_ch, long plane, size_t *t_off, size_t *v_off, size_t base) {
@@ -513,7 +596,7 @@ const char *wan_status_str(int st) {
 size_t wan_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, int W8) {
   if (check_cfg(cfg) != WAN_OK) return 0;
   if (H8 <= 0 || W8 <= 0 || H8 % 2 || W8 % 2) return 0;
-  if (check_dims(B, lat_f, H8 / 2, W8 / 2) != WAN_OK) return 0;
+  if (check_dims(*cfg, B, lat_f, H8 / 2, W8 / 2) != WAN_OK) return 0;
   const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
   return make_layout(*cfg, B, L, true).total;
 }
@@ -537,7 +620,7 @@ int wan_dit_block_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, 
   int st = check_cfg(cfg);
   if (st) return st;
   if (!x || !mod || !ctx || !ws) return WAN_ERR_NULL;
-  if ((st = check_dims(B, lat_f, Hp, Wp))) return st;
+  if ((st = check_dims(*cfg, B, lat_f, Hp, Wp))) return st;
   if ((st = check_block_weights(*cfg, w))) return st;
   if ((cfg->img_len > 0) != (img_ctx != nullptr)) return WAN_ERR_CONFIG;
   const long L = (long)lat_f * Hp * Wp;
@@ -553,7 +636,7 @@ int wan_dit_step_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, 
   int st = check_cfg(cfg);
   if (st) return st;
   if (!latent || !t || !ctx || !w || !out || !ws) return WAN_ERR_NULL;
-  if ((st = check_step_dims(B, lat_f, H8, W8))) return st;
+  if ((st = check_step_dims(*cfg, B, lat_f, H8, W8))) return st;
   const bool i2v = cfg->img_len > 0;
   if ((st = check_model_weights(*cfg, w, i2v))) return st;
   if (i2v != (clip_feat != nullptr)) return WAN_ERR_CONFIG;
@@ -612,7 +695,7 @@ int wan_dit_step_cached_fwd(const wan_cfg_t *cfg, const float *latent, const flo
   int st = check_cfg(cfg);
   if (st) return st;
   if (!latent || !t || !w || !out || !ws || (!kv_cache && cfg->n_blocks > 0)) return WAN_ERR_NULL;
-  if ((st = check_step_dims(B, lat_f, H8, W8))) return st;
+  if ((st = check_step_dims(*cfg, B, lat_f, H8, W8))) return st;
   if ((st = check_model_weights(*cfg, w, false))) return st;
   if (cache_bytes < kv_layout(*cfg, B).per_block * (size_t)cfg->n_blocks) return WAN_ERR_WORKSPACE;
   const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
@@ -636,7 +719,7 @@ int wan_euler_fwd(float *latent, const float *vel, int B, int in_ch, int out_ch,
 }
 
 size_t wan_sample_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, int W8) {
-  if (check_cfg(cfg) != WAN_OK || check_step_dims(B, lat_f, H8, W8) != WAN_OK) return 0;
+  if (check_cfg(cfg) != WAN_OK || check_step_dims(*cfg, B, lat_f, H8, W8) != WAN_OK) return 0;
   const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
   size_t t_off, v_off;
   return sample_extra(B, cfg->out_ch, (long)lat_f * H8 * W8, &t_off, &v_off,
@@ -649,7 +732,7 @@ int wan_sample_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, int H8
   int st = check_cfg(cfg);
   if (st) return st;
   if (!latent || !w || !ws || (!kv_cache && cfg->n_blocks > 0)) return WAN_ERR_NULL;
-  if ((st = check_step_dims(B, lat_f, H8, W8))) return st;
+  if ((st = check_step_dims(*cfg, B, lat_f, H8, W8))) return st;
   if (n_steps <= 0 || (guided && B != 2) || !isfinite(scale)) return WAN_ERR_SHAPE;
   if (cfg->in_ch < cfg->out_ch) return WAN_ERR_SHAPE;
   if ((st = check_model_weights(*cfg, w, false))) return st;
@@ -694,65 +777,6 @@ int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void
   return WAN_OK;
 }
 
-// ---- 8-bit attention: Int8 / E4M3 copies of q, k, V^T and the attention on them
-
-namespace {
-
-// byte offsets of the quantised copies in a workspace: q8, qs, k8, ks, v8t, vs, end
-void attn8_offsets(int B, int H, int Lq, int Lk, size_t off[7]) {
-  const size_t d = (size_t)H * 128, Lkp = (size_t)rup(Lk, 64), nkb = Lkp / 64;
-  const size_t sz[6] = {(size_t)B * Lq * d, (size_t)B * Lq * H * 4, (size_t)B * Lk * d,
-                        (size_t)B * H * nkb * 4, d * B * Lkp, (size_t)B * d * 4};
-  size_t o = 0;
-  for (int i = 0; i < 6; ++i) {
-    off[i] = o;
-    o += up(sz[i], ALIGN);
-  }
-  off[6] = o;
-}
-
-// sizes the 8-bit kernels address with 32-bit buffer offsets
-bool attn8_fits(int B, int H, int Lq, int Lk) {
-  const long d = (long)H * 128;
-  return (long)Lk * d < (1L << 31) && d * B * rup(Lk, 64) < (1L << 31) && (long)B * Lq < (1L << 31) / d;
-}
-
-Attn8Desc attn8_desc(const void *q8, const float *qs, const void *k8, const float *ks, const void *v8t,
-                     const float *vs, void *o, int ldo, int B, int H, int Lq, int Lk, bool q_scaled) {
-  Attn8Desc a;
-  a.q8 = static_cast<const int8_t *>(q8); a.ldq8 = (long)H * 128; a.qs = qs;
-  a.k8 = static_cast<const int8_t *>(k8); a.ldk8 = (long)H * 128; a.ks = ks;
-  a.v8t = static_cast<const uint8_t *>(v8t); a.v8_bstride = rup(Lk, 64); a.ldv8 = (long)B * a.v8_bstride;
-  a.vs = vs;
-  a.o = o; a.ldo = ldo;
-  a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk;
-  a.alpha = q_scaled ? 1.0f : 1.4426950408889634f / sqrtf(128.0f);
-  return a;
-}
-
-Attn8Quant attn8_quant(const void *q, int ldq, const void *k, int ldk, const void *vt, int ldv, int vt_bstride,
-                       int B, int H, int Lq, int Lk, void *q8, float *qs, void *k8, float *ks, void *v8t,
-                       float *vs) {
-  Attn8Quant z;
-  z.q = q; z.ldq = ldq; z.k = k; z.ldk = ldk; z.vt = vt; z.ldv = ldv; z.vt_bstride = vt_bstride;
-  z.B = B; z.H = H; z.Lq = Lq; z.Lk = Lk;
-  z.q8 = q8; z.ldq8 = (long)H * 128; z.qs = qs;
-  z.k8 = k8; z.ldk8 = (long)H * 128; z.ks = ks;
-  z.v8t = v8t; z.v8_bstride = rup(Lk, 64); z.ldv8 = (long)B * z.v8_bstride; z.vs = vs;
-  return z;
-}
-
-// argument checks shared by the 8-bit entry points taking bf16 q, k, V^T
-int attn8_check_inputs(int ldq, int ldk, int ldv, int vt_bstride, int B, int H, int Lq, int Lk) {
-  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return WAN_ERR_SHAPE;
-  if (ldq < H * 128 || ldk < H * 128 || ldq % 8 || ldk % 8) return WAN_ERR_SHAPE;
-  if (ldv % 8 || vt_bstride % 8 || vt_bstride < rup(Lk, 64) || (long)ldv < (long)B * vt_bstride)
-    return WAN_ERR_SHAPE;
-  if (!attn8_fits(B, H, Lq, Lk)) return WAN_ERR_SHAPE;
-  return WAN_OK;
-}
-
-}  // namespace
 
 size_t wan_attention_8bit_workspace_bytes(int B, int H, int Lq, int Lk) {
   if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || !attn8_fits(B, H, Lq, Lk)) return 0;
@@ -860,7 +884,7 @@ int wan_quantize_block_fp8(const wan_cfg_t *cfg, const wan_block_weights_t *w, v
 
 size_t wan_block_fp8_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int Hp, int Wp) {
   if (check_cfg(cfg) != WAN_OK || cfg->dtype != WAN_BF16) return 0;
-  if (check_dims(B, lat_f, Hp, Wp) != WAN_OK) return 0;
+  if (check_dims(*cfg, B, lat_f, Hp, Wp) != WAN_OK) return 0;
   return make_layout(*cfg, B, (long)lat_f * Hp * Wp, false, true).total;
 }
 
@@ -873,7 +897,7 @@ int wan_dit_block_fp8_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int 
   if (cfg->dtype != WAN_BF16) return WAN_ERR_DTYPE;
   if (!x || !mod || !ctx || !ws || !qbuf) return WAN_ERR_NULL;
   if ((uintptr_t)qbuf % ALIGN) return WAN_ERR_SHAPE;
-  if ((st = check_dims(B, lat_f, Hp, Wp))) return st;
+  if ((st = check_dims(*cfg, B, lat_f, Hp, Wp))) return st;
   if ((st = check_block_weights(*cfg, w, true))) return st;
   if ((cfg->img_len > 0) != (img_ctx != nullptr)) return WAN_ERR_CONFIG;
   const long L = (long)lat_f * Hp * Wp;
@@ -912,7 +936,7 @@ int wan_quantize_model_fp8(const wan_cfg_t *cfg, const wan_model_weights_t *w, v
 
 size_t wan_fp8_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, int W8, int sampler) {
   if (check_cfg(cfg) != WAN_OK || cfg->dtype != WAN_BF16) return 0;
-  if (check_step_dims(B, lat_f, H8, W8) != WAN_OK) return 0;
+  if (check_step_dims(*cfg, B, lat_f, H8, W8) != WAN_OK) return 0;
   const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
   const size_t base = make_layout(*cfg, B, L, true, true).total;
   if (!sampler) return base;
@@ -929,7 +953,7 @@ int wan_dit_step_fp8_fwd(const wan_cfg_t *cfg, const float *latent, const float 
   if (cfg->dtype != WAN_BF16) return WAN_ERR_DTYPE;
   if (!latent || !t || !ctx || !w || !out || !ws || (!qbuf && cfg->n_blocks > 0)) return WAN_ERR_NULL;
   if ((uintptr_t)qbuf % ALIGN) return WAN_ERR_SHAPE;
-  if ((st = check_step_dims(B, lat_f, H8, W8))) return st;
+  if ((st = check_step_dims(*cfg, B, lat_f, H8, W8))) return st;
   const bool i2v = cfg->img_len > 0;
   if ((st = check_model_weights(*cfg, w, i2v, true))) return st;
   if (i2v != (clip_feat != nullptr)) return WAN_ERR_CONFIG;
@@ -950,7 +974,7 @@ int wan_sample_fp8_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, in
   if (cfg->dtype != WAN_BF16) return WAN_ERR_DTYPE;
   if (!latent || !w || !ws || ((!kv_cache || !qbuf) && cfg->n_blocks > 0)) return WAN_ERR_NULL;
   if ((uintptr_t)qbuf % ALIGN) return WAN_ERR_SHAPE;
-  if ((st = check_step_dims(B, lat_f, H8, W8))) return st;
+  if ((st = check_step_dims(*cfg, B, lat_f, H8, W8))) return st;
   if (n_steps <= 0 || (guided && B != 2) || !isfinite(scale)) return WAN_ERR_SHAPE;
   if (cfg->in_ch < cfg->out_ch) return WAN_ERR_SHAPE;
   if ((st = check_model_weights(*cfg, w, false, true))) return st;
