@@ -317,11 +317,13 @@ def fp8_block_bench(steps: int, warmup: int):
           flush=True)
 
 
-def fp8_block_leg(W, cfg, work, bwd, mod, ctx, stream, steps, warmup, bf16_ms, tmlp):
+def fp8_block_leg(W, cfg, work, bwd, mod, ctx, stream, steps, warmup, bf16_ms, tmlp,
+                  label="fp8 e4m3 Linear layers, bf16 attention"):
     """Time the step with wan_dit_block_fp8_fwd in place of the bf16 block (the
     same t-MLP call first; weights quantised once beforehand; the per-token
     activation quantisation is inside the timed region), on its own copy of
-    the residual stream."""
+    the residual stream.  With cfg.attn8 the self-attention runs in 8 bits
+    (its Int8 / E4M3 quantisation inside the timed region too)."""
     import torch
     desc = W.block_weights(bwd)
     qbuf = torch.empty(W.block_fp8_bytes(cfg), dtype=torch.uint8, device="cuda")
@@ -347,7 +349,47 @@ def fp8_block_leg(W, cfg, work, bwd, mod, ctx, stream, steps, warmup, bf16_ms, t
     if not bool(torch.isfinite(x).all()):
         raise RuntimeError("non-finite FP8 block output")
     return {"ms_per_step": round(ms8, 4), "tokens_per_s": round(work.batch * work.L / (ms8 * 1e-3), 1),
-            "speedup_vs_bf16": round(bf16_ms / ms8, 4), "dtype": "fp8 e4m3 Linear layers, bf16 attention"}
+            "speedup_vs_bf16": round(bf16_ms / ms8, 4), "dtype": label}
+
+
+def attn8_leg(W, B, L, d, H, qk, vt, Lp, stream, n_att, bf16_attn_ms, sa_f):
+    """The 8-bit self-attention kernel on its own (Int8 / E4M3 copies of the
+    same q, k, V^T made once), timed with HIP events on the launch stream,
+    and the three quantisers it needs, timed separately."""
+    import torch
+    D, nkb = H * 128, Lp // 64
+    q8 = torch.empty((B * L, D), dtype=torch.int8, device="cuda")
+    qs = torch.empty((B * L, H), dtype=torch.float32, device="cuda")
+    k8 = torch.empty((B * L, D), dtype=torch.int8, device="cuda")
+    ks = torch.empty((B, H, nkb), dtype=torch.float32, device="cuda")
+    v8 = torch.empty((D, B * Lp), dtype=torch.uint8, device="cuda")
+    vs = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    o = torch.empty((B * L, d), dtype=torch.bfloat16, device="cuda")
+    quant = lambda: W.attention_8bit_quantize(qk, 2 * d, qk[:, d:], 2 * d, vt, B * Lp, Lp, B, H, L, L, q8, qs,
+                                              k8, ks, v8, vs, stream)
+    run = lambda: W.attention_8bit_q_fwd(q8, qs, k8, ks, v8, vs, o, d, B, H, L, L, q_scaled=True,
+                                         stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, f in (("quant", quant), ("attn", run)):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n_att):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / n_att
+    if not bool(torch.isfinite(o.float()).all()):
+        raise RuntimeError("non-finite 8-bit attention output")
+    tf = sa_f / (res["attn"] * 1e-3) / 1e12
+    return {"kernel": "k_attn_i8f8", "launch_ms": round(res["attn"], 4), "tflops": round(tf, 1),
+            "peak": PEAK_FP8_TFLOPS, "frac_of_8bit_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "quantise_ms": round(res["quant"], 4),
+            "speedup_vs_bf16_attention": round(bf16_attn_ms / res["attn"], 4),
+            "speedup_incl_quantise": round(bf16_attn_ms / (res["attn"] + res["quant"]), 4)}
 
 
 def main():
@@ -502,8 +544,15 @@ def main():
         "wall_s_timed": round(t_wall, 3),
     }
     if m.dtype == "bf16":   # the same block with its six Linear layers in FP8 (E4M3), same inputs
-        out["fp8_block"] = fp8_block_leg(W, cfg, work, bwd, mod, ctx, stream, args.steps, args.warmup, ms,
-                                         lambda: W.tmlp_fwd(cfg, t, tws_c, mod, tws, stream))
+        tm = lambda: W.tmlp_fwd(cfg, t, tws_c, mod, tws, stream)
+        out["fp8_block"] = fp8_block_leg(W, cfg, work, bwd, mod, ctx, stream, args.steps, args.warmup, ms, tm)
+        # ... and with the 8-bit self-attention as well
+        cfg8 = W.make_cfg(dim=d, heads=H, ffn=F, n_blocks=1, text_len=m.text_len, eps=m.eps, dtype=m.dtype,
+                          attn8=True)
+        out["fp8_attn8_block"] = fp8_block_leg(W, cfg8, work, bwd, mod, ctx, stream, args.steps, args.warmup,
+                                               ms, tm, "fp8 e4m3 Linear layers, 8-bit self-attention "
+                                                       "(Int8 QK^T, E4M3 PV)")
+        out["attn8"] = attn8_leg(W, B, L, d, H, qk, vt, Lp, stream, n_att, attn_ms, sa_f)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work, inp, tw, bw)
     print(json.dumps(out), flush=True)
