@@ -189,7 +189,20 @@ def sampler_bench(n_steps: int, warmup: int):
     fp8_ms = timed(lambda: W.sample_fp8_fwd(cfg, lat, n_steps, cache, mws, qbuf, ws8, True, 5.0, stream))
     if not bool(torch.isfinite(lat).all()):
         raise RuntimeError("non-finite FP8 sample")
-    per_c, per_p, per_8 = cached_ms / n_steps, plain_ms / n_steps, fp8_ms / n_steps
+    # ... and with every block's self-attention in 8 bits as well (cfg attn8)
+    cfg8 = W.make_cfg(dim=m.dim, heads=m.heads, ffn=m.ffn, n_blocks=m.n_blocks, in_ch=m.in_ch,
+                      out_ch=m.out_ch, freq_dim=m.freq_dim, text_len=m.text_len, eps=m.eps,
+                      dtype=m.dtype, attn8=True)
+    del ws8
+    ws8 = torch.empty(W.fp8_workspace_bytes(cfg8, B, work.lat_f, work.lat_h, work.lat_w, True),
+                      dtype=torch.uint8, device="cuda")
+    lat = lat0.clone()
+    W.sample_fp8_fwd(cfg8, lat, warmup, cache, mws, qbuf, ws8, True, 5.0, stream)
+    lat = lat0.clone()
+    a8_ms = timed(lambda: W.sample_fp8_fwd(cfg8, lat, n_steps, cache, mws, qbuf, ws8, True, 5.0, stream))
+    if not bool(torch.isfinite(lat).all()):
+        raise RuntimeError("non-finite FP8 + 8-bit attention sample")
+    per_c, per_p, per_8, per_a8 = cached_ms / n_steps, plain_ms / n_steps, fp8_ms / n_steps, a8_ms / n_steps
     print(json.dumps({
         "sampler": "wan1.3b-480p guidance pair (30 blocks, B=2, L=32760, 512 text tokens)",
         "steps": n_steps, "guidance": 5.0,
@@ -199,7 +212,8 @@ def sampler_bench(n_steps: int, warmup: int):
         "latent_tokens_per_s_cached": round(B * L / (per_c * 1e-3), 1),
         "ms_per_step_cached_fp8_blocks": round(per_8, 3), "fp8_speedup": round(per_c / per_8, 4),
         "fp8_weight_quantisation_ms": round(quant_ms, 3),
-        "dtype": "bf16 (and fp8 e4m3 block Linear layers)",
+        "ms_per_step_cached_fp8_attn8": round(per_a8, 3), "fp8_attn8_speedup": round(per_c / per_a8, 4),
+        "dtype": "bf16 (and fp8 e4m3 block Linear layers; and 8-bit self-attention)",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latent and text)",
     }), flush=True)
 
