@@ -103,7 +103,8 @@ def test_attention_prescaled_query(B, H, Lq, Lk):
     assert_parity(g, o, 3e-2, 1e-2, f"attention pre-scaled {B},{H},{Lq},{Lk}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (300, 256, 192), (513, 320, 64), (257, 512, 1280)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (77, 128, 64), (300, 256, 192), (513, 320, 64), (257, 512, 1280),
+                                   (512, 1536, 1536)])
 @pytest.mark.parametrize("mode", [0, 1, 2])
 def test_linear(M, N, K, mode):
     print(f"linear M={M} N={N} K={K} mode={mode}", flush=True)

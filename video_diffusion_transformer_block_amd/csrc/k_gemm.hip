@@ -615,8 +615,93 @@ static void gemm_go(const GemmDesc &g, hipStream_t s) {
   }
 }
 
+// Small GEMMs (the text / image K and V^T projections, the image MLP: M or N
+// of a few hundred, a few dozen 256x256 tiles -- too few workgroups for the
+// kernel above): 64x64 output tiles, four wavefronts of 32x32, operands
+// straight from global memory / L2 into registers -- one 16-byte load per lane
+// and operand per 16-deep K step, SPF steps ahead -- and one
+// v_mfma_f32_32x32x16_bf16 per step.  As above the tile is computed transposed,
+// so a lane stores runs of 4 consecutive columns of one output row.
+constexpr int SBM = 64, SBN = 64, SPF = 4;
+static_assert(64 % (16 * SPF) == 0, "K % 64 == 0 must make K / 16 a multiple of SPF");
+template <int KIND, bool BROWS>
+__global__ __launch_bounds__(256) void k_gemm_small(GemmDesc g) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int ncover = g.npad > g.N ? g.npad : g.N;
+  const int tiles_n = (ncover + SBN - 1) / SBN;
+  const int m0 = (int)(blockIdx.x / tiles_n) * SBM + (w >> 1) * 32;
+  const int n0 = (int)(blockIdx.x % tiles_n) * SBN + (w & 1) * 32;
+  // this lane's A row (output row) and B row (output column), clamped into the matrices
+  const bf16 *pa = reinterpret_cast<const bf16 *>(g.A) + (long)min(m0 + l32, g.M - 1) * g.lda + half * 8;
+  const bf16 *pb = reinterpret_cast<const bf16 *>(g.B) + (long)min(n0 + l32, g.N - 1) * g.ldb + half * 8;
+  const int KS = g.K / 16;   // a multiple of SPF (K % 64 == 0)
+  bf16x8 fa[SPF], fb[SPF];
+#pragma unroll
+  for (int i = 0; i < SPF; ++i) {
+    const uint4 ua = ld16(pa + i * 16), ub = ld16(pb + i * 16);
+    fa[i] = *reinterpret_cast<const bf16x8 *>(&ua);
+    fb[i] = *reinterpret_cast<const bf16x8 *>(&ub);
+  }
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int k0 = 0; k0 < KS; k0 += SPF) {
+#pragma unroll
+    for (int i = 0; i < SPF; ++i) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[i], acc, 0, 0, 0);
+      if (k0 + i + SPF < KS) {
+        const uint4 ua = ld16(pa + (k0 + i + SPF) * 16), ub = ld16(pb + (k0 + i + SPF) * 16);
+        fa[i] = *reinterpret_cast<const bf16x8 *>(&ua);
+        fb[i] = *reinterpret_cast<const bf16x8 *>(&ub);
+      }
+    }
+  }
+  // lane holds output row m0 + l32, columns n0 + 8 rb + 4 half + 0..3 (rb = 0..3)
+  const int m = m0 + l32;
+  if (m >= g.M) return;
+  const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
+  const float rbias = BROWS && bias ? (float)bias[m] : 0.f;
+  bf16 *crow = reinterpret_cast<bf16 *>(g.C) + (long)m * g.ldc;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int n = n0 + rb * 8 + half * 4;
+    if (n >= ncover) continue;
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nq = n + q < g.N ? n + q : g.N - 1;
+      v[q] = acc[rb * 4 + q] + (BROWS ? rbias : (bias ? (float)bias[nq] : 0.f));
+      if (KIND == OUT_GELU) v[q] = gelu_tanh(v[q]);
+      if (KIND == OUT_BF16 && n + q < g.scale_cols) v[q] *= g.col_scale;
+    }
+    if (n + 4 <= g.N) {
+      bf16x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = f2bf(v[q]);
+      *reinterpret_cast<bf16x4 *>(crow + n) = o;
+    } else {
+      for (int q = 0; q < 4 && n + q < ncover; ++q) crow[n + q] = n + q < g.N ? f2bf(v[q]) : f2bf(0.f);
+    }
+  }
+}
+
 hipError_t launch_gemm(const GemmDesc &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  // few tiles of the main kernel and a weight of at most 1536 x 1536 (larger
+  // ones, re-read from L2 by every 64-row tile, run faster on the main kernel):
+  // the small-GEMM kernel (bf16 / GELU outputs)
+  if (!g.fp8 && !g.f32 && (g.kind == OUT_BF16 || g.kind == OUT_GELU) && !(g.bias_rows && g.kind != OUT_BF16) &&
+      g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.ldc % 4 == 0 &&
+      (long)((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN) < 64 &&
+      (long)(g.M > g.N ? g.M : g.N) * g.K <= 1536L * 1536) {
+    const int ncover = g.npad > g.N ? g.npad : g.N;
+    const int blocks = ((g.M + SBM - 1) / SBM) * ((ncover + SBN - 1) / SBN);
+    if (g.bias_rows) k_gemm_small<OUT_BF16, true><<<blocks, 256, 0, s>>>(g);
+    else if (g.kind == OUT_GELU) k_gemm_small<OUT_GELU, false><<<blocks, 256, 0, s>>>(g);
+    else k_gemm_small<OUT_BF16, false><<<blocks, 256, 0, s>>>(g);
+    return hipGetLastError();
+  }
   if (g.fp8) {
     if (g.K % 64 || !g.a_scale || !g.b_scale || g.f32) return hipErrorInvalidValue;
     if (g.b_per_col && !g.bias_rows) return hipErrorInvalidValue;   // per-column scales: token columns only
