@@ -184,6 +184,11 @@ def test_attn8_sizes_and_invalid_arguments(W):
                                          dummy, dummy, dummy, dummy, None) == -1
     assert L.wan_attention_8bit_q_fwd(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 100, 2, 3, 100, 70, 0,
                                       None) == -2                           # ldo < H*128
+    # a head count whose row width does not fit an int is a shape error, not an overflow
+    assert L.wan_attention_8bit_fwd(dummy, 384, dummy, 384, dummy, 256, 128, dummy, 384, 2, 1 << 25, 100, 70,
+                                    0, dummy, ws, None) == -2
+    assert L.wan_attention_fwd(dummy, 384, dummy, 384, dummy, 256, 128, dummy, 384, 2, 1 << 25, 100, 70, 0,
+                               None) == -2
 
 
 def test_attn8_cfg_checks(W):

@@ -78,7 +78,7 @@ Attn8Quant attn8_quant(const void *q, int ldq, const void *k, int ldk, const voi
 // argument checks shared by the 8-bit entry points taking bf16 q, k, V^T
 int attn8_check_inputs(int ldq, int ldk, int ldv, int vt_bstride, int B, int H, int Lq, int Lk) {
   if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return WAN_ERR_SHAPE;
-  if (ldq < H * 128 || ldk < H * 128 || ldq % 8 || ldk % 8) return WAN_ERR_SHAPE;
+  if (ldq < (long)H * 128 || ldk < (long)H * 128 || ldq % 8 || ldk % 8) return WAN_ERR_SHAPE;
   if (ldv % 8 || vt_bstride % 8 || vt_bstride < rup(Lk, 64) || (long)ldv < (long)B * vt_bstride)
     return WAN_ERR_SHAPE;
   if (!attn8_fits(B, H, Lq, Lk)) return WAN_ERR_SHAPE;
@@ -768,7 +768,7 @@ int wan_attention_fwd(const void *q, int ldq, const void *k, int ldk, const void
                       void *stream) {
   if (!q || !k || !vt || !o) return WAN_ERR_NULL;
   if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return WAN_ERR_SHAPE;
-  if (ldq < H * 128 || ldk < H * 128 || ldo < H * 128 || ldq % 8 || ldk % 8 || ldo % 4)
+  if (ldq < (long)H * 128 || ldk < (long)H * 128 || ldo < (long)H * 128 || ldq % 8 || ldk % 8 || ldo % 4)
     return WAN_ERR_SHAPE;
   if (ldv % 8 || vt_bstride % 8 || vt_bstride < rup(Lk, 64) || (long)ldv < (long)B * vt_bstride)
     return WAN_ERR_SHAPE;
@@ -800,7 +800,7 @@ int wan_attention_8bit_q_fwd(const void *q8, const float *qs, const void *k8, co
                              const float *vs, void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled,
                              void *stream) {
   if (!q8 || !qs || !k8 || !ks || !v8t || !vs || !o) return WAN_ERR_NULL;
-  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || ldo < H * 128 || ldo % 4) return WAN_ERR_SHAPE;
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || ldo < (long)H * 128 || ldo % 4) return WAN_ERR_SHAPE;
   if (!attn8_fits(B, H, Lq, Lk)) return WAN_ERR_SHAPE;
   WAN_TRY(launch_attention8(attn8_desc(q8, qs, k8, ks, v8t, vs, o, ldo, B, H, Lq, Lk, q_scaled != 0), S(stream)));
   return WAN_OK;
@@ -812,7 +812,7 @@ int wan_attention_8bit_fwd(const void *q, int ldq, const void *k, int ldk, const
   if (!q || !k || !vt || !o || !ws) return WAN_ERR_NULL;
   int st = attn8_check_inputs(ldq, ldk, ldv, vt_bstride, B, H, Lq, Lk);
   if (st != WAN_OK) return st;
-  if (ldo < H * 128 || ldo % 4) return WAN_ERR_SHAPE;
+  if (ldo < (long)H * 128 || ldo % 4) return WAN_ERR_SHAPE;
   size_t off[7];
   attn8_offsets(B, H, Lq, Lk, off);
   if (ws_bytes < off[6]) return WAN_ERR_WORKSPACE;
