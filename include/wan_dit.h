@@ -113,7 +113,12 @@ typedef struct {
 } wan_model_weights_t;
 
 /* Workspace bytes needed by any entry point for batch B and a latent of
- * lat_f x H8 x W8 (H8 = H/8, W8 = W/8).  Returns 0 for an invalid cfg/shape. */
+ * lat_f x H8 x W8 (H8 = H/8, W8 = W/8).  Returns 0 for an invalid cfg/shape.
+ * Shapes every entry point accepts (WAN_ERR_SHAPE otherwise): B <= 8,
+ * B * L <= 2^30 tokens; for bf16 also L * max(ffn, 2d) * 2 bytes (one sample's
+ * largest GEMM operand) and d * B * round_up(L, 64) * 2 bytes (the
+ * self-attention's V^T) below 2^31.  A GEMM operand of several samples that
+ * reaches 2 GiB runs as launches over groups of samples. */
 size_t wan_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, int W8);
 
 /* Human-readable text of a status code (static storage). */
@@ -346,7 +351,8 @@ size_t wan_block_fp8_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int
 /* wan_dit_block_fwd with FP8 Linear layers.  Arguments as there, plus qbuf
  * written by wan_quantize_block_fp8 from the same w.  From w only the biases,
  * mod_bias and the text / image K/V weights are read: the six quantised weight
- * pointers may be NULL.  B * L * max(d, ffn) < 2^31. */
+ * pointers may be NULL.  L * max(d, ffn) < 2^31 (one sample's FP8 operands;
+ * larger batches are split into launches over samples). */
 int wan_dit_block_fp8_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, int Wp,
                           const float *mod, const wan_block_weights_t *w, const void *qbuf,
                           const void *ctx, const void *img_ctx, void *ws, size_t ws_bytes,
@@ -372,7 +378,8 @@ size_t wan_fp8_workspace_bytes(const wan_cfg_t *cfg, int B, int lat_f, int H8, i
 
 /* wan_dit_step_fwd with FP8 blocks: arguments as there, plus qbuf from
  * wan_quantize_model_fp8 for the same w (the blocks' six quantised weight
- * pointers are not read and may be NULL).  B * L * max(d, ffn) < 2^31. */
+ * pointers are not read and may be NULL).  L * max(d, ffn) < 2^31 (one
+ * sample's FP8 operands; larger batches are split into launches over samples). */
 int wan_dit_step_fp8_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, int B,
                          int lat_f, int H8, int W8, const void *ctx, const void *clip_feat,
                          const wan_model_weights_t *w, const void *qbuf, float *out, void *ws,

@@ -191,6 +191,18 @@ def test_attn8_sizes_and_invalid_arguments(W):
                                None) == -2
 
 
+def test_size_limits(W):
+    """Shapes the 32-bit operand offsets allow: the 14B block at 720P takes a
+    guided pair in bf16 (V^T of both samples under 2 GiB) but not three
+    samples; in FP8 only one sample's operands must fit."""
+    c = W.make_cfg(dim=5120, heads=40, ffn=13824)
+    assert W.workspace_bytes(c, 2, 21, 90, 160) > 0
+    assert W.workspace_bytes(c, 3, 21, 90, 160) == 0
+    assert W.fp8_workspace_bytes(c, 2, 21, 90, 160) > 0
+    # one sample whose FFN hidden state reaches 2 GiB (L * ffn * 2 bytes)
+    assert W.workspace_bytes(c, 1, 21, 96, 160) == 0
+
+
 def test_attn8_cfg_checks(W):
     """cfg attn8: bf16 only, 0 or 1, and the block workspace grows by the
     8-bit copies of q, k, V^T."""

@@ -686,7 +686,9 @@ __global__ __launch_bounds__(256) void k_gemm_small(GemmDesc g) {
   }
 }
 
-hipError_t launch_gemm(const GemmDesc &g, hipStream_t s) {
+namespace {
+
+hipError_t launch_gemm_one(const GemmDesc &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   // few tiles of the main kernel and a weight of at most 1536 x 1536 (larger
   // ones, re-read from L2 by every 64-row tile, run faster on the main kernel):
@@ -735,6 +737,70 @@ hipError_t launch_gemm(const GemmDesc &g, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+// The bf16 and FP8 kernels address A and B with 32-bit byte offsets.  An
+// operand of 2 GiB or more (the token side of a large batch: the FFN hidden
+// state of several samples) is split here into launches over row or column
+// slices, each operand slice below 2 GiB, each launch writing its own slice of
+// the output.  The gated residual's gate is per batch sample, so row slices of
+// that GEMM start at sample boundaries.
+hipError_t launch_gemm(const GemmDesc &g, hipStream_t s) {
+  if (g.f32 || g.M <= 0 || g.N <= 0) return launch_gemm_one(g, s);
+  const long eb = g.fp8 ? 1 : 2;                       // operand element bytes
+  const long ob = g.kind == OUT_F32 ? 4 : 2;           // C element bytes (not OUT_RESID)
+  const long lim = (1L << 31) - 1;
+  if (g.lda <= 0 || g.ldb <= 0) return hipErrorInvalidValue;
+  if ((long)g.M * g.lda * eb > lim) {
+    long rows = lim / (g.lda * eb);
+    if (g.kind == OUT_RESID && g.gate)
+      rows = g.rows_per_batch > 0 ? rows / g.rows_per_batch * g.rows_per_batch : 0;
+    else
+      rows = rows / GBM * GBM;
+    if (rows <= 0) return hipErrorInvalidValue;
+    for (long m0 = 0; m0 < g.M; m0 += rows) {
+      GemmDesc c = g;
+      c.M = (int)(g.M - m0 < rows ? g.M - m0 : rows);
+      c.A = static_cast<const char *>(g.A) + m0 * g.lda * eb;
+      if (g.kind == OUT_RESID) {
+        c.X = g.X + m0 * g.ldx;
+        if (g.gate) c.gate = g.gate + (m0 / g.rows_per_batch) * g.gate_bstride;
+      } else {
+        c.C = static_cast<char *>(g.C) + m0 * g.ldc * ob;
+      }
+      if (g.bias_rows && g.bias) c.bias = static_cast<const bf16 *>(g.bias) + m0;
+      if (g.fp8 && g.a_per_row) c.a_scale = g.a_scale + m0;
+      const hipError_t e = launch_gemm(c, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  if ((long)g.N * g.ldb * eb > lim) {
+    const long cols = lim / (g.ldb * eb) / GBN * GBN;
+    if (cols <= 0) return hipErrorInvalidValue;
+    for (long n0 = 0; n0 < g.N; n0 += cols) {
+      GemmDesc c = g;
+      c.N = (int)(g.N - n0 < cols ? g.N - n0 : cols);
+      const bool last = n0 + cols >= g.N;
+      c.B = static_cast<const char *>(g.B) + n0 * g.ldb * eb;
+      if (g.kind == OUT_RESID) {
+        c.X = g.X + n0;
+        if (g.gate) c.gate = g.gate + n0;
+      } else {
+        c.C = static_cast<char *>(g.C) + n0 * ob;
+      }
+      if (!g.bias_rows && g.bias) c.bias = static_cast<const bf16 *>(g.bias) + n0;
+      if (g.fp8 && g.b_per_col) c.b_scale = g.b_scale + n0;
+      c.npad = last && g.npad > g.N ? (int)(g.npad - n0) : 0;
+      c.scale_cols = g.scale_cols > n0 ? (int)(g.scale_cols - n0) : 0;
+      const hipError_t e = launch_gemm_one(c, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  return launch_gemm_one(g, s);
 }
 
 }  // namespace wan

@@ -207,7 +207,7 @@ int check_cfg(const wan_cfg_t *c) {
   if (c->dim <= 0 || c->heads <= 0 || c->head_dim <= 0 || c->ffn <= 0 || c->n_blocks < 0 ||
       c->in_ch <= 0 || c->out_ch <= 0 || c->freq_dim <= 0 || c->text_len <= 0 || c->img_len < 0)
     return WAN_ERR_SHAPE;
-  if (c->heads * c->head_dim != c->dim) return WAN_ERR_SHAPE;
+  if ((long)c->heads * c->head_dim != c->dim) return WAN_ERR_SHAPE;
   if (c->freq_dim % 2) return WAN_ERR_SHAPE;
   if (!(c->eps > 0.f) || !isfinite(c->eps)) return WAN_ERR_SHAPE;
   if (c->attn8 != 0 && c->attn8 != 1) return WAN_ERR_CONFIG;
@@ -229,6 +229,15 @@ int check_dims(const wan_cfg_t &c, int B, int lat_f, int Hp, int Wp) {
   const long L = (long)lat_f * Hp * Wp;
   if ((long)B * L > (1L << 30)) return WAN_ERR_SHAPE;
   if (c.attn8 && !attn8_fits(B, c.heads, (int)L, (int)L)) return WAN_ERR_SHAPE;
+  if (c.dtype == WAN_BF16) {
+    // the MFMA kernels address operands with 32-bit byte offsets: a GEMM
+    // operand of 2 GiB or more is split at sample boundaries, so one sample's
+    // (the FFN hidden state, Q||K) must fit; the self-attention's V^T of all
+    // samples is one operand
+    const long wmax = c.ffn > 2L * c.dim ? c.ffn : 2L * c.dim;
+    if (L * wmax * 2 >= (1L << 31)) return WAN_ERR_SHAPE;
+    if ((long)c.dim * B * rup(L, 64) * 2 >= (1L << 31)) return WAN_ERR_SHAPE;
+  }
   return WAN_OK;
 }
 
@@ -846,7 +855,6 @@ int wan_linear_fp8_fwd(const void *xq, const float *x_scale, const void *wq, con
                        const void *b, void *y, int M, int N, int K, int mode, void *stream) {
   if (!xq || !x_scale || !wq || !w_scale || !y) return WAN_ERR_NULL;
   if (M <= 0 || N <= 0 || K <= 0 || K % 64) return WAN_ERR_SHAPE;
-  if ((long)M * K >= (1L << 31) || (long)N * K >= (1L << 31)) return WAN_ERR_SHAPE;
   int kind = mode == 0 ? OUT_BF16 : mode == 1 ? OUT_F32 : mode == 2 ? OUT_GELU : -1;
   if (kind < 0) return WAN_ERR_CONFIG;
   GemmDesc g = gemm(xq, K, wq, K, M, N, K, b, kind, y, N, 0);
@@ -901,8 +909,8 @@ int wan_dit_block_fp8_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int 
   if ((st = check_block_weights(*cfg, w, true))) return st;
   if ((cfg->img_len > 0) != (img_ctx != nullptr)) return WAN_ERR_CONFIG;
   const long L = (long)lat_f * Hp * Wp;
-  // the FP8 GEMM addresses its operands with 32-bit byte offsets
-  if ((long)B * L * (cfg->ffn > cfg->dim ? cfg->ffn : cfg->dim) >= (1L << 31)) return WAN_ERR_SHAPE;
+  // one sample's FP8 operands below 2 GiB (larger GEMMs are split at samples)
+  if (L * (cfg->ffn > cfg->dim ? cfg->ffn : cfg->dim) >= (1L << 31)) return WAN_ERR_SHAPE;
   Layout y = make_layout(*cfg, B, L, false, true);
   if (ws_bytes < y.total) return WAN_ERR_WORKSPACE;
   const Fp8Layout ql = fp8_layout(*cfg);
@@ -958,7 +966,7 @@ int wan_dit_step_fp8_fwd(const wan_cfg_t *cfg, const float *latent, const float 
   if ((st = check_model_weights(*cfg, w, i2v, true))) return st;
   if (i2v != (clip_feat != nullptr)) return WAN_ERR_CONFIG;
   const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
-  if ((long)B * L * (cfg->ffn > cfg->dim ? cfg->ffn : cfg->dim) >= (1L << 31)) return WAN_ERR_SHAPE;
+  if (L * (cfg->ffn > cfg->dim ? cfg->ffn : cfg->dim) >= (1L << 31)) return WAN_ERR_SHAPE;
   Layout y = make_layout(*cfg, B, L, true, true);
   if (ws_bytes < y.total) return WAN_ERR_WORKSPACE;
   return step_run(*cfg, latent, t, B, lat_f, H8, W8, ctx, clip_feat, nullptr, *w, out, (char *)ws, y,
@@ -980,7 +988,7 @@ int wan_sample_fp8_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, in
   if ((st = check_model_weights(*cfg, w, false, true))) return st;
   if (cache_bytes < kv_layout(*cfg, B).per_block * (size_t)cfg->n_blocks) return WAN_ERR_WORKSPACE;
   const long L = (long)lat_f * (H8 / 2) * (W8 / 2);
-  if ((long)B * L * (cfg->ffn > cfg->dim ? cfg->ffn : cfg->dim) >= (1L << 31)) return WAN_ERR_SHAPE;
+  if (L * (cfg->ffn > cfg->dim ? cfg->ffn : cfg->dim) >= (1L << 31)) return WAN_ERR_SHAPE;
   const long plane = (long)lat_f * H8 * W8;
   Layout y = make_layout(*cfg, B, L, true, true);
   size_t t_off, v_off;
