@@ -409,8 +409,8 @@ def attn8_leg(W, B, L, d, H, qk, vt, Lp, stream, n_att, bf16_attn_ms, sa_f):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", type=int, default=2, help="block workload id (2: 1.3B, 4: 14B)")
     ap.add_argument("--sampler", type=int, default=0, metavar="STEPS",
