@@ -265,19 +265,32 @@ def pin_block(O):
     _close(O.block(x, m, w, ctx, H, rows=rows), y[:, rows], 1e-12, "block rows")
     # composition from torch library pieces
     for b in range(B):
-        mb = _t(m[b] + w["mod_bias"]).reshape(6, d)
-        xb = _t(x[b])
-        lin = lambda a, W, bb: TF.linear(a, _t(W), _t(bb))
-        h1 = TF.layer_norm(xb, (d,), eps=1e-6) * (1 + mb[1]) + mb[0]
-        sa = _t(_torch_mha(h1.numpy(), h1.numpy(), w["sa_wqkv"], w["sa_bqkv"], w["sa_wo"], w["sa_bo"], H))
-        x1 = xb + mb[2] * sa
-        xn = TF.layer_norm(x1, (d,), eps=1e-6).numpy()
-        ca = _t(_torch_mha(xn, ctx[b], np.concatenate([w["ca_wq"], w["ca_wkv"]]),
-                           np.concatenate([w["ca_bq"], w["ca_bkv"]]), w["ca_wo"], w["ca_bo"], H))
-        x2 = x1 + ca
-        h2 = TF.layer_norm(x2, (d,), eps=1e-6) * (1 + mb[4]) + mb[3]
-        z = lin(TF.gelu(lin(h2, w["ffn_w1"], w["ffn_b1"]), approximate="tanh"), w["ffn_w2"], w["ffn_b2"])
-        _close(y[b], (x2 + mb[5] * z).numpy(), 1e-10, "block vs torch composition")
+        _close(y[b], _torch_block(x[b], m[b], w, ctx[b], H), 1e-10, "block vs torch composition")
+
+
+def _torch_block(xb, mb, w, ctxb, H, imgb=None):
+    """One sample of the block built from torch library pieces (LayerNorm,
+    MultiheadAttention, Linear, GELU): x1 = x + gate1 SA(modulated LN x),
+    x2 = x1 + CA(LN x1) (text part + image part sharing Q and the out-
+    projection), x3 = x2 + gate2 FFN(modulated LN x2)."""
+    d = xb.shape[-1]
+    mb = _t(np.asarray(mb) + w["mod_bias"]).reshape(6, d)
+    xb = _t(xb)
+    lin = lambda a, W, bb: TF.linear(a, _t(W), _t(bb))
+    h1 = TF.layer_norm(xb, (d,), eps=1e-6) * (1 + mb[1]) + mb[0]
+    sa = _t(_torch_mha(h1.numpy(), h1.numpy(), w["sa_wqkv"], w["sa_bqkv"], w["sa_wo"], w["sa_bo"], H))
+    x1 = xb + mb[2] * sa
+    xn = TF.layer_norm(x1, (d,), eps=1e-6).numpy()
+    ca = _t(_torch_mha(xn, ctxb, np.concatenate([w["ca_wq"], w["ca_wkv"]]),
+                       np.concatenate([w["ca_bq"], w["ca_bkv"]]), w["ca_wo"], w["ca_bo"], H))
+    if imgb is not None:
+        ca = ca + _t(_torch_mha(xn, imgb, np.concatenate([w["ca_wq"], w["ca_wkv_img"]]),
+                                np.concatenate([w["ca_bq"], w["ca_bkv_img"]]), w["ca_wo"],
+                                w["ca_bo"], H)) - _t(w["ca_bo"])
+    x2 = x1 + ca
+    h2 = TF.layer_norm(x2, (d,), eps=1e-6) * (1 + mb[4]) + mb[3]
+    z = lin(TF.gelu(lin(h2, w["ffn_w1"], w["ffn_b1"]), approximate="tanh"), w["ffn_w2"], w["ffn_b2"])
+    return (x2 + mb[5] * z).numpy()
 
 
 # ---------------------------------------------------------------- patchify
@@ -384,8 +397,8 @@ def pin_step(O):
         blocks.append(w)
     mw["blocks"] = blocks
     assert np.array_equal(O.step(lat, t, ctx, mw, H), lat), "identity step"
-    # with real blocks: step == head(blocks(patchify)) composed by hand, and
-    # the batch entries are independent
+    # with real blocks the batch entries are independent (the composition
+    # against torch pieces is pin_step_wiring)
     for w in blocks:
         w["mod_bias"] = r.normal(size=6 * d) * 0.3
         w["ca_wo"] = r.normal(size=(d, d)) * 0.3
@@ -393,6 +406,88 @@ def pin_step(O):
     out = O.step(lat, t, ctx, mw, H)
     out1 = O.step(lat[1:], t[1:], ctx[1:], mw, H)
     _close(out1[0], out[1], 1e-9, "step batch independence")
+
+
+def _torch_step(lat, t, ctx, mw, H, clip=None):
+    """The denoising step built from torch library pieces and the pages' order
+    ([Note, Diffusion Transformer]; [Note, I2V 架构扩展]): Conv3d patchify with
+    kernel = stride = (1,2,2); the 256-wide sinusoid of the raw timestep through
+    Linear-SiLU-Linear once per sample; the image features of *that* sample
+    through Linear-GELU-Linear-GELU-Linear; the blocks in list order, each fed
+    the same modulation and contexts; the head Linear and the transposed
+    (1,2,2) scatter back to the latent grid."""
+    B, Cin, Fr, H8, W8 = lat.shape
+    d = mw["patch_w"].shape[0]
+    Hp, Wp = H8 // 2, W8 // 2
+    tw = mw["tmlp"]
+    half = 128
+    om = torch.exp(-math.log(10000.0) * torch.arange(half, dtype=torch.float64) / half)
+    wt = torch.zeros(64, 16, 1, 2, 2, dtype=torch.float64)
+    for c in range(16):
+        for a in range(2):
+            for bb in range(2):
+                wt[c * 4 + a * 2 + bb, c, 0, a, bb] = 1.0
+    outs = []
+    for s in range(B):
+        conv = TF.conv3d(_t(lat[s:s + 1]), _t(mw["patch_w"].reshape(d, Cin, 1, 2, 2)),
+                         _t(mw["patch_b"]), stride=(1, 2, 2))[0]          # [d, F, Hp, Wp]
+        x = conv.reshape(d, -1).T.numpy()
+        arg = float(t[s]) * om
+        e = torch.cat([torch.cos(arg), torch.sin(arg)])
+        m = TF.linear(TF.silu(TF.linear(e, _t(tw["w1"]), _t(tw["b1"]))), _t(tw["w2"]), _t(tw["b2"]))
+        img = None
+        if clip is not None:
+            iw = mw["img"]
+            g = lambda a: TF.gelu(a, approximate="tanh")
+            img = TF.linear(g(TF.linear(g(TF.linear(_t(clip[s]), _t(iw["w1"]), _t(iw["b1"]))),
+                                        _t(iw["w2"]), _t(iw["b2"]))), _t(iw["w3"]), _t(iw["b3"])).numpy()
+        for w in mw["blocks"]:
+            x = _torch_block(x, m.numpy(), w, ctx[s], H, img)
+        hx = TF.linear(_t(x), _t(mw["head_w"]), _t(mw["head_b"]))           # [L, 64]
+        inp = hx.T.reshape(1, 64, Fr, Hp, Wp)
+        outs.append(TF.conv_transpose3d(inp, wt, stride=(1, 2, 2))[0].numpy())
+    return np.stack(outs)
+
+
+def pin_step_wiring(O):
+    """step() against the step composed from torch pieces (``_torch_step``) on
+    an I2V pair whose samples differ in timestep, text context and image
+    features, with three distinct blocks (their order matters) and non-zero
+    extra patchify columns.  Also: swapping the two samples' clip features
+    swaps the outputs, the blocks in reverse order give a different result,
+    and a timestep change moves the output only through the t-MLP."""
+    r = _rng(14)
+    B, d, H, F = 2, 16, 2, 24
+    Fr, H8, W8, Lc, Li, feat = 2, 4, 6, 5, 3, 12
+    lat = r.normal(size=(B, 36, Fr, H8, W8))
+    t = np.array([37.5, 810.0])
+    ctx = r.normal(size=(B, Lc, d))
+    clip = r.normal(size=(B, Li, feat))
+    mw = {"patch_w": r.normal(size=(d, 36 * 4)) * 0.3, "patch_b": r.normal(size=d) * 0.3,
+          "head_w": r.normal(size=(64, d)) * 0.3, "head_b": r.normal(size=64) * 0.3,
+          "tmlp": {"w1": r.normal(size=(d, 256)) * 0.3, "b1": r.normal(size=d) * 0.3,
+                   "w2": r.normal(size=(6 * d, d)) * 0.3, "b2": r.normal(size=6 * d) * 0.3},
+          "img": {"w1": r.normal(size=(d, feat)) * 0.3, "b1": r.normal(size=d) * 0.3,
+                  "w2": r.normal(size=(d, d)) * 0.3, "b2": r.normal(size=d) * 0.3,
+                  "w3": r.normal(size=(d, d)) * 0.3, "b3": r.normal(size=d) * 0.3},
+          "blocks": [_tiny_block_weights(r, d, F, img=True, scale=0.4) for _ in range(3)]}
+    out = O.step(lat, t, ctx, mw, H, clip=clip)
+    ref = _torch_step(lat, t, ctx, mw, H, clip=clip)
+    _close(out, ref, 1e-9, "I2V step vs torch composition")
+    # sample-specific image context: swapping clip features between the two
+    # samples (all else equal) must change each sample's output
+    lat2 = np.concatenate([lat[:1], lat[:1]])
+    same = O.step(lat2, np.array([t[0], t[0]]), np.concatenate([ctx[:1], ctx[:1]]), mw, H, clip=clip)
+    assert np.max(np.abs(same[0] - same[1])) > 1e-6, "samples with different clip features agree"
+    # block order matters, and step follows the list order
+    rev = dict(mw); rev["blocks"] = mw["blocks"][::-1]
+    _close(O.step(lat, t, ctx, rev, H, clip=clip), _torch_step(lat, t, ctx, rev, H, clip=clip),
+           1e-9, "reversed blocks vs torch composition")
+    # T2V (16 channels, no image context) against the same composition
+    mw16 = dict(mw); mw16["patch_w"] = mw["patch_w"][:, :64]
+    mw16["blocks"] = [{k: v for k, v in w.items() if "img" not in k} for w in mw["blocks"]]
+    _close(O.step(lat[:, :16], t, ctx, mw16, H), _torch_step(lat[:, :16], t, ctx, mw16, H),
+           1e-9, "T2V step vs torch composition")
 
 
 # ---------------------------------------------------------------- sampler

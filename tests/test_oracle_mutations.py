@@ -82,6 +82,15 @@ MUTATIONS = {
     "attn8 inputs not rounded to bf16": ("o = multihead_8bit(bf16_round(q), bf16_round(k), bf16_round(v), heads)",
                                          "o = multihead_8bit(q, k, v, heads)"),
     "attn8 flag not passed to the SA": ("heads, rows=rows, fp8=fp8, attn8=attn8)", "heads, rows=rows, fp8=fp8)"),
+    "step drops the image context": ("x = block(x, m, wts, ctx, heads, eps, img=img, fp8=fp8, attn8=attn8)",
+                                     "x = block(x, m, wts, ctx, heads, eps, img=None, fp8=fp8, attn8=attn8)"),
+    "t-MLP fed t/1000": ("m = tmlp(t, tw[\"w1\"]", "m = tmlp(_f(t) / 1000.0, tw[\"w1\"]"),
+    "blocks in reverse order": ("for wts in (blocks if blocks is not None else mw[\"blocks\"]):",
+                                "for wts in list(blocks if blocks is not None else mw[\"blocks\"])[::-1]:"),
+    "clip of sample 0 for every sample": ("img = np.stack([image_context(clip[b],", "img = np.stack([image_context(clip[0],"),
+    "text context of sample 0 for every sample": ("ca = cross_attention(x1, _f(ctx[b]),", "ca = cross_attention(x1, _f(ctx[0]),"),
+    "modulation of sample 0 for every sample": ('h1 = modulate(layer_norm(xb, eps), mod["shift1"][b], mod["scale1"][b])',
+                                                'h1 = modulate(layer_norm(xb, eps), mod["shift1"][0], mod["scale1"][0])'),
     "head split strided": ("k[:, h * hd:(h + 1) * hd],\n                                     v[:, h * hd:(h + 1) * hd])",
                            "k[:, h::heads],\n                                     v[:, h::heads])"),
 }
