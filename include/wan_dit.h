@@ -292,8 +292,15 @@ int wan_attention_8bit_fwd(const void *q, int ldq, const void *k, int ldk, const
                            int vt_bstride, void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled,
                            void *ws, size_t ws_bytes, void *stream);
 
-/* y = x W^T + b for a bf16 x [M, K], W [N, K], b [N] (device), K % 64 == 0.
- * mode 0: y bf16 [M, N];  mode 1: y float32 [M, N];  mode 2: y bf16 = GELU_tanh(.) */
+/* One Linear layer of the block ([Note] Diffusion Transformer: the attention
+ * projections; [Note] 配置表: the FFN of width ffn with GELU):
+ *   y = x W^T + b for a bf16 x [M, K], W [N, K], b [N] or NULL (all device,
+ *   rows contiguous), K % 64 == 0, M, N > 0.
+ * mode 0: y bf16 [M, N];  mode 1: y float32 [M, N];  mode 2: y bf16 =
+ * GELU_tanh(.) (tanh form).  float32 accumulation.  Operands of 2 GiB or
+ * more run as launches over row / column slices.  Errors: WAN_ERR_NULL for
+ * a NULL x / W / y, WAN_ERR_SHAPE for the sizes above, WAN_ERR_CONFIG for
+ * another mode. */
 int wan_linear_fwd(const void *x, const void *w, const void *b, void *y, int M, int N, int K,
                    int mode, void *stream);
 

@@ -136,7 +136,7 @@ def silu(z):
 def gelu_tanh(u):
     """GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).  (R7)"""
     u = _f(u)
-    return 0.5 * u * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))
+    return 0.5 * u * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * (u * u * u))))
 
 
 def linear(x, w, b):
@@ -192,7 +192,7 @@ def block_modulation(m, beta):
 # attention  (R6)  [Note, Diffusion Transformer: full spatio-temporal attention;
 #                   text injected through cross-attention in every block]
 
-def attention(q, k, v, chunk: int = 1024):
+def attention(q, k, v, chunk: int = 256):
     """softmax(q k^T / sqrt(hd)) v for one head.  q [Lq, hd], k/v [Lk, hd].
     The softmax is materialised one query chunk at a time (rows are
     independent), with the row maximum subtracted before exp."""
@@ -209,12 +209,25 @@ def attention(q, k, v, chunk: int = 1024):
     return out
 
 
+# Heads are independent, so a long run may attend to several heads at once:
+# HEAD_THREADS > 1 hands the heads to a pool of that many threads (each head's
+# arithmetic is unchanged; the BLAS inside each head then runs on one thread).
+HEAD_THREADS = 1
+
+
 def multihead(q, k, v, heads: int):
     """Split the feature axis into ``heads`` equal heads (head h = columns
     h*hd .. (h+1)*hd), attend per head, concatenate."""
     hd = q.shape[1] // heads
-    return np.concatenate([attention(q[:, h * hd:(h + 1) * hd], k[:, h * hd:(h + 1) * hd],
-                                     v[:, h * hd:(h + 1) * hd]) for h in range(heads)], axis=1)
+    one = lambda h: attention(q[:, h * hd:(h + 1) * hd], k[:, h * hd:(h + 1) * hd],
+                              v[:, h * hd:(h + 1) * hd])
+    if HEAD_THREADS <= 1 or heads == 1:
+        return np.concatenate([one(h) for h in range(heads)], axis=1)
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(HEAD_THREADS) as ex:
+        outs = list(ex.map(one, range(heads)))
+    return np.concatenate(outs, axis=1)
 
 
 def self_attention(hmod, wqkv, bqkv, wo, bo, heads: int, rows: Optional[np.ndarray] = None,

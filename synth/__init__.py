@@ -291,6 +291,44 @@ def attention_inputs(seed: int, B: int, H: int, Lq: int, Lk: int, hd: int = 128,
     return q, k, v
 
 
+def attention_inputs_full(seed: int, H: int, L: int, hd: int = 128, qk_std: float = 2.0,
+                          threads: int = 8):
+    """Q, K, V [L, H*hd] (one batch sample) for attention stress tests at the
+    full sequence lengths, bf16-rounded float32; each head's slice of each
+    tensor has its own PCG64 stream (drawn on ``threads`` host threads).
+    q, k ~ N(0, qk_std^2) (logits std qk_std^2), v ~ N(0, 1)."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = [np.empty((L, H * hd), np.float32) for _ in range(3)]
+
+    def fill(job):
+        which, h = job
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2025, 97, seed, H, L, which, h])))
+        a = g.standard_normal((L, hd), dtype=np.float32)
+        if which < 2:
+            a *= np.float32(qk_std)
+        out[which][:, h * hd:(h + 1) * hd] = bf16_round(a)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, [(w, h) for w in range(3) for h in range(H)]))
+    return out[0], out[1], out[2]
+
+
+def block_weights_iter(w: "Workload", threads: int = 8):
+    """Yield ``block_weights(w, i)`` for i = 0 .. n_blocks-1 in order, with up
+    to ``threads`` blocks drawn ahead on host threads (the values are those
+    of ``block_weights``: every tensor keeps its own seeded stream)."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = w.model.n_blocks
+    ahead = max(1, threads)
+    with ThreadPoolExecutor(ahead) as ex:
+        futs = {j: ex.submit(block_weights, w, j) for j in range(min(n, ahead))}
+        for i in range(n):
+            bw = futs.pop(i).result()
+            if i + ahead < n:
+                futs[i + ahead] = ex.submit(block_weights, w, i + ahead)
+            yield bw
+
+
 def linear_inputs(seed: int, M: int, N: int, K: int):
     """x ~ N(0,1), W ~ N(0, 1/K), b ~ N(0, 1), all bf16-rounded float32."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2025, 98, seed, M, N, K])))

@@ -60,8 +60,10 @@ def test_block_mini(name):
     assert_parity(g_mod, o_mod, 1e-4, 1e-5, "t-MLP")
     assert_parity(g_x, o_x, 3e-2, 1e-2, "block output")
     # the block's update alone (x_out - x_in), judged relative to its own size
-    tol = 1e-4 if work.model.dtype == "f32" else 3e-2
-    assert_parity(g_x - x0, o_x - x0, tol, tol, "block update")
+    if work.model.dtype == "f32":
+        assert_parity(g_x - x0, o_x - x0, 1e-4, 1e-4, "block update")
+    else:
+        assert_parity(g_x - x0, o_x - x0, 3e-2, 1e-2, "block update")
 
 
 @pytest.mark.parametrize("cid", [2, 4])
@@ -76,4 +78,64 @@ def test_block_full_size_sampled_rows(cid):
     x0, g_mod, o_mod, g_x, o_x = _run_block(work, rows=rows)
     assert_parity(g_mod, o_mod, 1e-4, 1e-5, "t-MLP")
     assert_parity(g_x[:, rows], o_x, 3e-2, 1e-2, "block output (sampled rows)")
-    assert_parity(g_x[:, rows] - x0[:, rows], o_x - x0[:, rows], 3e-2, 3e-2, "block update")
+    assert_parity(g_x[:, rows] - x0[:, rows], o_x - x0[:, rows], 3e-2, 1e-2, "block update")
+
+
+def _centered(a):
+    return a - a.mean(axis=-2, keepdims=True)
+
+
+@pytest.mark.parametrize("branch", ["sa", "ca", "ffn"])
+def test_block_branches_full_size(branch):
+    """Each branch of the full 1.3B 480P block (L = 32760) alone, against the
+    oracle's branch output (block(..., return_parts=True)) on sampled rows,
+    on the branch's own scale.  The branch is isolated through the block's
+    own inputs: the modulation input sets the gates (gate = 1 for the branch
+    under test, 0 for the other gated branch) and the cross-attention out-
+    projection is zeroed unless the cross-attention is tested, so
+    x_out - x_in is that branch's output.
+
+    Besides the raw branch (the usual bar) its token-dependent part (each
+    feature's mean over the sampled rows removed) is compared: at these
+    weights the self-attention output is close to its bias, and a softmax
+    replaced by the mean of V would leave the raw branch within the bar but
+    make the centred part zero (relative error 1).  The centred self-
+    attention part takes a looser bar (0.1): the attention output is stored
+    in bf16 before the out-projection, and its rounding (~2^-9 of |o|) is a
+    few percent of the token-dependent part at this sequence length (0.9%
+    at L = 2048 in a CPU emulation of the rounding points; the part shrinks
+    as the softmax flattens over more keys)."""
+    import video_diffusion_transformer_block_amd as W
+    from tests.gpu_util import assert_parity, cfg_of, up, up_block, workspace
+    work = synth.CONFIGS[2]
+    m = work.model
+    d, L = m.dim, work.L
+    rows = np.unique(np.concatenate([[0, 255, 256, L - 1],
+                                     np.random.default_rng(7).integers(0, L, 60)]))
+    print(f"block branch {branch} C2 L={L}, {len(rows)} sampled rows", flush=True)
+    inp = synth.workload_inputs(work)
+    tw = synth.tmlp_weights(work)
+    bw = dict(synth.block_weights(work, 0))
+    mod = O.tmlp(inp["t"], tw["w1"], tw["b1"], tw["w2"], tw["b2"]).astype(np.float32)
+    beta = bw["mod_bias"].astype(np.float32)
+    g1, g2 = {"sa": (1, 0), "ca": (0, 0), "ffn": (0, 1)}[branch]
+    mod[:, 2 * d:3 * d] = np.float32(g1) - beta[2 * d:3 * d]
+    mod[:, 5 * d:6 * d] = np.float32(g2) - beta[5 * d:6 * d]
+    if branch != "ca":
+        bw["ca_wo"] = np.zeros_like(bw["ca_wo"])
+        bw["ca_bo"] = np.zeros_like(bw["ca_bo"])
+    cfg = cfg_of(work)
+    # every device tensor the launch reads stays referenced until it has run
+    x, modd, ctxd = up(inp["x"], "f32"), up(mod, "f32"), up(inp["ctx"], m.dtype)
+    bwd, ws = up_block(bw, m.dtype), workspace(cfg, work)
+    W.dit_block_fwd(cfg, x, 1, work.lat_f, work.Hp, work.Wp, modd, W.block_weights(bwd), ctxd,
+                    None, ws)
+    torch.cuda.synchronize()
+    g = (x.cpu().numpy().astype(np.float64) - inp["x"])[:, rows]
+    _, parts = O.block(inp["x"], mod.astype(np.float64), bw, inp["ctx"], m.heads, m.eps,
+                       rows=rows, return_parts=True)
+    o = parts[0][branch][None]
+    r = assert_parity(g, o, 3e-2, 1e-2, f"{branch} branch")
+    c = assert_parity(_centered(g), _centered(o), 3e-2, 0.1 if branch == "sa" else 1e-2,
+                      f"{branch} branch, token-dependent part")
+    print(f"  raw {r}  centred {c}", flush=True)

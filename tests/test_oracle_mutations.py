@@ -91,8 +91,8 @@ MUTATIONS = {
     "text context of sample 0 for every sample": ("ca = cross_attention(x1, _f(ctx[b]),", "ca = cross_attention(x1, _f(ctx[0]),"),
     "modulation of sample 0 for every sample": ('h1 = modulate(layer_norm(xb, eps), mod["shift1"][b], mod["scale1"][b])',
                                                 'h1 = modulate(layer_norm(xb, eps), mod["shift1"][0], mod["scale1"][0])'),
-    "head split strided": ("k[:, h * hd:(h + 1) * hd],\n                                     v[:, h * hd:(h + 1) * hd])",
-                           "k[:, h::heads],\n                                     v[:, h::heads])"),
+    "head split strided": ("k[:, h * hd:(h + 1) * hd],\n                              v[:, h * hd:(h + 1) * hd])",
+                           "k[:, h::heads],\n                              v[:, h::heads])"),
 }
 
 

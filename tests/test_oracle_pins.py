@@ -34,3 +34,17 @@ def test_param_counts_match_model_names():
         assert abs(total / m["total_params"] - 1) < 0.10, (m["name"], total)
         unshared_extra = n * 6 * d * d
         assert abs(unshared_extra / (total + unshared_extra) - g["adaln_sharing_saving"]) < 0.06
+
+
+def test_threaded_heads_match_sequential():
+    """The optional head thread pool changes no arithmetic."""
+    r = np.random.default_rng(3)
+    q, k, v = (r.normal(size=(70, 4 * 32)) for _ in range(3))
+    ref = O.multihead(q, k, v, 4)
+    old = O.HEAD_THREADS
+    try:
+        O.HEAD_THREADS = 3
+        got = O.multihead(q, k, v, 4)
+    finally:
+        O.HEAD_THREADS = old
+    assert np.max(np.abs(got - ref)) <= 1e-12

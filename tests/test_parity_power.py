@@ -23,3 +23,20 @@ def test_stress_inputs_reject_unscaled_softmax():
     bad = O.multihead(q[0] * np.sqrt(128.0), k[0], v[0], 2)   # drops the 1/sqrt(hd)
     m = metrics(bad, ref)
     assert m["max_abs"] > 3e-2 and m["mean_rel"] > 1e-2, m
+
+
+def test_full_length_inputs_reject_mean_of_v_and_unscaled_softmax():
+    """The full-length stress inputs (12 heads x 32760 tokens, peaked logits
+    with raised key runs) on 64 sampled query rows: the plain mean of V and a
+    softmax without the 1/sqrt(hd) scale both fail the GPU tests' bar."""
+    from tests.attn_full_inputs import full_inputs, sampled_rows
+    H, L = 12, 32760
+    q, k, v = full_inputs(H, L, threads=8)
+    rows = sampled_rows(L, n=64)
+    ref = O.multihead(q[rows], k, v, H)
+    mean_v = np.broadcast_to(v.astype(np.float64).mean(axis=0, keepdims=True), ref.shape)
+    m = metrics(mean_v, ref)
+    assert m["max_abs"] > 3e-2 and m["mean_rel"] > 1e-2, m
+    bad = O.multihead(q[rows] * np.sqrt(128.0), k, v, H)
+    m = metrics(bad, ref)
+    assert m["max_abs"] > 3e-2 and m["mean_rel"] > 1e-2, m
