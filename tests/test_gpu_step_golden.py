@@ -44,6 +44,9 @@ def test_full_step_against_oracle_samples(cid):
     from tests.gpu_util import assert_parity, cfg_of, up
     work = synth.CONFIGS[cid]
     m = work.model
+    if not os.path.exists(golden_path(cid)):
+        pytest.skip(f"{os.path.basename(golden_path(cid))} not written yet "
+                    f"(python -m tests.golden.make_full_step_golden --config {cid})")
     with open(golden_path(cid)) as f:
         gold = json.load(f)
     print(f"full step {work.name}: B={work.batch} L={work.L} blocks={m.n_blocks} "
