@@ -19,7 +19,9 @@
  *     step output are always float32.  The per-block modulation bias is float32.
  *   - Every pointer named "device" is device memory owned by the caller; the
  *     library never allocates or frees memory.  Temporaries live in the
- *     caller's workspace (ws, ws_bytes), sized by wan_workspace_bytes().
+ *     caller's workspace (ws, ws_bytes), sized by wan_workspace_bytes(); the
+ *     one exception, wan_dit_block_fwd_noalloc, keeps them in a static device
+ *     array of the library.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and the call returns without waiting.  Calls are stateless;
  *     concurrent calls need distinct workspaces and outputs.
@@ -145,6 +147,36 @@ int wan_tmlp_fwd(const wan_cfg_t *cfg, const float *t, int B, const wan_tmlp_wei
 int wan_dit_block_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, int Wp,
                       const float *mod, const wan_block_weights_t *w, const void *ctx,
                       const void *img_ctx, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- the block without a caller workspace --------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the block
+ * of wan_dit_block_fwd with its temporaries in a static device array of
+ * WAN_NOALLOC_SCRATCH_BYTES owned by the library (one per GPU, held until
+ * the process ends) instead of a caller workspace.  The caller still passes
+ * every input and the residual stream x.  It allocates nothing and calls no
+ * allocating routine.  Results equal wan_dit_block_fwd's bit for bit (same
+ * kernels, same order).
+ *   - Sizes whose temporaries exceed WAN_NOALLOC_SCRATCH_BYTES return
+ *     WAN_ERR_WORKSPACE before anything is enqueued
+ *     (wan_dit_block_noalloc_bytes gives the need; at the 1.3B width about
+ *     36 KB per token, so up to ~7000 tokens per call).
+ *   - All calls on one GPU share the array and it keeps the last call's
+ *     contents (every byte a call reads it has written first): calls that
+ *     overlap on one GPU (other streams, other host threads) race and must
+ *     be serialised by the caller.
+ *   - WAN_ERR_HIP when the array's device address cannot be looked up.
+ * Other arguments and errors as wan_dit_block_fwd. */
+#define WAN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* Scratch bytes one wan_dit_block_fwd_noalloc call needs (0 for an invalid
+ * cfg / shape); the call succeeds when this is at most
+ * WAN_NOALLOC_SCRATCH_BYTES. */
+size_t wan_dit_block_noalloc_bytes(const wan_cfg_t *cfg, int B, int lat_f, int Hp, int Wp);
+
+int wan_dit_block_fwd_noalloc(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, int Wp,
+                              const float *mod, const wan_block_weights_t *w, const void *ctx,
+                              const void *img_ctx, void *stream);
 
 /* One denoising step ([Note] Diffusion Transformer: patchify with a (1,2,2)
  * 3D convolution, N blocks, unpatchify; [Note] I2V 架构扩展 for the I2V

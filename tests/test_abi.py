@@ -214,3 +214,27 @@ def test_attn8_cfg_checks(W):
     c.attn8 = 1
     base = W.workspace_bytes(W.make_cfg(dim=256, heads=2, ffn=256), 1, 2, 4, 4)
     assert W.workspace_bytes(c, 1, 2, 4, 4) == base + W.attention_8bit_workspace_bytes(1, 2, 8, 8)
+
+
+def test_noalloc_scratch_limit(W):
+    """The allocation-free block: the header's scratch size matches the
+    binding's, the need grows with the tokens, and a size beyond the scratch
+    is refused with WAN_ERR_WORKSPACE before any device work."""
+    src = open(HEADER, encoding="utf-8").read()
+    m = re.search(r"#define\s+WAN_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == W.NOALLOC_SCRATCH_BYTES
+    c = W.make_cfg(dim=1536, heads=12, ffn=8960)
+    small = W.dit_block_noalloc_bytes(c, 1, 2, 30, 52)
+    assert 0 < small <= W.NOALLOC_SCRATCH_BYTES
+    assert small < W.dit_block_noalloc_bytes(c, 2, 2, 30, 52)
+    assert W.dit_block_noalloc_bytes(c, 1, 21, 30, 52) > W.NOALLOC_SCRATCH_BYTES
+    assert W.dit_block_noalloc_bytes(c, 9, 2, 30, 52) == 0
+    L = W.lib()
+    dummy = C.c_void_p(256)   # never dereferenced: every call below fails validation first
+    bw = W.binding.BlockW(*([256] * 17))
+    assert L.wan_dit_block_fwd_noalloc(C.byref(c), dummy, 1, 21, 30, 52, dummy, C.byref(bw), dummy,
+                                       None, None) == -4
+    assert L.wan_dit_block_fwd_noalloc(C.byref(c), None, 1, 2, 30, 52, dummy, C.byref(bw), dummy,
+                                       None, None) == -1
+    assert L.wan_dit_block_fwd_noalloc(C.byref(c), dummy, 1, 2, 30, 52, dummy, C.byref(bw), dummy,
+                                       dummy, None) == -5                  # image context without img_len

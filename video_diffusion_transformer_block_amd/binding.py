@@ -18,6 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("WANDIT_LIB") or os.path.join(_HERE, "libwandit.so")
 
 WAN_F32, WAN_BF16 = 0, 1
+# the static scratch of wan_dit_block_fwd_noalloc (WAN_NOALLOC_SCRATCH_BYTES in the header)
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 EXPORTS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
            "wan_status_str", "wan_tmlp_fwd", "wan_dit_block_fwd", "wan_dit_step_fwd",
@@ -27,10 +29,12 @@ EXPORTS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_by
            "wan_quantize_block_fp8", "wan_block_fp8_workspace_bytes", "wan_dit_block_fp8_fwd",
            "wan_model_fp8_bytes", "wan_quantize_model_fp8", "wan_fp8_workspace_bytes",
            "wan_dit_step_fp8_fwd", "wan_sample_fp8_fwd", "wan_attention_8bit_workspace_bytes",
-           "wan_attention_8bit_quantize", "wan_attention_8bit_q_fwd", "wan_attention_8bit_fwd")
+           "wan_attention_8bit_quantize", "wan_attention_8bit_q_fwd", "wan_attention_8bit_fwd",
+           "wan_dit_block_noalloc_bytes", "wan_dit_block_fwd_noalloc")
 _SIZE_FNS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
              "wan_block_fp8_bytes", "wan_block_fp8_workspace_bytes", "wan_model_fp8_bytes",
-             "wan_fp8_workspace_bytes", "wan_attention_8bit_workspace_bytes")
+             "wan_fp8_workspace_bytes", "wan_attention_8bit_workspace_bytes",
+             "wan_dit_block_noalloc_bytes")
 
 
 class WanError(RuntimeError):
@@ -83,6 +87,9 @@ def lib() -> C.CDLL:
         L.wan_tmlp_fwd.argtypes = [C.POINTER(Cfg), vp, i, C.POINTER(TmlpW), vp, vp, sz, vp]
         L.wan_dit_block_fwd.argtypes = [C.POINTER(Cfg), vp, i, i, i, i, vp, C.POINTER(BlockW), vp,
                                         vp, vp, sz, vp]
+        L.wan_dit_block_noalloc_bytes.argtypes = [C.POINTER(Cfg), i, i, i, i]
+        L.wan_dit_block_fwd_noalloc.argtypes = [C.POINTER(Cfg), vp, i, i, i, i, vp, C.POINTER(BlockW),
+                                                vp, vp, vp]
         L.wan_dit_step_fwd.argtypes = [C.POINTER(Cfg), vp, vp, i, i, i, i, vp, vp, C.POINTER(ModelW),
                                        vp, vp, sz, vp]
         L.wan_i2v_mask.argtypes = [vp, i, i, i, i, vp]
@@ -192,6 +199,18 @@ def dit_block_fwd(cfg: Cfg, x: torch.Tensor, B: int, lat_f: int, Hp: int, Wp: in
            lib().wan_dit_block_fwd(C.byref(cfg), _p(x), B, lat_f, Hp, Wp, _p(mod), C.byref(bw),
                                    _p(ctx), _p(img_ctx), _p(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)))
+
+
+def dit_block_noalloc_bytes(cfg: Cfg, B: int, lat_f: int, Hp: int, Wp: int) -> int:
+    return int(lib().wan_dit_block_noalloc_bytes(C.byref(cfg), B, lat_f, Hp, Wp))
+
+
+def dit_block_fwd_noalloc(cfg: Cfg, x: torch.Tensor, B: int, lat_f: int, Hp: int, Wp: int,
+                          mod: torch.Tensor, bw: BlockW, ctx: torch.Tensor,
+                          img_ctx: Optional[torch.Tensor], stream=None):
+    _check("wan_dit_block_fwd_noalloc",
+           lib().wan_dit_block_fwd_noalloc(C.byref(cfg), _p(x), B, lat_f, Hp, Wp, _p(mod),
+                                           C.byref(bw), _p(ctx), _p(img_ctx), _stream(stream)))
 
 
 def dit_step_fwd(cfg: Cfg, latent: torch.Tensor, t: torch.Tensor, ctx: torch.Tensor,

@@ -17,11 +17,22 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/wan_dit.h"
 #include "attn8.hpp"
 #include "kernels.hpp"
 
 using namespace wan;
+
+// Device scratch of the allocation-free block entry point
+// (wan_dit_block_fwd_noalloc): its temporaries live in this file-scope array
+// instead of a caller's workspace.  Every GPU the library runs on holds its
+// own copy until the process ends.  In host code the array's name is only a
+// stand-in, not a device address: the address comes from hipGetSymbolAddress,
+// taken once per device with that device current (scratch_base below), and
+// only that address is ever handed to kernels.
+static __device__ __align__(256) char scratch[WAN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -585,6 +596,25 @@ int sample_run(const wan_cfg_t &c, float *latent, int B, int lat_f, int H8, int 
   return WAN_OK;
 }
 
+// ---- the block without a caller workspace
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+char *scratch_dev[MAX_DEVICES];   // device address of `scratch` per device ordinal
+
+// the current device's scratch address (looked up on the first call on that
+// device, with the device current); nullptr when the lookup fails
+char *scratch_base() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_dev[dev] = static_cast<char *>(p);
+  }
+  return scratch_dev[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -636,6 +666,28 @@ int wan_dit_block_fwd(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, 
   Layout y = make_layout(*cfg, B, L, false);
   if (ws_bytes < y.total) return WAN_ERR_WORKSPACE;
   return block_run(*cfg, x, B, L, mod, *w, ctx, img_ctx, nullptr, (char *)ws, y, S(stream));
+}
+
+size_t wan_dit_block_noalloc_bytes(const wan_cfg_t *cfg, int B, int lat_f, int Hp, int Wp) {
+  if (check_cfg(cfg) != WAN_OK || check_dims(*cfg, B, lat_f, Hp, Wp) != WAN_OK) return 0;
+  return make_layout(*cfg, B, (long)lat_f * Hp * Wp, false).total;
+}
+
+int wan_dit_block_fwd_noalloc(const wan_cfg_t *cfg, float *x, int B, int lat_f, int Hp, int Wp,
+                              const float *mod, const wan_block_weights_t *w, const void *ctx,
+                              const void *img_ctx, void *stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (!x || !mod || !ctx) return WAN_ERR_NULL;
+  if ((st = check_dims(*cfg, B, lat_f, Hp, Wp))) return st;
+  if ((st = check_block_weights(*cfg, w))) return st;
+  if ((cfg->img_len > 0) != (img_ctx != nullptr)) return WAN_ERR_CONFIG;
+  const long L = (long)lat_f * Hp * Wp;
+  Layout y = make_layout(*cfg, B, L, false);
+  if (y.total > WAN_NOALLOC_SCRATCH_BYTES) return WAN_ERR_WORKSPACE;
+  char *ws = scratch_base();
+  if (!ws) return WAN_ERR_HIP;
+  return block_run(*cfg, x, B, L, mod, *w, ctx, img_ctx, nullptr, ws, y, S(stream));
 }
 
 int wan_dit_step_fwd(const wan_cfg_t *cfg, const float *latent, const float *t, int B, int lat_f,
