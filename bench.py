@@ -80,11 +80,15 @@ def cpu_baseline(work, inp, tw, bw, budget_s: float = 25.0):
     extrapolated linearly in r to r = L and turned into tokens/s."""
     import numpy as np
     import oracle.wan_oracle as O
+    blas, threads = "unknown", 1
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            threads = max(i.get("num_threads", 1) for i in info)
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        pass
     m = work.model
     L = work.L
     m_vec = O.tmlp(inp["t"], tw["w1"], tw["b1"], tw["w2"], tw["b2"])
@@ -99,11 +103,129 @@ def cpu_baseline(work, inp, tw, bw, budget_s: float = 25.0):
     per_row = max((t2 - t1) / (r2 - r1), 1e-9)
     fixed = max(t1 - per_row * r1, 0.0)
     full = fixed + per_row * L
-    return {"value": work.batch * L / full, "unit": "tokens/s", "cores": int(threads),
+    return {"value": work.batch * L / full, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+            "blas_threads": int(threads), "blas": blas, "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"oracle.block on {r1} and {r2} sampled query rows of the same input "
                       f"(K/V for all {L} tokens each time; {t1:.1f}s and {t2:.1f}s); full-block time "
                       f"{full:.1f}s extrapolated linearly in the row count"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (what lscpu prints as 'Model name')."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def block_gemm_leg(W, B, L, d, F, stream, reps=10):
+    """The block's Linear layers on its own kernels (wan_linear_fwd), HIP events
+    on the launch stream: Q||K (bf16 out), V^T (the swapped-operand GEMM),
+    the d x d out-projection (float32 out, as the residual epilogue), the
+    cross-attention query, FFN up (GELU) and FFN down (float32 out)."""
+    import torch
+    M = B * L
+    shapes = [("qk", M, 2 * d, d, 0), ("vt", d, L, d, 0), ("oproj", M, d, d, 1), ("ca_q", M, d, d, 0),
+              ("ffn_up", M, F, d, 2), ("ffn_down", M, d, F, 1)]
+    g = torch.Generator(device="cpu").manual_seed(11)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res, tot_ms, tot_fl = {}, 0.0, 0.0
+    for name, m, n, k, mode in shapes:
+        x = torch.randn((m, k), generator=g).to(torch.bfloat16).cuda()
+        w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16).cuda()
+        b = (torch.randn(n, generator=g) * 0.02).to(torch.bfloat16).cuda()
+        y = torch.empty((m, n), dtype=torch.float32 if mode == 1 else torch.bfloat16, device="cuda")
+        run = lambda: W.linear_fwd(x, w, b, y, m, n, k, mode, stream)
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        fl = 2.0 * m * n * k
+        mult = 2 if name in ("oproj", "ca_q") else 1      # the block runs two of the d x d shapes each
+        tot_ms += ms * mult
+        tot_fl += fl * mult
+        res[name] = {"M": m, "N": n, "K": k, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                     "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    return {"kernel": "k_gemm_bf16", "shapes": res, "sum_ms": round(tot_ms, 4),
+            "tflops": round(tot_fl / tot_ms / 1e9, 1), "frac": round(tot_fl / tot_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "note": "sum over the block's GEMMs (the d x d projection shape counted for the SA and CA "
+                    "out-projections and for the CA query and Q-side shapes it stands for)"}
+
+
+def ln_leg(W, B, L, d, stream, reps=20):
+    """LayerNorm + modulate of the residual stream (wan_ln_modulate_fwd): 4 B
+    read + 2 B written per element, against HBM's 8 TB/s."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(13)
+    x = torch.randn((B, L, d), generator=g).cuda()
+    mod = (torch.randn((B, 6 * d), generator=g) * 0.3).cuda()
+    h = torch.empty((B * L, d), dtype=torch.bfloat16, device="cuda")
+    run = lambda: W.ln_modulate_fwd(x, B, L, d, mod, 0, 1e-6, h, stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    by = 6.0 * B * L * d
+    return {"kernel": "k_ln_mod_reg", "ms": round(ms, 4), "bytes": int(by), "gbs": round(by / ms / 1e6, 1),
+            "peak_gbs": PEAK_HBM_GBS, "frac": round(by / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+
+def step_leg(W, work, steps=2, warmup=1):
+    """The full denoising step of a step workload (the 1.3B guidance pair: 30
+    blocks, B = 2, L = 32760): wan_dit_step_fwd, weights drawn on the device
+    (N(0, 0.02), bf16), HIP events on the launch stream."""
+    import torch
+
+    import synth
+    m = work.model
+    B, L = work.batch, work.L
+    cfg = W.make_cfg(dim=m.dim, heads=m.heads, ffn=m.ffn, n_blocks=m.n_blocks, in_ch=m.in_ch,
+                     out_ch=m.out_ch, freq_dim=m.freq_dim, text_len=m.text_len, eps=m.eps, dtype=m.dtype)
+    mw = synth.device_model_weights(work)
+    mws, keep = W.model_weights(mw, [W.block_weights(b) for b in mw["blocks"]])
+    inp = synth.workload_inputs(work)
+    lat = torch.from_numpy(inp["latent"]).cuda()
+    t = torch.from_numpy(inp["t"]).cuda()
+    ctx = torch.from_numpy(inp["ctx"]).to(torch.bfloat16).cuda()
+    out = torch.empty((B, 16, work.lat_f, work.lat_h, work.lat_w), dtype=torch.float32, device="cuda")
+    ws = torch.empty(W.workspace_bytes(cfg, B, work.lat_f, work.lat_h, work.lat_w), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    run = lambda: W.dit_step_fwd(cfg, lat, t, ctx, None, mws, out, ws, stream)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("non-finite step output")
+    gemm_f, sa_f, ca_f = block_flops(B, L, m.dim, m.heads, m.ffn, m.text_len)
+    fl = m.n_blocks * (gemm_f + sa_f + ca_f)
+    return {"workload": work.name, "blocks": m.n_blocks, "batch": B, "tokens": L, "steps": steps,
+            "ms_per_step": round(ms, 3), "latent_tokens_per_s": round(B * L / (ms * 1e-3), 1),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+            "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def traffic_pass(W, B, L, d, H, dev):
@@ -567,6 +689,10 @@ def main():
                                                ms, tm, "fp8 e4m3 Linear layers, 8-bit self-attention "
                                                        "(Int8 QK^T, E4M3 PV)")
         out["attn8"] = attn8_leg(W, B, L, d, H, qk, vt, Lp, stream, n_att, attn_ms, sa_f)
+    out["gemm"] = block_gemm_leg(W, B, L, d, F, stream)
+    out["ln_modulate"] = ln_leg(W, B, L, d, stream)
+    if args.config == 2:
+        out["c3_step"] = step_leg(W, synth.CONFIGS[3])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work, inp, tw, bw)
     print(json.dumps(out), flush=True)

@@ -324,6 +324,20 @@ int wan_attention_8bit_fwd(const void *q, int ldq, const void *k, int ldk, const
                            int vt_bstride, void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* The block's normalisation before a branch ([Note] Diffusion Transformer:
+ * shared AdaLN; LayerNorm without affine, eps inside the square root):
+ *   h = (x - mean) / sqrt(var + eps) * (1 + scale) + shift  over the last axis
+ *   (biased variance), rounded to bf16.
+ * x [B, L, d] float32 device; mod [B, 6d] float32 device: a block's combined
+ * modulation (the shared MLP output plus the block's own bias; order shift1,
+ * scale1, gate1, shift2, scale2, gate2), or NULL for the plain LayerNorm of
+ * the cross-attention; branch 0 takes (shift1, scale1), branch 1 (shift2,
+ * scale2); h [B*L, d] bf16 device.  Errors: WAN_ERR_NULL for a NULL x / h,
+ * WAN_ERR_SHAPE for B outside 1..8, L or d <= 0, B*L > 2^30 or eps not
+ * positive and finite, WAN_ERR_CONFIG for another branch with mod given. */
+int wan_ln_modulate_fwd(const float *x, int B, int L, int d, const float *mod, int branch, float eps,
+                        void *h, void *stream);
+
 /* One Linear layer of the block ([Note] Diffusion Transformer: the attention
  * projections; [Note] 配置表: the FFN of width ffn with GELU):
  *   y = x W^T + b for a bf16 x [M, K], W [N, K], b [N] or NULL (all device,

@@ -238,3 +238,13 @@ def test_noalloc_scratch_limit(W):
                                        None, None) == -1
     assert L.wan_dit_block_fwd_noalloc(C.byref(c), dummy, 1, 2, 30, 52, dummy, C.byref(bw), dummy,
                                        dummy, None) == -5                  # image context without img_len
+
+
+def test_ln_modulate_invalid_arguments(W):
+    L = W.lib()
+    dummy = C.c_void_p(256)   # never dereferenced: every call below fails validation first
+    assert L.wan_ln_modulate_fwd(None, 1, 4, 8, None, 0, 1e-6, dummy, None) == -1
+    assert L.wan_ln_modulate_fwd(dummy, 9, 4, 8, None, 0, 1e-6, dummy, None) == -2     # B > 8
+    assert L.wan_ln_modulate_fwd(dummy, 1, 0, 8, None, 0, 1e-6, dummy, None) == -2     # L = 0
+    assert L.wan_ln_modulate_fwd(dummy, 1, 4, 8, None, 0, 0.0, dummy, None) == -2      # eps
+    assert L.wan_ln_modulate_fwd(dummy, 1, 4, 8, dummy, 2, 1e-6, dummy, None) == -5    # branch

@@ -122,3 +122,26 @@ def test_linear(M, N, K, mode):
         ref = O.gelu_tanh(ref)
     tol = 1e-4 if mode == 1 else 3e-2
     assert_parity(ty.float().cpu().numpy(), ref, tol, 1e-2 if mode != 1 else 1e-5, f"linear {mode}")
+
+
+@pytest.mark.parametrize("B,L,d,branch", [(2, 300, 1536, 0), (1, 257, 1536, 1), (1, 77, 384, -1),
+                                          (2, 50, 200, 0)])
+def test_ln_modulate(B, L, d, branch):
+    """wan_ln_modulate_fwd: LayerNorm (+ the block's modulation of one branch)
+    to bf16, against the oracle's layer_norm / modulate; d = 200 takes the
+    generic kernel."""
+    print(f"ln_modulate B={B} L={L} d={d} branch={branch}", flush=True)
+    import video_diffusion_transformer_block_amd as W
+    from tests.gpu_util import DEV, assert_parity
+    g = np.random.default_rng([B, L, d])
+    x = (g.standard_normal((B, L, d)) * 1.5 + 0.3).astype(np.float32)
+    mod = (g.standard_normal((B, 6 * d)) * 0.3).astype(np.float32)
+    tx, tm = torch.from_numpy(x).to(DEV), torch.from_numpy(mod).to(DEV)
+    h = torch.empty((B * L, d), dtype=torch.bfloat16, device=DEV)
+    W.ln_modulate_fwd(tx, B, L, d, tm if branch >= 0 else None, branch, 1e-6, h)
+    torch.cuda.synchronize()
+    ref = O.layer_norm(x, 1e-6)
+    if branch >= 0:
+        sh, sc = (0, d) if branch == 0 else (3 * d, 4 * d)
+        ref = np.stack([O.modulate(ref[b], mod[b, sh:sh + d], mod[b, sc:sc + d]) for b in range(B)])
+    assert_parity(h.float().cpu().numpy().reshape(B, L, d), ref, 3e-2, 1e-2, "ln_modulate")

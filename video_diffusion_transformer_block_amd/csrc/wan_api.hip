@@ -1049,6 +1049,18 @@ int wan_sample_fp8_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, in
                     (char *)ws, y, t_off, v_off, S(stream), (const char *)qbuf);
 }
 
+int wan_ln_modulate_fwd(const float *x, int B, int L, int d, const float *mod, int branch, float eps,
+                        void *h, void *stream) {
+  if (!x || !h) return WAN_ERR_NULL;
+  if (B <= 0 || B > 8 || L <= 0 || d <= 0 || (long)B * L > (1L << 30)) return WAN_ERR_SHAPE;
+  if (!(eps > 0.f) || !isfinite(eps)) return WAN_ERR_SHAPE;
+  if (mod && branch != 0 && branch != 1) return WAN_ERR_CONFIG;
+  const int shift_off = branch ? 3 * d : 0, scale_off = branch ? 4 * d : d;
+  WAN_TRY(launch_ln_mod(x, B * L, L, d, mod, 6L * d, shift_off, scale_off, mod != nullptr, eps, h, 0,
+                        S(stream)));
+  return WAN_OK;
+}
+
 int wan_linear_fwd(const void *x, const void *w, const void *b, void *y, int M, int N, int K,
                    int mode, void *stream) {
   if (!x || !w || !y) return WAN_ERR_NULL;
