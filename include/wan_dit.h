@@ -324,6 +324,17 @@ int wan_attention_8bit_fwd(const void *q, int ldq, const void *k, int ldk, const
                            int vt_bstride, void *o, int ldo, int B, int H, int Lq, int Lk, int q_scaled,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* Measurement hook (for timing the dominant kernel of [Note] Infra's workload
+ * split, the full self-attention, inside the block's own launch sequence):
+ * start / stop are hipEvent_t handles the library records on the call's
+ * stream immediately before and after every bf16 or 8-bit self-attention of
+ * the block, step and sampler calls this host thread makes next (a call with
+ * several blocks records them for each block; the last pair stays).  Both
+ * NULL: no recording (the default).  Per host thread; the caller owns the
+ * events.  Errors: WAN_ERR_NULL when only one of the two is NULL.  A failed
+ * record surfaces as WAN_ERR_HIP from the block call. */
+int wan_set_attention_events(void *start, void *stop);
+
 /* The block's normalisation before a branch ([Note] Diffusion Transformer:
  * shared AdaLN; LayerNorm without affine, eps inside the square root):
  *   h = (x - mean) / sqrt(var + eps) * (1 + scale) + shift  over the last axis

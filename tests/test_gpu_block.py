@@ -139,3 +139,40 @@ def test_block_branches_full_size(branch):
     c = assert_parity(_centered(g), _centered(o), 3e-2, 0.1 if branch == "sa" else 1e-2,
                       f"{branch} branch, token-dependent part")
     print(f"  raw {r}  centred {c}", flush=True)
+
+
+def test_attention_event_hook_times_the_block_attention():
+    """wan_set_attention_events: the events bracket the block's self-attention
+    launch (a positive time shorter than the whole block) and change nothing
+    in the output; cleared, the next call records nothing."""
+    import video_diffusion_transformer_block_amd as W
+    from tests.gpu_util import cfg_of, run_tmlp, up, up_block, workspace
+    work = MINI_BLOCKS["bf16-ragged-b2"]
+    m = work.model
+    cfg = cfg_of(work)
+    inp = synth.workload_inputs(work)
+    tw = synth.tmlp_weights(work)
+    bwd = up_block(synth.block_weights(work, 0), m.dtype)
+    mod = run_tmlp(cfg, work, {k: up(v, m.dtype) for k, v in tw.items()}, up(inp["t"], "f32"))
+    ctx, ws = up(inp["ctx"], m.dtype), workspace(cfg, work)
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record(s)
+    x_ref = up(inp["x"], "f32")
+    W.dit_block_fwd(cfg, x_ref, work.batch, work.lat_f, work.Hp, work.Wp, mod, W.block_weights(bwd), ctx,
+                    None, ws)
+    x = up(inp["x"], "f32")
+    ev[2].record(s)
+    W.set_attention_events(ev[0], ev[1])
+    W.dit_block_fwd(cfg, x, work.batch, work.lat_f, work.Hp, work.Wp, mod, W.block_weights(bwd), ctx,
+                    None, ws)
+    W.set_attention_events(None, None)
+    ev[3].record(s)
+    torch.cuda.synchronize()
+    assert torch.equal(x, x_ref)
+    sa, blk = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    print(f"self-attention {sa:.4f} ms of a {blk:.4f} ms block", flush=True)
+    assert 0 < sa < blk
+    with pytest.raises(W.WanError):
+        W.set_attention_events(ev[0], None)

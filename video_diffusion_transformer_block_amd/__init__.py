@@ -14,5 +14,5 @@ from .binding import (NOALLOC_SCRATCH_BYTES, Cfg, WanError, attention_fwd, atten
                       sample_fp8_fwd,
                       dit_step_cached_fwd, dit_step_fwd, euler_fwd, i2v_mask, kv_cache_bytes,
                       kv_cache_fwd, lib, linear_fp8_fwd, linear_fwd, ln_modulate_fwd, make_cfg, model_weights, sample_fwd,
-                      quantize_rows_fp8, quantize_tensor_fp8, sample_workspace_bytes, status_str,
+                      quantize_rows_fp8, quantize_tensor_fp8, sample_workspace_bytes, set_attention_events, status_str,
                       tmlp_fwd, tmlp_weights, workspace_bytes)

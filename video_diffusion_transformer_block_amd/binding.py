@@ -30,7 +30,8 @@ EXPORTS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_by
            "wan_model_fp8_bytes", "wan_quantize_model_fp8", "wan_fp8_workspace_bytes",
            "wan_dit_step_fp8_fwd", "wan_sample_fp8_fwd", "wan_attention_8bit_workspace_bytes",
            "wan_attention_8bit_quantize", "wan_attention_8bit_q_fwd", "wan_attention_8bit_fwd",
-           "wan_dit_block_noalloc_bytes", "wan_dit_block_fwd_noalloc", "wan_ln_modulate_fwd")
+           "wan_dit_block_noalloc_bytes", "wan_dit_block_fwd_noalloc", "wan_ln_modulate_fwd",
+           "wan_set_attention_events")
 _SIZE_FNS = ("wan_workspace_bytes", "wan_kv_cache_bytes", "wan_sample_workspace_bytes",
              "wan_block_fp8_bytes", "wan_block_fp8_workspace_bytes", "wan_model_fp8_bytes",
              "wan_fp8_workspace_bytes", "wan_attention_8bit_workspace_bytes",
@@ -96,6 +97,7 @@ def lib() -> C.CDLL:
         L.wan_attention_fwd.argtypes = [vp, i, vp, i, vp, i, i, vp, i, i, i, i, i, i, vp]
         L.wan_linear_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
         L.wan_ln_modulate_fwd.argtypes = [vp, i, i, i, vp, i, C.c_float, vp, vp]
+        L.wan_set_attention_events.argtypes = [vp, vp]
         L.wan_kv_cache_bytes.argtypes = [C.POINTER(Cfg), i]
         L.wan_kv_cache_bytes.restype = sz
         L.wan_sample_workspace_bytes.argtypes = [C.POINTER(Cfg), i, i, i, i]
@@ -259,6 +261,14 @@ def attention_8bit_fwd(q, ldq, k, ldk, vt, ldv, vt_bstride, o, ldo, B, H, Lq, Lk
 def linear_fwd(x, w, b, y, M, N, K, mode, stream=None):
     _check("wan_linear_fwd", lib().wan_linear_fwd(_p(x), _p(w), _p(b), _p(y), M, N, K, mode,
                                                   _stream(stream)))
+
+
+def set_attention_events(start=None, stop=None):
+    """Events (torch.cuda.Event, already created by a first record) the library
+    records around the self-attention launches of this thread's next block
+    calls; None, None clears them."""
+    ev = lambda e: None if e is None else e.cuda_event
+    _check("wan_set_attention_events", lib().wan_set_attention_events(ev(start), ev(stop)))
 
 
 def ln_modulate_fwd(x, B, L, d, mod, branch, eps, h, stream=None):

@@ -36,6 +36,11 @@ static __device__ __align__(256) char scratch[WAN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
+// events the calling host thread asked to have recorded around its next
+// self-attention launches (wan_set_attention_events); per thread, so calls
+// from other threads are unaffected
+thread_local hipEvent_t att_ev_start = nullptr, att_ev_stop = nullptr;
+
 constexpr size_t ALIGN = 256;
 size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 long rup(long v, long a) { return (v + a - 1) / a * a; }
@@ -387,6 +392,17 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
                                         (int)L, (int)L, false), s);
   };
 
+  // the self-attention, between the measurement events when the thread has set them
+  auto self_attn_timed = [&]() -> hipError_t {
+    if (att_ev_start) {
+      const hipError_t e = hipEventRecord(att_ev_start, s);
+      if (e != hipSuccess) return e;
+    }
+    const hipError_t e = self_attn();
+    if (e != hipSuccess || !att_ev_stop) return e;
+    return hipEventRecord(att_ev_stop, s);
+  };
+
   WAN_TRY(launch_mod_combine(mod, w.mod_bias, modb, B, 6 * d, s));
   // ---- self-attention branch
   WAN_TRY(ln(0, d, 1));
@@ -405,7 +421,7 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
       g.npad = (int)y.Lp;
       WAN_TRY(launch_gemm(fp8(g, q8->sc + 0, 0, q8->as + (long)b * L, 1), s));
     }
-    WAN_TRY(self_attn());
+    WAN_TRY(self_attn_timed());
   } else {
     GemmDesc gqk = gemm(h, d, w.sa_wqkv, d, M, 2 * d, d, w.sa_bqkv, OUT_BF16, qk, 2 * d, 0);
     WAN_TRY(launch_gemm(c.attn8 ? gqk : qscaled(gqk, d, hd), s));
@@ -417,7 +433,7 @@ int block_run(const wan_cfg_t &c, float *x, int B, long L, const float *mod,
       g.npad = (int)y.Lp;   // keys L .. Lp-1 of this batch segment are zero
       WAN_TRY(launch_gemm(g, s));
     }
-    WAN_TRY(self_attn());
+    WAN_TRY(self_attn_timed());
   }
   WAN_TRY(linear(resid(o, d, w.sa_wo, M, d, d, w.sa_bo, x, modb + 2 * d, 6 * d, (int)L, f32), 1,
                  false));
@@ -1047,6 +1063,13 @@ int wan_sample_fp8_fwd(const wan_cfg_t *cfg, float *latent, int B, int lat_f, in
   if (ws_bytes < sample_extra(B, cfg->out_ch, plane, &t_off, &v_off, y.total)) return WAN_ERR_WORKSPACE;
   return sample_run(*cfg, latent, B, lat_f, H8, W8, n_steps, guided, scale, (const char *)kv_cache, *w,
                     (char *)ws, y, t_off, v_off, S(stream), (const char *)qbuf);
+}
+
+int wan_set_attention_events(void *start, void *stop) {
+  if ((start == nullptr) != (stop == nullptr)) return WAN_ERR_NULL;
+  att_ev_start = static_cast<hipEvent_t>(start);
+  att_ev_stop = static_cast<hipEvent_t>(stop);
+  return WAN_OK;
 }
 
 int wan_ln_modulate_fwd(const float *x, int B, int L, int d, const float *mod, int branch, float eps,
