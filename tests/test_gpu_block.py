@@ -66,15 +66,28 @@ def test_block_mini(name):
         assert_parity(g_x - x0, o_x - x0, 3e-2, 1e-2, "block update")
 
 
-@pytest.mark.parametrize("cid", [2, 4])
+# the full-size blocks: 1.3B at 480P, 14B at 720P, and one block of the 14B
+# image-to-video model at 480P (d = 5120, 40 heads, 257 image tokens beside the
+# 512 text tokens: [Note] I2V 架构扩展, decoupled cross-attention)
+FULL_BLOCKS = {
+    2: synth.CONFIGS[2],
+    4: synth.CONFIGS[4],
+    "i2v14b": synth.mini(51, "wan14b-i2v-block-480p", dim=5120, heads=40, ffn=13824, n_blocks=1,
+                         lat_f=21, lat_h=60, lat_w=104, batch=1, text_len=512, img_len=257,
+                         kind="block"),
+}
+
+
+@pytest.mark.parametrize("cid", list(FULL_BLOCKS))
 def test_block_full_size_sampled_rows(cid):
     from tests.gpu_util import assert_parity
-    work = synth.CONFIGS[cid]
+    work = FULL_BLOCKS[cid]
     L = work.L
-    rng = np.random.default_rng(cid)
+    rng = np.random.default_rng(work.cid)
     rows = np.unique(np.concatenate([[0, 1, 255, 256, L - 1, L - 2, (L // 256) * 256],
                                      rng.integers(0, L, 57)]))
-    print(f"block C{cid} full size L={L}, {len(rows)} sampled rows", flush=True)
+    print(f"block {work.name} full size L={L} d={work.model.dim} img={work.model.img_len}, "
+          f"{len(rows)} sampled rows", flush=True)
     x0, g_mod, o_mod, g_x, o_x = _run_block(work, rows=rows)
     assert_parity(g_mod, o_mod, 1e-4, 1e-5, "t-MLP")
     assert_parity(g_x[:, rows], o_x, 3e-2, 1e-2, "block output (sampled rows)")
