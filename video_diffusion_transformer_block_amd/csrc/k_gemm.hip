@@ -116,8 +116,8 @@ WAN_DEV void epilogue_regs(const GemmDesc &g, const f32x16 (&acc)[4][2], int lan
 
 // Epilogue of bf16 outputs through LDS: per wave 4 slabs of 32 rows x 64
 // columns (fp32, padded rows), written from the transposed tile's runs of 4
-// columns, read back so that every lane finishes 8 contiguous columns
-// (cb + 8q, q = 0..3) of one row and stores 16 bytes.  Everything it reads
+// columns, read back so that every lane finishes 8 contiguous columns of one
+// row per pass and stores 16 bytes.  Everything it reads
 // from global memory (bias, FP8 scales) is loaded before its first store: the
 // memory counter retires in issue order, so a load issued after a store would
 // wait for that store.  The caller has synchronised the workgroup.
@@ -128,36 +128,34 @@ WAN_DEV void epilogue(const GemmDesc &g, const f32x16 (&acc)[4][2], float *lds, 
   const int half = lane >> 5, l32 = lane & 31;
   constexpr int EP = 68;
   float *ep = lds + w * 32 * EP;
-  const int row = lane >> 1, cb = (lane & 1) * 32;
-  const int nb = n0 + wn * 64 + cb;          // column of q = 0
-  const int mb = m0 + wm * 128 + row;        // row of slab 0
+  // read-back: in pass p a lane finishes row 8p + lane/8 of the slab, columns
+  // c8 .. c8+7 (c8 = 8 (lane % 8)), so one store instruction writes 8 rows of
+  // 128 contiguous bytes (the previous mapping, 2 lanes per row 32 columns
+  // apart, spread each store over 32 rows and ran 3-8% slower)
+  const int rr = lane >> 3, c8 = (lane & 7) * 8;
+  const int n = n0 + wn * 64 + c8;             // this lane's first column
+  const int mb = m0 + wm * 128 + rr;           // row of slab 0, pass 0
   const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
-  // column terms of the lane's 32 columns (a bias per column, or an FP8
-  // scale per column when the columns are tokens: the bias-rows GEMMs), row
-  // terms of its 4 rows (indices clamped into the matrix; clamped values are
-  // never stored)
   constexpr bool CADD = !BROWS, CMUL = SCALED && BROWS;
-  bf16x8 cadd[4];   // kept as bf16: 4 registers per 8 columns
-  float cmul[4][8], radd[4], rmul[4];
+  // column terms of the lane's 8 columns, row terms of its 16 rows (indices
+  // clamped into the matrix; clamped values are never stored), all loaded
+  // before the first store
+  bf16x8 cadd;
+  float cmul[8], radd[16], rmul[16];
+  if (CADD && bias && n + 8 <= g.N) {
+    const uint4 u = ld16(bias + n);
+    cadd = *reinterpret_cast<const bf16x8 *>(&u);
+  } else {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int n = nb + q * 8;
-    if (CADD && bias && n + 8 <= g.N) {
-      const uint4 u = ld16(bias + n);
-      cadd[q] = *reinterpret_cast<const bf16x8 *>(&u);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        cadd[q][k] = CADD && bias ? bias[n + k < g.N ? n + k : g.N - 1] : (bf16)0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      cmul[q][k] = CMUL ? g.b_scale[g.b_per_col ? (n + k < g.N ? n + k : g.N - 1) : 0] : 1.f;
+    for (int k = 0; k < 8; ++k) cadd[k] = CADD && bias ? bias[n + k < g.N ? n + k : g.N - 1] : (bf16)0.f;
   }
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    cmul[k] = CMUL ? g.b_scale[g.b_per_col ? (n + k < g.N ? n + k : g.N - 1) : 0] : 1.f;
   const float csc = SCALED && !CMUL ? g.b_scale[0] : 1.f;   // a per-tensor column scale
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int mc = min(mb + i * 32, g.M - 1);
+  for (int i = 0; i < 16; ++i) {
+    const int mc = min(mb + (i >> 2) * 32 + (i & 3) * 8, g.M - 1);
     radd[i] = bias && BROWS ? (float)bias[mc] : 0.f;
     rmul[i] = SCALED ? g.a_scale[g.a_per_row ? mc : 0] * csc : 1.f;
   }
@@ -174,30 +172,29 @@ WAN_DEV void epilogue(const GemmDesc &g, const f32x16 (&acc)[4][2], float *lds, 
             make_float4(acc[i][jj][4 * q], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2], acc[i][jj][4 * q + 3]);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
-    const int m = mb + i * 32;
-    if (m < g.M) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nb + q * 8;
-        if (n < lim) {
-          const float4 u0 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8);
-          const float4 u1 = *reinterpret_cast<const float4 *>(ep + row * EP + cb + q * 8 + 4);
-          float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    for (int p = 0; p < 4; ++p) {
+      const int r = 8 * p + rr;
+      const int m = mb + i * 32 + 8 * p;
+      if (m < g.M && n < lim) {
+        const float4 u0 = *reinterpret_cast<const float4 *>(ep + r * EP + c8);
+        const float4 u1 = *reinterpret_cast<const float4 *>(ep + r * EP + c8 + 4);
+        float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        const int ri = i * 4 + p;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            v[k] = v[k] * rmul[i] * (CMUL ? cmul[q][k] : 1.f) + radd[i] + (CADD ? (float)cadd[q][k] : 0.f);
-            if (KIND == OUT_GELU) v[k] = gelu_tanh(v[k]);
-            if (KIND == OUT_BF16 && n < g.scale_cols) v[k] *= g.col_scale;
-          }
-          bf16 *c = reinterpret_cast<bf16 *>(g.C) + (long)m * g.ldc + n;
-          if (n + 8 <= g.N) {
-            bf16x8 o;
+        for (int k = 0; k < 8; ++k) {
+          v[k] = v[k] * rmul[ri] * (CMUL ? cmul[k] : 1.f) + radd[ri] + (CADD ? (float)cadd[k] : 0.f);
+          if (KIND == OUT_GELU) v[k] = gelu_tanh(v[k]);
+          if (KIND == OUT_BF16 && n < g.scale_cols) v[k] *= g.col_scale;
+        }
+        bf16 *c = reinterpret_cast<bf16 *>(g.C) + (long)m * g.ldc + n;
+        if (n + 8 <= g.N) {
+          bf16x8 o;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) o[k] = f2bf(v[k]);
-            *reinterpret_cast<bf16x8 *>(c) = o;
-          } else {
-            for (int k = 0; k < 8 && n + k < lim; ++k) c[k] = n + k < g.N ? f2bf(v[k]) : f2bf(0.f);
-          }
+          for (int k = 0; k < 8; ++k) o[k] = f2bf(v[k]);
+          *reinterpret_cast<bf16x8 *>(c) = o;
+        } else {
+          for (int k = 0; k < 8 && n + k < lim; ++k) c[k] = n + k < g.N ? f2bf(v[k]) : f2bf(0.f);
         }
       }
     }
