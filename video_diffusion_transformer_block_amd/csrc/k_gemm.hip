@@ -42,78 +42,6 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 // have landed and every LDS read of this wavefront has returned
 template <int N> WAN_DEV void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0070 | N); }
 
-// Epilogue of a float32 output on 4 consecutive columns n..n+3 (n % 4 == 0)
-// of row m, or element-wise for a ragged column tail: a plain store, or the
-// gated residual x += gate * v into the float32 stream.
-template <int KIND, bool BROWS, bool SCALED>
-WAN_DEV void epi4(const GemmDesc &g, int m, int n, float *v) {
-  static_assert(KIND == OUT_F32 || KIND == OUT_RESID, "float32 outputs only");
-  static_assert(!BROWS, "bias along rows: bf16 outputs only");
-  const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
-  const bool full = n + 4 <= g.N;
-  if (SCALED) {   // FP8 dequantisation: row scale (per token or per tensor) times the tensor's
-    const float sc = g.a_scale[g.a_per_row ? m : 0] * g.b_scale[0];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] *= sc;
-  }
-  if (bias) {
-    if (full) {
-      const uint2 u = *reinterpret_cast<const uint2 *>(bias + n);
-      const bf16 *e = reinterpret_cast<const bf16 *>(&u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] += (float)e[i];
-    } else {
-      for (int i = 0; i < 4 && n + i < g.N; ++i) v[i] += (float)bias[n + i];
-    }
-  }
-  if (KIND == OUT_F32) {
-    float *c = reinterpret_cast<float *>(g.C) + (long)m * g.ldc + n;
-    if (full) *reinterpret_cast<float4 *>(c) = make_float4(v[0], v[1], v[2], v[3]);
-    else
-      for (int i = 0; i < 4 && n + i < g.N; ++i) c[i] = v[i];
-  } else {  // OUT_RESID: x += gate * v
-    float *xp = g.X + (long)m * g.ldx + n;
-    const float *gp = g.gate ? g.gate + (long)(m / g.rows_per_batch) * g.gate_bstride + n : nullptr;
-    if (full) {
-      float4 x = *reinterpret_cast<float4 *>(xp);
-      if (gp) {
-        const float4 gg = *reinterpret_cast<const float4 *>(gp);
-        x.x += gg.x * v[0]; x.y += gg.y * v[1]; x.z += gg.z * v[2]; x.w += gg.w * v[3];
-      } else {
-        x.x += v[0]; x.y += v[1]; x.z += v[2]; x.w += v[3];
-      }
-      *reinterpret_cast<float4 *>(xp) = x;
-    } else {
-      for (int i = 0; i < 4 && n + i < g.N; ++i) xp[i] += (gp ? gp[i] : 1.0f) * v[i];
-    }
-  }
-}
-
-// Epilogue straight from the accumulators, no LDS: the tile is computed with
-// the MFMA operands swapped (C^T = B A^T), so lane l of block (i, j) of
-// wavefront (wm, wn) holds C[m][n .. n+3] in registers 4q .. 4q+3, with
-// m = m0 + wm*128 + i*32 + l%32 and n = n0 + wn*64 + j*32 + 8q + 4(l/32).
-template <int KIND, bool BROWS, bool SCALED>
-WAN_DEV void epilogue_regs(const GemmDesc &g, const f32x16 (&acc)[4][2], int lane, int m0, int n0,
-                           int wm, int wn) {
-  const int half = lane >> 5, l32 = lane & 31;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 128 + i * 32 + l32;
-    if (m >= g.M) continue;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 64 + j * 32 + q * 8 + half * 4;
-        if (n < g.N) {
-          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          epi4<KIND, BROWS, SCALED>(g, m, n, v);
-        }
-      }
-  }
-}
-
 // Epilogue of bf16 outputs through LDS: per wave 4 slabs of 32 rows x 64
 // columns (fp32, padded rows), written from the transposed tile's runs of 4
 // columns, read back so that every lane finishes 8 contiguous columns of one
@@ -203,13 +131,119 @@ WAN_DEV void epilogue(const GemmDesc &g, const f32x16 (&acc)[4][2], float *lds, 
   }
 }
 
+// Epilogue of float32 outputs through LDS: the slabs of the bf16 epilogue,
+// read back with 16 lanes per row (4 columns, 16 bytes each), so one store
+// writes 4 rows of 256 contiguous bytes.  The gated residual reads x[m, n]
+// with the same pattern; the gate rows of the wave's 128 rows are loaded
+// before the first store when those rows span at most two batch samples.
+template <int KIND, bool SCALED>
+WAN_DEV void epilogue_f32(const GemmDesc &g, const f32x16 (&acc)[4][2], float *lds, int w, int lane,
+                          int m0, int n0, int wm, int wn) {
+  static_assert(KIND == OUT_F32 || KIND == OUT_RESID, "float32 outputs only");
+  const int half = lane >> 5, l32 = lane & 31;
+  constexpr int EP = 68;
+  float *ep = lds + w * 32 * EP;
+  const int rr = lane >> 4, c4 = (lane & 15) * 4;
+  const int n = n0 + wn * 64 + c4;
+  const int mw = m0 + wm * 128;
+  const bool full = n + 4 <= g.N;
+  const bf16 *bias = reinterpret_cast<const bf16 *>(g.bias);
+  float b4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (bias && n < g.N) {
+    if (full) {
+      const uint2 u = *reinterpret_cast<const uint2 *>(bias + n);
+      const bf16 *e = reinterpret_cast<const bf16 *>(&u);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) b4[k] = (float)e[k];
+    } else {
+      for (int k = 0; k < 4; ++k) b4[k] = n + k < g.N ? (float)bias[n + k] : 0.f;
+    }
+  }
+  float rmul[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int mc = min(mw + i * 32 + l32, g.M - 1);
+    rmul[i] = SCALED ? g.a_scale[g.a_per_row ? mc : 0] * g.b_scale[0] : 1.f;
+  }
+  // gates of the first and the last row's sample (columns clamped into N)
+  float4 gA = make_float4(1.f, 1.f, 1.f, 1.f), gB = gA;
+  int mB = 0x7fffffff;          // first row of the second sample
+  bool two = true;
+  if (KIND == OUT_RESID && g.gate) {
+    const int rpb = g.rows_per_batch;
+    const int bA = mw / rpb, bL = min(mw + 127, g.M - 1) / rpb;
+    two = bL - bA <= 1;
+    mB = (bA + 1) * rpb;
+    const int nc = full ? n : 0;
+    const float *gp = g.gate + nc;
+    gA = *reinterpret_cast<const float4 *>(gp + (long)bA * g.gate_bstride);
+    gB = *reinterpret_cast<const float4 *>(gp + (long)bL * g.gate_bstride);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(ep + l32 * EP + jj * 32 + q * 8 + half * 4) =
+            make_float4(acc[i][jj][4 * q] * rmul[i], acc[i][jj][4 * q + 1] * rmul[i],
+                        acc[i][jj][4 * q + 2] * rmul[i], acc[i][jj][4 * q + 3] * rmul[i]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    float4 xv[8];
+    if (KIND == OUT_RESID && full) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int m = mw + i * 32 + 4 * p + rr;
+        if (m < g.M) xv[p] = *reinterpret_cast<const float4 *>(g.X + (long)m * g.ldx + n);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int r = 4 * p + rr;
+      const int m = mw + i * 32 + r;
+      if (m < g.M && n < g.N) {
+        const float4 u = *reinterpret_cast<const float4 *>(ep + r * EP + c4);
+        float v[4] = {u.x + b4[0], u.y + b4[1], u.z + b4[2], u.w + b4[3]};
+        if (KIND == OUT_F32) {
+          float *c = reinterpret_cast<float *>(g.C) + (long)m * g.ldc + n;
+          if (full) *reinterpret_cast<float4 *>(c) = make_float4(v[0], v[1], v[2], v[3]);
+          else
+            for (int k = 0; k < 4 && n + k < g.N; ++k) c[k] = v[k];
+        } else {
+          float gg[4] = {1.f, 1.f, 1.f, 1.f};
+          if (g.gate) {
+            if (two && full) {
+              const float4 s = m < mB ? gA : gB;
+              gg[0] = s.x; gg[1] = s.y; gg[2] = s.z; gg[3] = s.w;
+            } else {
+              const float *gp = g.gate + (long)(m / g.rows_per_batch) * g.gate_bstride + n;
+              for (int k = 0; k < 4; ++k) gg[k] = n + k < g.N ? gp[k] : 0.f;
+            }
+          }
+          float *xp = g.X + (long)m * g.ldx + n;
+          if (full) {
+            float4 x = xv[p];
+            x.x += gg[0] * v[0]; x.y += gg[1] * v[1]; x.z += gg[2] * v[2]; x.w += gg[3] * v[3];
+            *reinterpret_cast<float4 *>(xp) = x;
+          } else {
+            for (int k = 0; k < 4 && n + k < g.N; ++k) xp[k] += gg[k] * v[k];
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // Every tile is computed transposed (C^T = B A^T: MFMA operands swapped), so
-// a lane holds runs of 4 consecutive columns of one output row.  Float32
-// outputs (plain and the residual update of the float32 stream) are written
-// straight from those registers: 16-byte runs per lane, no LDS round trip.
-// bf16 outputs are staged through LDS (one 16-byte write per run), so that
-// every lane then stores 16 contiguous bytes of bf16.
-template <int KIND> constexpr bool epi_from_regs() { return KIND == OUT_F32 || KIND == OUT_RESID; }
+// a lane holds runs of 4 consecutive columns of one output row.  Both
+// epilogues stage a wave's 32-row slab through LDS (one 16-byte write per run)
+// and read it back row-contiguous, so that each store instruction covers a few
+// whole 128-256 byte row segments (2 lanes per row, 32 columns apart, wrote
+// 32 rows x 32 bytes per float32 store and ran 12% slower at d x d).
+template <int KIND> constexpr bool epi_f32() { return KIND == OUT_F32 || KIND == OUT_RESID; }
 
 template <int KIND, bool BROWS>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
@@ -355,10 +389,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
   if (kt < KT) tile(kt, 0);
   if (kt + 1 < KT) tile(kt + 1, 1);
 
-  if constexpr (epi_from_regs<KIND>()) {
-    epilogue_regs<KIND, BROWS, false>(g, acc, lane, m0, n0, wm, wn);
+  __syncthreads();
+  if constexpr (epi_f32<KIND>()) {
+    epilogue_f32<KIND, false>(g, acc, reinterpret_cast<float *>(smem), w, lane, m0, n0, wm, wn);
   } else {
-    __syncthreads();
     epilogue<KIND, BROWS, false>(g, acc, reinterpret_cast<float *>(smem), w, lane, m0, n0, wm, wn);
   }
 }
@@ -532,11 +566,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(GemmDesc g) {
   for (; kt < KT; ++kt)             // the last 1 .. 3 tiles: one generic copy with run-time flags
     tile(kt, kt & 1, kt + 2 < KT, kt + 1 < KT);
 
-  if constexpr (epi_from_regs<KIND>()) {
-    epilogue_regs<KIND, BROWS, true>(g, acc, lane, m0, n0, wm, wn);
+  // 8 wavefronts x 32 rows x 68 floats staged through an LDS buffer of its own
+  __shared__ __attribute__((aligned(16))) float sEp[GW * 32 * 68];
+  if constexpr (epi_f32<KIND>()) {
+    static_assert(!BROWS, "bias along rows: bf16 outputs only");
+    epilogue_f32<KIND, true>(g, acc, sEp, w, lane, m0, n0, wm, wn);
   } else {
-    // 8 wavefronts x 32 rows x 68 floats staged through an LDS buffer of its own
-    __shared__ __attribute__((aligned(16))) float sEp[GW * 32 * 68];
     epilogue<KIND, BROWS, true>(g, acc, sEp, w, lane, m0, n0, wm, wn);
   }
 }
