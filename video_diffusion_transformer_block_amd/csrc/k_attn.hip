@@ -6,8 +6,13 @@
 //
 // bf16 path (hd = 128), flash style with an online softmax:
 //  * a 512-thread workgroup owns 256 queries of one (batch, head): eight
-//    wavefronts of 32 queries, two per SIMD, so one wavefront's softmax
-//    (VALU) overlaps the other's matrix instructions;
+//    wavefronts of 32 queries, two per SIMD;
+//  * each wavefront interleaves its own matrix and vector work: the
+//    exponentials of a tile are split in two halves, one laid between the
+//    next tile's score MFMAs and one between the previous tile's PV MFMAs,
+//    with LDS fragments read three MFMAs ahead (left to the compiler's
+//    scheduler, the score MFMAs ran back to back on one-ahead reads and the
+//    exponentials after them: 2% slower in the block);
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    a lane then holds 16 keys of ONE query, so the row max / row sum are
 //    per-lane reductions plus one exchange between lanes l and l^32;
@@ -38,12 +43,11 @@
 
 namespace wan {
 
-#ifndef WAN_ATTN_QB
-#define WAN_ATTN_QB 1
-#endif
-constexpr int AQ = 256;   // queries per workgroup
+constexpr int AQ = 256;   // queries per workgroup: 8 wavefronts of 32
 constexpr int AK = 64;    // keys per tile
 constexpr int HD = 128;   // head dim
+constexpr int KBW = 2;    // 1-KB blocks of a K (or V^T) tile each of the 8 wavefronts loads
+constexpr int NA = 3;     // LDS fragment reads in flight ahead of their MFMA
 constexpr float PMAX = 65536.0f;   // 2^16: probabilities above it raise the running max
 
 WAN_DEV float other_half(float v) { return __shfl_xor(v, 32); }
@@ -56,18 +60,10 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 WAN_DEV int ksig(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 WAN_DEV int vswz(int row) { return (row >> 1) & 7; }   // 16-byte chunk XOR for 128-byte rows
 
-// QB = 32-query blocks per wavefront (1 or 2).  A workgroup always owns AQ =
-// 256 queries: 8 / QB wavefronts.  With QB = 2 each K / V^T fragment read from
-// LDS feeds two MFMAs (half the LDS traffic per MFMA) and a wavefront has a
-// SIMD to itself (512 registers; the accumulators of O fit in AGPRs).
-constexpr int QB = WAN_ATTN_QB;
-static_assert(QB == 1 || QB == 2, "one or two 32-query blocks per wavefront");
 // QS: q arrives multiplied by scale * log2(e) (a score is then already in
 // log2 units); otherwise every score is multiplied by it before the exp2.
 template <bool QS>
-__global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
-  constexpr int NW = 8 / QB;          // wavefronts per workgroup
-  constexpr int KBW = 16 / NW;        // 1-KB blocks of a K (or V^T) tile each wavefront loads
+__global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnDesc a) {
   // One LDS variable per stage: the compiler gives each its own alias scope,
   // so LDS reads of one stage need not wait for loads still landing in the
   // other (it cannot tell two halves of one array apart).  The steady-state
@@ -104,41 +100,33 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
   const bf16 *Kg = reinterpret_cast<const bf16 *>(a.k);
   const bf16 *Vg = reinterpret_cast<const bf16 *>(a.vt);
 
-  // ---- Q fragments (B operand of S^T = K Q^T): for query block qb the lane
-  // holds Q[q][st*16 + g*8 .. +8] of query q = qrow[qb]
+  // ---- Q fragments (B operand of S^T = K Q^T): the lane holds
+  // Q[q][st*16 + g*8 .. +8] of its query q = qrow
   // log2 units per score unit: 1 for a pre-scaled q, else scale * log2(e)
   const float c = QS ? 1.0f : a.scale * 1.4426950408889634f;
-  int qrow[QB];
-  bf16x8 qf[QB][8];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    qrow[qb] = qt * AQ + (w * QB + qb) * 32 + l32;
-    const bool ok = qrow[qb] < Lq;
-    const bf16 *qp = Qg + (long)(b * Lq + (ok ? qrow[qb] : 0)) * a.ldq + h * HD + g * 8;
+  const int qrow = qt * AQ + w * 32 + l32;
+  bf16x8 qf[8];
+  {
+    const bool ok = qrow < Lq;
+    const bf16 *qp = Qg + (long)(b * Lq + (ok ? qrow : 0)) * a.ldq + h * HD + g * 8;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       uint4 v = ok ? ld16(qp + st * 16) : make_uint4(0, 0, 0, 0);
-      qf[qb][st] = *reinterpret_cast<bf16x8 *>(&v);
+      qf[st] = *reinterpret_cast<bf16x8 *>(&v);
     }
   }
 
-  f32x16 o[4][QB];
+  f32x16 o[4];   // O^T: head-dim rows t*32 .. +31 x the wavefront's 32 queries
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  // nm: -m in all 16 entries (the score MFMAs' initial accumulator); m is the
+  // running max in score units (log2 units when QS)
+  f32x16 nm;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[t][qb][r] = 0.f;
-  // nm[qb]: -m in all 16 entries (the score MFMAs' initial accumulator); m
-  // is the running max in score units (log2 units when QS)
-  f32x16 nm[QB];
-  float l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    l[qb] = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nm[qb][r] = 0.f;
-  }
+  for (int r = 0; r < 16; ++r) nm[r] = 0.f;
+  float l = 0.f;
 
   // ---- tile loaders: K tile = 64 keys x 16 chunks; V^T tile = 128 rows x 8 chunks
   const long vbase = (long)b * a.vt_bstride;
@@ -194,169 +182,116 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
   int voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) voff[j] = l32 * AK + (((2 * j + g) ^ vswz(l32)) * 8);
+  // LDS fragments: MFMA i = 2 st + kb of a score section (the two 32-key
+  // chains alternate), MFMA i = (2 kb + hf) * 4 + t of a PV section
+  auto kfr = [&](const bf16 *sk, int i) {
+    return *reinterpret_cast<const bf16x8 *>(sk + (i & 1) * 32 * HD + koff[i >> 1]);
+  };
+  auto vfr = [&](const bf16 *sv, int i) {
+    return *reinterpret_cast<const bf16x8 *>(sv + (i & 3) * 32 * AK + voff[i >> 2]);
+  };
 
   const int ntiles = (Lk + AK - 1) / AK;
 
-  // S^T - m of a tile (two 32-key blocks x QB query blocks); each K
-  // fragment feeds the QB query blocks
-  constexpr int NPRE = 2;   // fragments read ahead of a section's other work
-  auto kfrag = [&](const bf16 *sk, int i) {   // i-th K fragment of a score section (kb = i / 8, st = i % 8)
-    return *reinterpret_cast<const bf16x8 *>(sk + (i / 8) * 32 * HD + koff[i % 8]);
-  };
-  auto qk_pre = [&](const bf16 *sk, f32x16 (&s)[2][QB], const bf16x8 (&pre)[NPRE]) {
+  // S^T - m of a tile (the first tile; the steady state interleaves these MFMAs)
+  auto qk = [&](const bf16 *sk, f32x16 (&s)[2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int i = kb * 8 + st;
-        bf16x8 ka = i < NPRE ? pre[i < NPRE ? i : 0] : kfrag(sk, i);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][st], st ? s[kb][qb] : nm[qb],
-                                                              0, 0, 0);
-      }
-    }
-  };
-  auto qk = [&](const bf16 *sk, f32x16 (&s)[2][QB]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sk + kb * 32 * HD + koff[st]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][st], st ? s[kb][qb] : nm[qb],
-                                                              0, 0, 0);
-      }
-    }
+    for (int i = 0; i < 16; ++i)
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr(sk, i), qf[i >> 1], i >> 1 ? s[i & 1] : nm,
+                                                         0, 0, 0);
   };
   // keys past Lk -> -inf (last tile only)
-  auto mask_tail = [&](f32x16 (&s)[2][QB], int j) {
+  auto mask_tail = [&](f32x16 (&s)[2], int j) {
     if ((j + 1) * AK > Lk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j * AK + kb * 32 + 16 * (r >> 3) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            if (key >= Lk) s[kb][qb][r] = -INFINITY;
+          if (key >= Lk) s[kb][r] = -INFINITY;
         }
     }
   };
-  // row max of a score tile per query block, merged across the two lane halves
-  auto rowmax = [&](const f32x16 (&s)[2][QB], float (&mx)[QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float v = s[0][qb][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v = fmaxf(v, s[kb][qb][r]);
-      mx[qb] = fmaxf(v, other_half(v));
-    }
-  };
-  // probabilities of a tile, exp2 of the centred scores, bf16 in the
-  // B-operand layout, and this lane's part of their row sums (a row sum adds
-  // the bf16-rounded probabilities, two per v_dot2 with (1, 1): the
-  // normaliser then matches exactly the weights the PV MFMA uses)
-  auto probs = [&](const f32x16 (&s)[2][QB], bf16x8 (&pb)[QB][2][2], float (&ls)[QB]) {
-    bf16x2 one;
-    one[0] = (bf16)1.0f; one[1] = (bf16)1.0f;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pb[qb][kb][hf][e] = f2bf(__builtin_amdgcn_exp2f(QS ? s[kb][qb][hf * 8 + e]
-                                                               : s[kb][qb][hf * 8 + e] * c));
-          const bf16x2 *pp = reinterpret_cast<const bf16x2 *>(&pb[qb][kb][hf]);
-          ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[0], one, ls0, false);
-          ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[1], one, ls1, false);
-          ls0 = __builtin_amdgcn_fdot2_f32_bf16(pp[2], one, ls0, false);
-          ls1 = __builtin_amdgcn_fdot2_f32_bf16(pp[3], one, ls1, false);
-        }
-      ls[qb] = ls0 + ls1;
-    }
-  };
-  // lower every centred score of s by dm (per query block)
-  auto shift = [&](f32x16 (&s)[2][QB], const float (&dm)[QB]) {
+  // row max of a score tile, merged across the two lane halves
+  auto rowmax = [&](const f32x16 (&s)[2]) {
+    float v = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int r = 0; r < 16; ++r) v = fmaxf(v, s[kb][r]);
+    return fmaxf(v, other_half(v));
+  };
+  // One unit of a tile's probabilities: registers 2u, 2u+1 (u = 0..7) of a
+  // 32-key block's centred scores sk -> exp2 -> bf16 pair u % 4 of pbk[u / 4]
+  // (the B-operand layout of the PV MFMA), added to row-sum chain u % 2.  A
+  // row sum adds the bf16-rounded probabilities, two per v_dot2 with (1, 1):
+  // the normaliser then matches exactly the weights the PV MFMA uses.
+  bf16x2 one2;
+  one2[0] = (bf16)1.0f; one2[1] = (bf16)1.0f;
+  auto punit = [&](const f32x16 &sk, int u, bf16x8 (&pbk)[2], float (&lsc)[2]) {
+    const int hf = u >> 2, pp = u & 3;
+    const float e0 = __builtin_amdgcn_exp2f(QS ? sk[2 * u] : sk[2 * u] * c);
+    const float e1 = __builtin_amdgcn_exp2f(QS ? sk[2 * u + 1] : sk[2 * u + 1] * c);
+    pbk[hf][2 * pp] = f2bf(e0);
+    pbk[hf][2 * pp + 1] = f2bf(e1);
+    bf16x2 pr;
+    pr[0] = pbk[hf][2 * pp]; pr[1] = pbk[hf][2 * pp + 1];
+    lsc[pp & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsc[pp & 1], false);
+  };
+  // all probabilities of a tile and their row sum (the same units in the same order)
+  auto probs = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float &ls) {
+    float lsc[2] = {0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] -= dm[qb];
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) punit(s[kb], u, pb[kb], lsc);
+    ls = lsc[0] + lsc[1];
+  };
+  // lower every centred score of s by dm
+  auto shift = [&](f32x16 (&s)[2], float dm) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] -= dm;
   };
   // a probability of this tile passed PMAX (or is not finite): raise the
   // running max to the tile's max, rescale the accumulators, recompute the
   // tile's probabilities; snxt (already scored against the old max) follows
-  auto overflow = [&](f32x16 (&scur)[2][QB], f32x16 (&snxt)[2][QB], bool has_next,
-                      bf16x8 (&pb)[QB][2][2], float (&ls)[QB]) {
-    bool big = false;
+  auto overflow = [&](f32x16 (&scur)[2], f32x16 (&snxt)[2], bool has_next, bf16x8 (&pb)[2][2],
+                      float &ls) {
+    if (__builtin_amdgcn_ballot_w64(!(ls <= PMAX)) == 0) return;
+    const float dm = fmaxf(rowmax(scur), 0.f);
+    const float alpha = __builtin_amdgcn_exp2f(-dm * c);
+    l *= alpha;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) big |= !(ls[qb] <= PMAX);
-    if (__builtin_amdgcn_ballot_w64(big) == 0) return;
-    float mx[QB], dm[QB];
-    rowmax(scur, mx);
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      dm[qb] = fmaxf(mx[qb], 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-dm[qb] * c);
-      l[qb] *= alpha;
+      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][qb][r] *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) nm[qb][r] -= dm[qb];
-    }
+    for (int r = 0; r < 16; ++r) nm[r] -= dm;
     shift(scur, dm);
     if (has_next) shift(snxt, dm);
     probs(scur, pb, ls);
   };
-  // O^T += V^T P^T; each V^T fragment feeds the QB query blocks
-  auto vfrag = [&](const bf16 *sv, int i) {   // i-th V^T fragment of a PV section (kb, hf = i / 4, t = i % 4)
-    return *reinterpret_cast<const bf16x8 *>(sv + (i % 4) * 32 * AK + voff[i / 4]);
-  };
-  auto pv_pre = [&](const bf16 *sv, const bf16x8 (&pb)[QB][2][2], const bf16x8 (&pre)[NPRE]) {
+  // O^T += V^T P^T (the last tile; the steady state interleaves these MFMAs)
+  auto pv = [&](const bf16 *sv, const bf16x8 (&pb)[2][2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int i = (2 * kb + hf) * 4 + t;
-          bf16x8 va = i < NPRE ? pre[i < NPRE ? i : 0] : vfrag(sv, i);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            o[t][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][kb][hf], o[t][qb], 0, 0, 0);
-        }
-  };
-  auto pv = [&](const bf16 *sv, const bf16x8 (&pb)[QB][2][2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          bf16x8 va = *reinterpret_cast<const bf16x8 *>(sv + t * 32 * AK + voff[2 * kb + hf]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            o[t][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][kb][hf], o[t][qb], 0, 0, 0);
-        }
+    for (int i = 0; i < 16; ++i)
+      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr(sv, i), pb[i >> 3][(i >> 2) & 1], o[i & 3],
+                                                         0, 0, 0);
   };
 
   // Pipeline: K runs one tile ahead of V.  At the top of iteration j the LDS
   // holds K(j+1) in stage (j+1)&1 and V(j) in stage j&1; the centred scores
-  // S(j) are in registers.  Iteration j: K(j+2) and V(j+1) start loading into
-  // the stages freed in iteration j-1; the S(j+1) MFMAs interleaved with the
-  // exponentials of tile j; (rare) overflow: raise the max; the PV(j) MFMAs;
-  // wait for the loads; one barrier.
+  // S(j) are in registers, and so are the probabilities of S(j)'s first
+  // 32-key block.  Iteration j: K(j+2) and V(j+1) start loading into the
+  // stages freed in iteration j-1; section 1: the 16 S(j+1) MFMAs, every
+  // second one followed by one unit of S(j)'s second block; (rare) overflow:
+  // raise the max; section 2: the 16 PV(j) MFMAs, every second one followed
+  // by one unit of S(j+1)'s first block; wait for the loads; one barrier.
+  // Each MFMA's fragment is read NA MFMAs ahead, and a scheduling barrier
+  // after every MFMA keeps this order, so each wavefront keeps the matrix and
+  // the vector unit busy together.
   constexpr std::integral_constant<int, 0> P0{};
   constexpr std::integral_constant<int, 1> P1{};
   gloadK(0, P0);
@@ -364,128 +299,122 @@ __global__ __launch_bounds__(512 / QB, 1) void k_attn_bf16(AttnDesc a) {
   gloadV(0, P0);
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(0), K(1), V(0) landed
   __syncthreads();
-  f32x16 sa[2][QB], sb[2][QB];
+  f32x16 sa[2], sb[2];   // centred scores of the current / next tile
+  bf16x8 pa[2], pn[2];   // probabilities of the first block of the current / next tile
+  float la[2], ln[2];    // their row-sum chains
   {   // the first tile sets the running max exactly
-    float mx[QB];
     qk(sK0, sa);
     mask_tail(sa, 0);
-    rowmax(sa, mx);
+    const float mx = rowmax(sa);
     shift(sa, mx);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int r = 0; r < 16; ++r) nm[r] = -mx;
+    la[0] = la[1] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) nm[qb][r] = -mx[qb];
+    for (int u = 0; u < 8; ++u) punit(sa[0], u, pa, la);
   }
   __syncthreads();   // every wavefront has read K(0): its buffer may be refilled
 
-  // MFMAs per section, and the LDS reads / VALU instructions laid between them
-  constexpr int NMF = 16 * QB;
-  // one pipelined iteration; tile j+1 exists; P is the parity of j.
-  // (load_k2: tile j+2 exists; mask_next: tile j+1 is the last, possibly
-  // ragged, tile; both are constants in the steady-state loop, so no branch
-  // stays there.)
-  auto step = [&](auto P, int j, f32x16 (&scur)[2][QB], f32x16 (&snxt)[2][QB], bool load_k2,
-                  bool mask_next) {
+  // one pipelined iteration; tile j+1 exists; P is the parity of j; pc / lc:
+  // probabilities and row-sum chains of S(j)'s first block, pnx / lnx the
+  // same for S(j+1) (written here).  (load_k2: tile j+2 exists; mask_next:
+  // tile j+1 is the last, possibly ragged, tile; both are constants in the
+  // steady-state loop, so no branch stays there.)
+  auto step = [&](auto P, int j, f32x16 (&scur)[2], f32x16 (&snxt)[2], bf16x8 (&pc)[2], float (&lc)[2],
+                  bf16x8 (&pnx)[2], float (&lnx)[2], bool load_k2, bool mask_next) {
     const auto Q = other(P);
-    // the first K fragments of the score section are read before the tile
-    // loads are issued (their LDS latency then overlaps the load issue;
-    // 5.13 -> 5.07 ms at 12 x 32760)
-    bf16x8 kpre[NPRE];
+    const bf16 *sk = kbuf(Q);
+    const bf16 *sv = vbuf(P);
+    bf16x8 fr[NA + 1];
+    // the first fragments are read before the tile loads are issued (their
+    // LDS latency then overlaps the load issue)
 #pragma unroll
-    for (int i = 0; i < NPRE; ++i) kpre[i] = kfrag(kbuf(Q), i);
+    for (int i = 0; i < NA; ++i) fr[i] = kfr(sk, i);
     __builtin_amdgcn_sched_barrier(0);
     // both tile loads start at the top, so each has the whole iteration to
-    // land before the wait at its end (issuing V(j+1) after the score MFMAs
-    // instead left it half an iteration: 5.30 -> 5.17 ms at 12 x 32760)
+    // land before the wait at its end
     if (load_k2) gloadK(j + 2, P);   // buffer of K(j), read in iteration j-1
     gloadV(j + 1, Q);                // buffer of V(j-1), read in iteration j-1
-    bf16x8 pb[QB][2][2];
-    float ls[QB];
-    // matrix unit: next scores; vector unit: this tile's probabilities
-    qk_pre(kbuf(Q), snxt, kpre);
-    probs(scur, pb, ls);
-    // LDS reads run ahead of their use; VALU fills the MFMA shadow
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int q = 0; q < NMF; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      if (q % QB == 0 && q < NMF - 4 * QB)
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
-    }
-    // likewise the first V^T fragments of the PV section, before the running-max check
-    bf16x8 vpre[NPRE];
-#pragma unroll
-    for (int i = 0; i < NPRE; ++i) vpre[i] = vfrag(vbuf(P), i);
-    if (mask_next) mask_tail(snxt, j + 1);
-    overflow(scur, snxt, true, pb, ls);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l[qb] += ls[qb];
     __builtin_amdgcn_sched_barrier(0);
-    // matrix unit: PV of this tile
-    pv_pre(vbuf(P), pb, vpre);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    bf16x8 pt[2][2];                 // this tile's probabilities, the PV B operands
+    pt[0][0] = pc[0]; pt[0][1] = pc[1];
 #pragma unroll
-    for (int q = 0; q < NMF; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (q % QB == 0 && q < NMF - 4 * QB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < 16; ++i) {   // section 1
+      if (i + NA < 16) fr[(i + NA) % (NA + 1)] = kfr(sk, i + NA);
+      const int st = i >> 1, kb = i & 1;
+      snxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (NA + 1)], qf[st], st ? snxt[kb] : nm,
+                                                         0, 0, 0);
+      if (i & 1) punit(scur[1], i >> 1, pt[1], lc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (mask_next) mask_tail(snxt, j + 1);
+    float ls = lc[0] + lc[1];
+    overflow(scur, snxt, true, pt, ls);
+    l += ls;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) fr[i] = vfr(sv, i);
+    lnx[0] = lnx[1] = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {   // section 2
+      if (i + NA < 16) fr[(i + NA) % (NA + 1)] = vfr(sv, i + NA);
+      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (NA + 1)], pt[i >> 3][(i >> 2) & 1],
+                                                         o[i & 3], 0, 0, 0);
+      if (i & 1) punit(snxt[0], i >> 1, pnx, lnx);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): K(j+2), V(j+1) landed, LDS reads done
     __syncthreads();
   };
   // the last tile: no next scores
-  auto last = [&](auto P, f32x16 (&scur)[2][QB]) {
-    bf16x8 pb[QB][2][2];
-    float ls[QB];
-    probs(scur, pb, ls);
-    overflow(scur, scur, false, pb, ls);
+  auto last = [&](auto P, f32x16 (&scur)[2], bf16x8 (&pc)[2], float (&lc)[2]) {
+    bf16x8 pt[2][2];
+    pt[0][0] = pc[0]; pt[0][1] = pc[1];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l[qb] += ls[qb];
-    pv(vbuf(P), pb);
+    for (int u = 0; u < 8; ++u) punit(scur[1], u, pt[1], lc);
+    float ls = lc[0] + lc[1];
+    overflow(scur, scur, false, pt, ls);
+    l += ls;
+    pv(vbuf(P), pt);
   };
   int j = 0;
   for (; j + 3 < ntiles; j += 2) {     // unrolled by two (score buffers and stages alternate);
-    step(P0, j, sa, sb, true, false);            // never computes the last tile's scores
-    step(P1, j + 1, sb, sa, true, false);
+    step(P0, j, sa, sb, pa, la, pn, ln, true, false);       // never computes the last tile's scores
+    step(P1, j + 1, sb, sa, pn, ln, pa, la, true, false);
   }
   // the last 1 .. 3 tiles, one at a time with run-time stages; the current
   // scores are in sa
   for (; j + 1 < ntiles; ++j) {
-    step(j & 1, j, sa, sb, j + 2 < ntiles, j + 2 == ntiles);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sa[kb][qb] = sb[kb][qb];
+    step(j & 1, j, sa, sb, pa, la, pn, ln, j + 2 < ntiles, j + 2 == ntiles);
+    sa[0] = sb[0]; sa[1] = sb[1];
+    pa[0] = pn[0]; pa[1] = pn[1];
+    la[0] = ln[0]; la[1] = ln[1];
   }
-  last(j & 1, sa);
+  last(j & 1, sa, pa, la);
 
-  // ---- normalise and store: lane holds O^T[hd = t*32 + (r/4)*8 + g*4 + r%4][q = qrow[qb]]
+  // ---- normalise and store: lane holds O^T[hd = t*32 + (r/4)*8 + g*4 + r%4][q = qrow]
+  const float inv = 1.0f / (l + other_half(l));
+  if (qrow >= Lq) return;
+  const long orow = (long)(b * Lq + qrow);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float inv = 1.0f / (l[qb] + other_half(l[qb]));
-    if (qrow[qb] >= Lq) continue;
-    const long orow = (long)(b * Lq + qrow[qb]);
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int hd0 = t * 32 + rb * 8 + g * 4;
-        float v0 = o[t][qb][rb * 4 + 0] * inv, v1 = o[t][qb][rb * 4 + 1] * inv;
-        float v2 = o[t][qb][rb * 4 + 2] * inv, v3 = o[t][qb][rb * 4 + 3] * inv;
-        if (a.out_mode == 1) {
-          *reinterpret_cast<float4 *>(a.acc32 + orow * (a.H * HD) + h * HD + hd0) =
-              make_float4(v0, v1, v2, v3);
-          continue;
-        }
-        if (a.out_mode == 2) {
-          float4 p = *reinterpret_cast<const float4 *>(a.acc32 + orow * (a.H * HD) + h * HD + hd0);
-          v0 += p.x; v1 += p.y; v2 += p.z; v3 += p.w;
-        }
-        bf16x4 ov;
-        ov[0] = f2bf(v0); ov[1] = f2bf(v1); ov[2] = f2bf(v2); ov[3] = f2bf(v3);
-        *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(a.o) + orow * a.ldo + h * HD + hd0) = ov;
+    for (int rb = 0; rb < 4; ++rb) {
+      const int hd0 = t * 32 + rb * 8 + g * 4;
+      float v0 = o[t][rb * 4 + 0] * inv, v1 = o[t][rb * 4 + 1] * inv;
+      float v2 = o[t][rb * 4 + 2] * inv, v3 = o[t][rb * 4 + 3] * inv;
+      if (a.out_mode == 1) {
+        *reinterpret_cast<float4 *>(a.acc32 + orow * (a.H * HD) + h * HD + hd0) = make_float4(v0, v1, v2, v3);
+        continue;
       }
-  }
+      if (a.out_mode == 2) {
+        float4 p = *reinterpret_cast<const float4 *>(a.acc32 + orow * (a.H * HD) + h * HD + hd0);
+        v0 += p.x; v1 += p.y; v2 += p.z; v3 += p.w;
+      }
+      bf16x4 ov;
+      ov[0] = f2bf(v0); ov[1] = f2bf(v1); ov[2] = f2bf(v2); ov[3] = f2bf(v3);
+      *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(a.o) + orow * a.ldo + h * HD + hd0) = ov;
+    }
 }
 
 // float32 path: one wavefront per (batch, head, query); lanes stride over the
@@ -553,8 +482,8 @@ hipError_t launch_attention(const AttnDesc &a, hipStream_t s) {
   if ((long)a.H * a.hd * a.ldv * 2 >= (1L << 31)) return hipErrorInvalidValue;
   if (a.vt_bstride < (a.Lk + AK - 1) / AK * AK) return hipErrorInvalidValue;
   const int nqt = (a.Lq + AQ - 1) / AQ;
-  if (a.q_scaled) k_attn_bf16<true><<<a.B * a.H * nqt, 512 / QB, 0, s>>>(a);
-  else k_attn_bf16<false><<<a.B * a.H * nqt, 512 / QB, 0, s>>>(a);
+  if (a.q_scaled) k_attn_bf16<true><<<a.B * a.H * nqt, 512, 0, s>>>(a);
+  else k_attn_bf16<false><<<a.B * a.H * nqt, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
