@@ -25,6 +25,8 @@
 
 namespace wan {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int GBM = 256, GBN = 256;
 constexpr int GBK = 64, NSTAGE = 2;     // K tile 64 (four MFMA k-substeps), two LDS stages
 constexpr int GW = 8;            // wavefronts per workgroup (two per SIMD)
@@ -120,7 +122,10 @@ WAN_DEV void epilogue(const GemmDesc &g, const f32x16 (&acc)[4][2], float *lds, 
           bf16x8 o;
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = f2bf(v[k]);
-          *reinterpret_cast<bf16x8 *>(c) = o;
+          // non-temporal: the output stream does not allocate in L2 over the
+          // operand tiles (block step 8.11 -> 8.04 ms; the same hint on the
+          // float32 stream measured no gain)
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(&o), reinterpret_cast<u32x4 *>(c));
         } else {
           for (int k = 0; k < 8 && n + k < lim; ++k) c[k] = n + k < g.N ? f2bf(v[k]) : f2bf(0.f);
         }
