@@ -37,8 +37,8 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 # Valid only for the kernel sources they were taken on: reported as null
 # once k_attn.hip, common.hpp or attn.hpp change.
 ATTN_TRAFFIC = {
-    "sources_sha256": "0ec154d451aec92bfc68731f59c4d68d44afbcefaa9f670444f7c6a18100c91e",
-    "fetch_kib": 442447, "write_kib": 100231, "fetch_scale": 2.00, "write_scale": 1.00,
+    "sources_sha256": "97fe764837f7bdc2d94a0e36b80849e69831605cb63adc228379ddbb1d900a47",
+    "fetch_kib": 453210, "write_kib": 120571, "fetch_scale": 2.00, "write_scale": 1.00,
 }
 
 
