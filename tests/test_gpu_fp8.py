@@ -142,6 +142,12 @@ FP8_BLOCKS = {
                                  lat_f=3, lat_h=20, lat_w=40, batch=2, text_len=40, kind="block"),
     "bf16-i2v": synth.mini(12, "bf16-i2v", dim=256, heads=2, ffn=512, n_blocks=1, lat_f=2,
                            lat_h=16, lat_w=24, batch=1, text_len=64, img_len=257, kind="block"),
+    # short samples: a GEMM wavefront's 128 rows span all three (L = 25), so the
+    # gated-residual epilogue takes each row's own gate.  (The five-sample L = 6
+    # case runs in the bf16 block test only: over its 30 rows the max-abs
+    # comparison with the FP8 effect is decided by single E4M3 code steps.)
+    "bf16-b3-short": synth.mini(13, "bf16-b3-short", dim=256, heads=2, ffn=512, n_blocks=1,
+                                lat_f=1, lat_h=10, lat_w=10, batch=3, text_len=40, kind="block"),
 }
 
 
@@ -151,6 +157,8 @@ def _run_block_fp8(work, rows=None):
     m = work.model
     cfg = cfg_of(work)
     inp = synth.workload_inputs(work)
+    if work.batch > 2:   # distinct timesteps, so every sample has gates of its own
+        inp["t"] = np.linspace(60.0, 940.0, work.batch).astype(np.float32)
     tw = synth.tmlp_weights(work)
     bw = synth.block_weights(work, 0)
     img = None
