@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
+PEAK_SCLK_MHZ = 2400.0        # the shader clock the published peaks are quoted at
 
 # HBM bytes per self-attention launch of this workload, from two rocprofv3
 # --pmc passes over `bench.py --traffic-pass` (FETCH_SIZE, then WRITE_SIZE,
@@ -59,6 +60,54 @@ def attn_traffic_bytes():
     if attn_sources_sha256() != t["sources_sha256"]:
         return None
     return int(round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])))
+
+
+class ClockSampler:
+    """Samples the GPU shader clock while a timed region runs: a host thread
+    reads the driver's current-level line (the one marked '*') of
+    /sys/class/drm/card*/device/pp_dpm_sclk every `period` seconds.  Used as a
+    context manager; `mhz()` is the mean over the samples, or None when the
+    file is not there."""
+
+    def __init__(self, period: float = 0.002):
+        import glob
+        import threading
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = cards[0] if len(cards) == 1 else None
+        self.period, self.samples = period, []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True) if self.path else None
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._thread:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def mhz(self):
+        return sum(self.samples) / len(self.samples) if self.samples else None
 
 
 def block_flops(B, L, d, H, F, Lc, Li=0):
@@ -614,15 +663,16 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    t_wall = time.perf_counter()
-    for i in range(args.steps):
-        W.set_attention_events(*sa_ev[i])
-        step()
-    e1.record(stream)
-    W.set_attention_events(None, None)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
+    with ClockSampler() as clock:
+        e0.record(stream)
+        t_wall = time.perf_counter()
+        for i in range(args.steps):
+            W.set_attention_events(*sa_ev[i])
+            step()
+        e1.record(stream)
+        W.set_attention_events(None, None)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
     sa_ms = [a.elapsed_time(b) for a, b in sa_ev]
     attn_block_ms = sum(sa_ms) / len(sa_ms)
@@ -693,7 +743,14 @@ def main():
                      "launches": len(sa_ms),
                      "standalone_launch_ms": round(attn_ms, 4),
                      "standalone_tflops": round(attn_solo_tf, 1),
-                     "flop_per_launch": sa_f},
+                     "flop_per_launch": sa_f,
+                     # the same against the peak at the shader clock sampled during the timed steps
+                     "sclk_mhz": None if clock.mhz() is None else round(clock.mhz(), 1),
+                     "sclk_samples": len(clock.samples),
+                     "peak_at_sclk": None if clock.mhz() is None
+                     else round(PEAK_BF16_TFLOPS * clock.mhz() / PEAK_SCLK_MHZ, 1),
+                     "frac_at_sclk": None if clock.mhz() is None
+                     else round(attn_tf / (PEAK_BF16_TFLOPS * clock.mhz() / PEAK_SCLK_MHZ), 4)},
         "wall_s_timed": round(t_wall, 3),
     }
     if m.dtype == "bf16":   # the same block with its six Linear layers in FP8 (E4M3), same inputs

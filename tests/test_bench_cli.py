@@ -16,3 +16,21 @@ def test_more_than_one_gpu_is_refused(n):
     assert r.returncode == 2, (r.returncode, r.stderr[-500:])
     assert "one GPU only" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_clock_sampler_reads_the_current_level(tmp_path):
+    """The shader-clock sampler takes the default line marked '*' (the current
+    level, whether a listed DPM level or the 'S:' line) and averages samples."""
+    sys.path.insert(0, ROOT)
+    import bench
+    for text, mhz in [("S: 2104Mhz *\n0: 500Mhz\n1: 2400Mhz\n", 2104.0),
+                      ("0: 500Mhz\n1: 2400Mhz *\n", 2400.0),
+                      ("0: 500Mhz\n1: 2400Mhz\n", None)]:
+        f = tmp_path / "pp_dpm_sclk"
+        f.write_text(text)
+        c = bench.ClockSampler()
+        c.path = str(f)
+        assert c._read() == mhz
+    c = bench.ClockSampler()
+    c.path, c.samples = None, [2000.0, 2100.0]
+    assert c.mhz() == 2050.0
