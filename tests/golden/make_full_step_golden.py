@@ -14,10 +14,15 @@ Workloads:
     whose first frame is given), 257 image tokens through the image MLP
     ([Note, I2V 架构扩展]; [News, 核心创新四]).
 
-Usage (hours of CPU time at float64; each workload is independent):
+  * ``wan14b-i2v-step-short``: the same 14B image-to-video step on a short
+    clip (latent 21 x 8 x 8, L = 336 tokens), full width and depth.
+
+Usage (hours of CPU time at float64 for 3 and 5, minutes for 53; each
+workload is independent):
 
     python -m tests.golden.make_full_step_golden --config 3
     python -m tests.golden.make_full_step_golden --config 5
+    python -m tests.golden.make_full_step_golden --config 53
 """
 from __future__ import annotations
 
@@ -36,8 +41,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 N_SAMPLED = 4096          # output elements stored per batch sample
 
 
+# the 14B image-to-video model at its full width and depth on a short clip
+# (latent 21 x 8 x 8, L = 336 tokens): small enough for the oracle to take
+# minutes, so the step can also be compared in float32
+SHORT_I2V = synth.mini(53, "wan14b-i2v-step-short", dim=5120, heads=40, ffn=13824, n_blocks=40,
+                       lat_f=21, lat_h=8, lat_w=8, batch=1, text_len=512, in_ch=36, img_len=257)
+WORKLOADS = {3: synth.CONFIGS[3], 5: synth.CONFIGS[5], 53: SHORT_I2V}
+
+
 def golden_path(cid: int) -> str:
-    return os.path.join(HERE, f"step_{synth.CONFIGS[cid].name}.json")
+    return os.path.join(HERE, f"step_{WORKLOADS[cid].name}.json")
 
 
 def step_inputs(cid: int):
@@ -45,7 +58,7 @@ def step_inputs(cid: int):
     step workload, exactly as the GPU test builds them.  The I2V mask
     channels are the expansion of a binary mask over the 81 video frames with
     only frame 0 given."""
-    w = synth.CONFIGS[cid]
+    w = WORKLOADS[cid]
     inp = synth.workload_inputs(w)
     lat = inp["latent"]
     if w.model.in_ch > 16:
@@ -66,11 +79,11 @@ def sample_index(cid: int, shape):
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("--config", type=int, choices=(3, 5), required=True)
+    ap.add_argument("--config", type=int, choices=tuple(WORKLOADS), required=True)
     ap.add_argument("--head-threads", type=int, default=os.cpu_count() or 1)
     a = ap.parse_args(argv)
     cid = a.config
-    w = synth.CONFIGS[cid]
+    w = WORKLOADS[cid]
     m = w.model
     O.HEAD_THREADS = a.head_threads
     t0 = time.perf_counter()
