@@ -18,8 +18,8 @@
 // groups of 8 M-tiles so that the 32 workgroups an XCD runs at once share A
 // and B slices in that XCD's L2.  The MFMAs compute the tile transposed
 // (operands swapped), so each lane holds runs of 4 consecutive columns of one
-// output row: float32 outputs are written straight from the accumulators,
-// bf16 outputs are staged through LDS.
+// output row; both epilogues stage a wavefront's slab through LDS and store
+// whole row segments.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -413,8 +413,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
 // in the same k order, which is all the dot product needs.  Per tile: the
 // loads of tile kt+2 start, the 8 MFMAs of tile kt run from registers, one
 // barrier, then the fragments of tile kt+1 are read into the same registers
-// while those MFMAs execute.  The epilogue (registers or LDS, as for bf16
-// operands) scales by the row scale times the column scale.
+// while those MFMAs execute.  The epilogues (LDS-staged, as for bf16
+// operands) scale by the row scale times the column scale.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 template <int KIND, bool BROWS>
