@@ -23,3 +23,14 @@ def full_inputs(H, L, threads=16):
     for a, b in outlier_ranges(L):
         k[a:b] = synth.bf16_round(k[a:b] * np.float32(2.5))
     return q, k, v
+
+
+def cross_inputs(H, Lq, Lk, threads=16):
+    """Cross-attention stress inputs at the block's real shapes: queries of the
+    full token sequence (q ~ N(0, 4)) against Lk context keys (k ~ N(0, 4),
+    v ~ N(0, 1)), with the same raised key runs scaled to the short context."""
+    q, _, _ = synth.attention_inputs_full(7, H, Lq, qk_std=2.0, threads=threads)
+    _, k, v = synth.attention_inputs_full(8, H, Lk, qk_std=2.0, threads=threads)
+    for a, b in [(3, 11), (Lk // 2, Lk // 2 + 8), (Lk - 9, Lk - 1)]:
+        k[a:b] = synth.bf16_round(k[a:b] * np.float32(2.5))
+    return q, k, v

@@ -16,7 +16,7 @@ import pytest
 
 import oracle.wan_oracle as O
 import synth
-from tests.attn_full_inputs import full_inputs, sampled_rows
+from tests.attn_full_inputs import cross_inputs, full_inputs, sampled_rows
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -26,20 +26,22 @@ FULL = [(12, 32760), (40, 75600)]
 
 
 def run_gpu(q, k, v, H, q_scaled):
-    """wan_attention_fwd on one sample: q, k [L, H*128]; V^T zero-padded to
-    whole 64-key tiles (the layout the block's projections write)."""
+    """wan_attention_fwd on one sample: q [Lq, H*128], k [Lk, H*128]; V^T
+    zero-padded to whole 64-key tiles (the layout the block's projections
+    write)."""
     import video_diffusion_transformer_block_amd as W
-    L, D = q.shape
-    Lp = (L + 63) // 64 * 64
+    Lq, D = q.shape
+    Lk = k.shape[0]
+    Lp = (Lk + 63) // 64 * 64
     tq = torch.from_numpy(q).to(torch.bfloat16).cuda()
     tk = torch.from_numpy(k).to(torch.bfloat16).cuda()
     tv = torch.zeros((D, Lp), dtype=torch.bfloat16, device="cuda")
     if v is None:
-        tv[:, :L] = 1.0
+        tv[:, :Lk] = 1.0
     else:
-        tv[:, :L] = torch.from_numpy(v).to(torch.bfloat16).cuda().t()
-    to = torch.empty((L, D), dtype=torch.bfloat16, device="cuda")
-    W.attention_fwd(tq, D, tk, D, tv, Lp, Lp, to, D, 1, H, L, L, q_scaled=q_scaled)
+        tv[:, :Lk] = torch.from_numpy(v).to(torch.bfloat16).cuda().t()
+    to = torch.empty((Lq, D), dtype=torch.bfloat16, device="cuda")
+    W.attention_fwd(tq, D, tk, D, tv, Lp, Lp, to, D, 1, H, Lq, Lk, q_scaled=q_scaled)
     torch.cuda.synchronize()
     return to
 
@@ -75,4 +77,28 @@ def test_attention_full_length_rows_sum_to_one(H, L):
     q = synth.bf16_round(q * np.float32(C_LOG2))
     g = run_gpu(q, k, None, H, True)
     err = float((g.float() - 1.0).abs().max())
+    assert err <= 4e-3, err
+
+
+# the cross-attention shapes of the blocks: the 1.3B and 14B text attention
+# (512 keys) and the 14B image-to-video image attention (257 keys, a ragged
+# last tile); [Note] Diffusion Transformer (text cross-attention), I2V 架构扩展
+CROSS = [(12, 32760, 512), (40, 75600, 512), (40, 32760, 257)]
+
+
+@pytest.mark.parametrize("H,Lq,Lk", CROSS)
+def test_cross_attention_full_size_sampled_rows(H, Lq, Lk):
+    """Peaked logits and raised key runs against a short context, the
+    pre-scaled queries the block's projections write: sampled query rows
+    against the oracle, and V = 1 -> O = 1 on every row."""
+    from tests.gpu_util import assert_parity
+    print(f"cross-attention H={H} Lq={Lq} Lk={Lk}", flush=True)
+    q, k, v = cross_inputs(H, Lq, Lk)
+    rows = sampled_rows(Lq)
+    q = synth.bf16_round(q * np.float32(C_LOG2))
+    g = run_gpu(q, k, v, H, True)[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    o = O.multihead(q[rows].astype(np.float64) / C_LOG2, k, v, H)
+    m = assert_parity(g, o, 3e-2, 1e-2, f"cross-attention H={H} Lq={Lq} Lk={Lk} ({len(rows)} rows)")
+    print(f"  {len(rows)} rows: {m}", flush=True)
+    err = float((run_gpu(q, k, None, H, True).float() - 1.0).abs().max())
     assert err <= 4e-3, err

@@ -40,3 +40,18 @@ def test_full_length_inputs_reject_mean_of_v_and_unscaled_softmax():
     bad = O.multihead(q[rows] * np.sqrt(128.0), k, v, H)
     m = metrics(bad, ref)
     assert m["max_abs"] > 3e-2 and m["mean_rel"] > 1e-2, m
+
+
+def test_cross_inputs_reject_mean_of_v_and_unscaled_softmax():
+    """The cross-attention stress inputs (512 text keys, 257 image keys; the
+    rows are independent, so 256 query rows show it): the plain mean of V and
+    a softmax without the 1/sqrt(hd) scale both fail the GPU tests' bar."""
+    from tests.attn_full_inputs import cross_inputs
+    for H, Lk in [(12, 512), (40, 257)]:
+        q, k, v = cross_inputs(H, 256, Lk, threads=8)
+        ref = O.multihead(q, k, v, H)
+        mean_v = np.broadcast_to(v.astype(np.float64).mean(axis=0, keepdims=True), ref.shape)
+        m = metrics(mean_v, ref)
+        assert m["max_abs"] > 3e-2 and m["mean_rel"] > 1e-2, m
+        m = metrics(O.multihead(q * np.sqrt(128.0), k, v, H), ref)
+        assert m["max_abs"] > 3e-2 and m["mean_rel"] > 1e-2, m
