@@ -49,8 +49,8 @@ SHORT_I2V = synth.mini(53, "wan14b-i2v-step-short", dim=5120, heads=40, ffn=1382
 WORKLOADS = {3: synth.CONFIGS[3], 5: synth.CONFIGS[5], 53: SHORT_I2V}
 
 
-def golden_path(cid: int) -> str:
-    return os.path.join(HERE, f"step_{WORKLOADS[cid].name}.json")
+def golden_path(cid: int, fp8: bool = False) -> str:
+    return os.path.join(HERE, f"step_{WORKLOADS[cid].name}{'-fp8' if fp8 else ''}.json")
 
 
 def step_inputs(cid: int):
@@ -81,6 +81,8 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, choices=tuple(WORKLOADS), required=True)
     ap.add_argument("--head-threads", type=int, default=os.cpu_count() or 1)
+    ap.add_argument("--fp8", action="store_true",
+                    help="every block's six Linear layers in FP8 (E4M3, the oracle's emulation)")
     a = ap.parse_args(argv)
     cid = a.config
     w = WORKLOADS[cid]
@@ -99,7 +101,7 @@ def main(argv=None):
                   f"({time.perf_counter() - tb:.0f}s, {time.perf_counter() - t0:.0f}s total)",
                   flush=True)
 
-    out = O.step(lat, t, ctx, mw, m.heads, eps=m.eps, clip=clip, blocks=blocks())
+    out = O.step(lat, t, ctx, mw, m.heads, eps=m.eps, clip=clip, blocks=blocks(), fp8=a.fp8)
     idx = sample_index(cid, out.shape)
     per = out.shape[1:]
     samples = []
@@ -112,17 +114,18 @@ def main(argv=None):
             "abs_max_all": float(np.max(np.abs(flat))),
         })
     rec = {
-        "what": f"velocity of the {w.name} denoising step, sampled elements (float64 oracle)",
+        "what": f"velocity of the {w.name} denoising step{' with FP8 blocks' if a.fp8 else ''}, "
+                "sampled elements (float64 oracle)",
         "workload": w.name, "config_id": cid,
         "output_shape": list(out.shape), "per_sample_shape": list(per),
         "index_order": "flat index into one sample's [C, F, H8, W8] velocity (row-major)",
-        "writer": "python -m tests.golden.make_full_step_golden --config %d" % cid,
+        "writer": "python -m tests.golden.make_full_step_golden --config %d%s" % (cid, " --fp8" if a.fp8 else ""),
         "oracle_seconds": round(time.perf_counter() - t0, 1),
         "samples": samples,
     }
-    with open(golden_path(cid), "w") as f:
+    with open(golden_path(cid, a.fp8), "w") as f:
         json.dump(rec, f)
-    print(f"[golden C{cid}] wrote {golden_path(cid)} after {time.perf_counter() - t0:.0f}s", flush=True)
+    print(f"[golden C{cid}] wrote {golden_path(cid, a.fp8)} after {time.perf_counter() - t0:.0f}s", flush=True)
     return 0
 
 
