@@ -414,7 +414,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmDesc g) {
 // loads of tile kt+2 start, the 8 MFMAs of tile kt run from registers, one
 // barrier, then the fragments of tile kt+1 are read into the same registers
 // while those MFMAs execute.  The epilogues (LDS-staged, as for bf16
-// operands) scale by the row scale times the column scale.
+// operands) scale by the row scale times the column scale.  This kernel takes the
+// shapes whose K is not a multiple of 256; k_gemm_fp8w below the rest.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 template <int KIND, bool BROWS>
@@ -578,6 +579,170 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(GemmDesc g) {
     epilogue_f32<KIND, true>(g, acc, sEp, w, lane, m0, n0, wm, wn);
   } else {
     epilogue<KIND, BROWS, true>(g, acc, sEp, w, lane, m0, n0, wm, wn);
+  }
+}
+
+// FP8 operands with K a multiple of 256 (every Linear layer of the models:
+// K = 1536, 5120, 8960, 13824): the same output tile, wavefronts and MFMA,
+// with 128-deep K tiles -- the bf16 kernel's 128-byte rows, swizzle and
+// direct loads -- so one barrier and one load wait cover 16 MFMAs per
+// wavefront instead of 8.  A tile is two k-substeps of 64.  The fragments sit
+// in one set of registers that is refilled as it frees up (see `sub`), so
+// each LDS read runs three or more MFMAs ahead of its use and two stages of
+// 64 KB fit beside it.  The accumulation order over K is the 64-deep kernel's,
+// so the two give bitwise equal outputs.
+template <int KIND, bool BROWS>
+__global__ __launch_bounds__(512, 1) void k_gemm_fp8w(GemmDesc g) {
+  constexpr int GBK8 = 128;                   // K tile, bytes = elements: 128-byte rows, as the bf16 kernel's
+  constexpr int CH = GBK8 / 16;               // 16-byte chunks per tile row (8)
+  constexpr int RPB = 1024 / GBK8;            // rows per 1-KB direct-load block (8)
+  constexpr int BPW = GBM / RPB / GW;         // blocks per wavefront per operand tile (4)
+  constexpr int LPT = 2 * BPW;                // direct loads per wavefront per K tile
+  constexpr int SB = (GBM + GBN) * GBK8;      // bytes per stage: A rows, then B rows
+  // one LDS variable per stage (the compiler gives each its own alias scope,
+  // so reads of one stage need not wait for direct loads landing in the other)
+  __shared__ __attribute__((aligned(16))) uint8_t s0[SB];
+  __shared__ __attribute__((aligned(16))) uint8_t s1[SB];
+  auto stage = [&](auto ST) -> uint8_t * {
+    if constexpr (decltype(ST)::value == 0) return s0;
+    else return s1;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using TA = std::true_type;
+  using FA = std::false_type;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 2, wn = w & 3;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int tiles_m = (g.M + GBM - 1) / GBM;
+  const int tiles_n = (g.N + GBN - 1) / GBN;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int group = GROUP_M * tiles_n;
+  const int first_m = (bid / group) * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (bid % group) % gm;
+  const int tn = (bid % group) / gm;
+  const int m0 = tm * GBM, n0 = tn * GBN;
+
+  // global -> LDS as in the bf16 kernel: lane i of a 1-KB block lands at row
+  // blk*RPB + i/CH, physical chunk i%CH, and fetches logical chunk (i%CH) ^ swz(row)
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)g.A, 0, (int)((unsigned)g.M * (unsigned)g.lda), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)g.B, 0, (int)((unsigned)g.N * (unsigned)g.ldb), 0x00020000);
+  int oa[BPW], ob[BPW];
+#pragma unroll
+  for (int r = 0; r < BPW; ++r) {
+    const int row = (w * BPW + r) * RPB + lane / CH;
+    const int c = (lane % CH) ^ swz_row<CH>(row);
+    oa[r] = (int)((unsigned)min(m0 + row, g.M - 1) * (unsigned)g.lda + c * 16);
+    ob[r] = (int)((unsigned)min(n0 + row, g.N - 1) * (unsigned)g.ldb + c * 16);
+  }
+  auto gload = [&](int kt, auto st) {
+    const int k0b = kt * GBK8;
+    uint8_t *da = stage(st) + w * BPW * 1024;
+    uint8_t *db = stage(st) + GBM * GBK8 + w * BPW * 1024;
+#pragma unroll
+    for (int r = 0; r < BPW; ++r) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(da + r * 1024), 16, oa[r], k0b, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(db + r * 1024), 16, ob[r], k0b, 0, 0);
+    }
+  };
+  // k-substep ks (64 bytes of K): a lane's fragment is 32 bytes, logical
+  // chunks 4 ks + 2 half + {0, 1} of its row; the swizzle depends only on l32
+  int aoff[2][2], boff[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = ((4 * ks + 2 * half + j) ^ swz_row<CH>(l32)) * 16;
+      aoff[ks][j] = (wm * 128 + l32) * GBK8 + c;
+      boff[ks][j] = GBM * GBK8 + (wn * 64 + l32) * GBK8 + c;
+    }
+
+  // accumulators in AGPRs (an AGPR operand makes the compiler split the 256
+  // registers 128 / 128); fragments and addresses use the VGPRs
+  asm volatile("; accumulators in AGPRs" :: "a"(0.0f));
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // one set of fragment registers, refilled as they free up: the MFMAs of a
+  // substep run in one of two orders, and after each MFMA that was the last
+  // user of a fragment, that fragment of the next substep is read into it.
+  // Order A: (0,0) (1,0) (2,0) (3,0) (3,1) (2,1) (1,1) (0,1); order B: (3,0)
+  // (2,0) (1,0) (0,0) (0,1) (1,1) (2,1) (3,1) (A fragment, B fragment).  Each
+  // order consumes the fragments in the order the other one frees them, so
+  // every read runs at least three MFMAs ahead of its use.
+  i32x8 fa[4], fb[2];
+  auto frag = [&](const uint8_t *p, const int (&off)[2]) -> i32x8 {
+    const uint4 lo = *reinterpret_cast<const uint4 *>(p + off[0]);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(p + off[1]);
+    i32x8 v;
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    return v;
+  };
+  auto sub = [&](auto ORDER_A, auto READS, const uint8_t *rs, auto RKS) __attribute__((always_inline)) {
+    constexpr int rks = decltype(RKS)::value;
+    constexpr bool oa_ = decltype(ORDER_A)::value, rd = decltype(READS)::value;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int j = n >> 2;
+      const int i = oa_ ? (j ? 7 - n : n) : (j ? n - 4 : 3 - n);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0,
+                                                                  0x7F7F7F7F, 0, 0x7F7F7F7F);
+      if constexpr (rd) {
+        if (n == 3) fb[0] = frag(rs, boff[rks]);
+        if (n >= 4) fa[i] = frag(rs + i * 32 * GBK8, aoff[rks]);
+        if (n == 7) fb[1] = frag(rs + 32 * GBK8, boff[rks]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int KT = g.K / GBK8;                  // even (K % 256 == 0, checked on the host)
+  gload(0, I0{});
+  gload(1, I1{});
+  wait_vm<LPT>();
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = frag(s0 + i * 32 * GBK8, aoff[0]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fb[j] = frag(s0 + j * 32 * GBK8, boff[0]);
+
+  // tile kt in stage ST: substep 0 (reading substep 1 of this stage); wait
+  // for tile kt+1's loads and every read of this stage; one barrier; tile
+  // kt+2 starts loading into this stage; substep 1 (reading substep 0 of
+  // tile kt+1 -- after the last tile, a harmless read of a settled stage)
+  auto tile = [&](int kt, auto ST) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value;
+    sub(TA{}, TA{}, stage(ST), I1{});
+    wait_vm<0>();
+    __syncthreads();
+    if (kt + 2 < KT) gload(kt + 2, ST);
+    sub(FA{}, TA{}, stage(std::integral_constant<int, st ^ 1>{}), I0{});
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    tile(kt, I0{});
+    tile(kt + 1, I1{});
+  }
+
+  // the epilogue stages each wavefront's slab (32 x 68 floats) in the stage
+  // buffers: wavefronts 0-3 in s0, 4-7 in s1
+  __syncthreads();
+  if constexpr (epi_f32<KIND>()) {
+    static_assert(!BROWS, "bias along rows: bf16 outputs only");
+    if (w < 4) epilogue_f32<KIND, true>(g, acc, reinterpret_cast<float *>(s0), w, lane, m0, n0, wm, wn);
+    else epilogue_f32<KIND, true>(g, acc, reinterpret_cast<float *>(s1), w - 4, lane, m0, n0, wm, wn);
+  } else {
+    if (w < 4) epilogue<KIND, BROWS, true>(g, acc, reinterpret_cast<float *>(s0), w, lane, m0, n0, wm, wn);
+    else epilogue<KIND, BROWS, true>(g, acc, reinterpret_cast<float *>(s1), w - 4, lane, m0, n0, wm, wn);
   }
 }
 
@@ -746,6 +911,21 @@ hipError_t launch_gemm_one(const GemmDesc &g, hipStream_t s) {
     if (g.b_per_col && !g.bias_rows) return hipErrorInvalidValue;   // per-column scales: token columns only
     if ((long)g.M * g.lda >= (1L << 31) || (long)g.N * g.ldb >= (1L << 31)) return hipErrorInvalidValue;
     const int blocks = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
+    if (g.K % 256 == 0) {   // an even count of 128-deep K tiles
+      if (g.bias_rows) {
+        if (g.kind != OUT_BF16) return hipErrorInvalidValue;
+        k_gemm_fp8w<OUT_BF16, true><<<blocks, GW * 64, 0, s>>>(g);
+        return hipGetLastError();
+      }
+      switch (g.kind) {
+        case OUT_BF16: k_gemm_fp8w<OUT_BF16, false><<<blocks, GW * 64, 0, s>>>(g); break;
+        case OUT_F32: k_gemm_fp8w<OUT_F32, false><<<blocks, GW * 64, 0, s>>>(g); break;
+        case OUT_GELU: k_gemm_fp8w<OUT_GELU, false><<<blocks, GW * 64, 0, s>>>(g); break;
+        case OUT_RESID: k_gemm_fp8w<OUT_RESID, false><<<blocks, GW * 64, 0, s>>>(g); break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
     if (g.bias_rows) {
       if (g.kind != OUT_BF16) return hipErrorInvalidValue;
       k_gemm_fp8<OUT_BF16, true><<<blocks, GW * 64, 0, s>>>(g);
