@@ -110,6 +110,24 @@ class ClockSampler:
         return sum(self.samples) / len(self.samples) if self.samples else None
 
 
+def clock_fields(clock, achieved_tf):
+    """The sampled shader clock and the MFMA peak at that clock.  The driver's
+    level is only a sample of the running clock: a rate above the peak at the
+    sampled clock shows that the samples missed it (seen under a profiler),
+    and then no fraction is given."""
+    mhz = clock.mhz()
+    out = {"sclk_mhz": None if mhz is None else round(mhz, 1), "sclk_samples": len(clock.samples),
+           "peak_at_sclk": None, "frac_at_sclk": None}
+    if mhz is not None:
+        peak = PEAK_BF16_TFLOPS * mhz / PEAK_SCLK_MHZ
+        out["peak_at_sclk"] = round(peak, 1)
+        if achieved_tf <= peak:
+            out["frac_at_sclk"] = round(achieved_tf / peak, 4)
+        else:
+            out["sclk_note"] = "the sampled level is below the clock the measured rate needs"
+    return out
+
+
 def block_flops(B, L, d, H, F, Lc, Li=0):
     hd = d // H
     M = B * L
@@ -745,12 +763,7 @@ def main():
                      "standalone_tflops": round(attn_solo_tf, 1),
                      "flop_per_launch": sa_f,
                      # the same against the peak at the shader clock sampled during the timed steps
-                     "sclk_mhz": None if clock.mhz() is None else round(clock.mhz(), 1),
-                     "sclk_samples": len(clock.samples),
-                     "peak_at_sclk": None if clock.mhz() is None
-                     else round(PEAK_BF16_TFLOPS * clock.mhz() / PEAK_SCLK_MHZ, 1),
-                     "frac_at_sclk": None if clock.mhz() is None
-                     else round(attn_tf / (PEAK_BF16_TFLOPS * clock.mhz() / PEAK_SCLK_MHZ), 4)},
+                     **clock_fields(clock, attn_tf)},
         "wall_s_timed": round(t_wall, 3),
     }
     if m.dtype == "bf16":   # the same block with its six Linear layers in FP8 (E4M3), same inputs

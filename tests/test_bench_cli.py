@@ -34,3 +34,20 @@ def test_clock_sampler_reads_the_current_level(tmp_path):
     c = bench.ClockSampler()
     c.path, c.samples = None, [2000.0, 2100.0]
     assert c.mhz() == 2050.0
+
+
+def test_clock_fields_drop_an_impossible_fraction():
+    """A rate above the peak at the sampled clock means the samples missed the
+    running clock: the peak at that clock is still reported, the fraction is not."""
+    sys.path.insert(0, ROOT)
+    import bench
+    c = bench.ClockSampler()
+    c.path, c.samples = None, [1728.0]
+    f = bench.clock_fields(c, 1312.0)
+    assert f["peak_at_sclk"] == 1800.0 and f["frac_at_sclk"] == round(1312.0 / 1800.0, 4)
+    c.samples = [1024.0]
+    f = bench.clock_fields(c, 1312.0)
+    assert f["peak_at_sclk"] == round(2500.0 * 1024 / 2400, 1) and f["frac_at_sclk"] is None
+    assert "sclk_note" in f
+    c.samples = []
+    assert bench.clock_fields(c, 1312.0)["sclk_mhz"] is None
