@@ -11,7 +11,7 @@ Inputs are resident in HBM before timing starts; the block updates the
 residual stream in place, so successive timed steps chain blocks.
 
 Prints one JSON line (tokens/s of the block, attention roofline, CPU oracle
-baseline on a bounded sample).  ``--gpus`` above 1 is refused: this build
+baseline on a bounded sample).  ``--gpus`` above 1 is refused: the library
 runs on one GPU.
 """
 from __future__ import annotations
@@ -618,7 +618,7 @@ def main():
         args.no_cpu_baseline = True
         args.warmup, args.steps = 1, 1
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
