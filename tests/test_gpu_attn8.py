@@ -10,7 +10,12 @@ oracle from exact attention.  The bar: mean |kernel - oracle| at most 1.25x
 mean |oracle - exact|, and max |kernel - oracle| at most the larger of 3e-2
 and max |oracle - exact|.  (A CPU replay of the kernel's algorithm gives
 ratios 0.19 - 0.81 for the mean and 0.37 - 0.77 for the max on these
-inputs.)"""
+inputs.)  Beside it, a fixed bar that does not lean on the oracle: the
+kernel's mean relative error against exact attention (float64) at most 8e-2.
+E4M3 keeps 3 mantissa bits, and on these inputs the oracle's own 8-bit
+rounding gives 1.8e-2 - 3.9e-2 (computed on the CPU); the bar is twice the
+largest of those, where an attention that drops the softmax (mean of V)
+lands at 0.5 or more."""
 import numpy as np
 import pytest
 
@@ -21,6 +26,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 C_LOG2 = np.log2(np.e) / np.sqrt(128.0)
+ATTN8_MEAN_REL = 8e-2    # fixed bar against exact attention (module docstring)
 
 
 def _rup(v, a):
@@ -70,6 +76,8 @@ def _assert_attn8(g, o8, ex, what):
           f"|oracle - exact| max {eq.max():.4f} mean {eq.mean():.5f}", flush=True)
     assert ek.max() <= bar_max, f"{what}: max {ek.max():.4f} > {bar_max:.4f}"
     assert ek.mean() <= 1.25 * eq.mean(), f"{what}: mean {ek.mean():.5f} > 1.25 x {eq.mean():.5f}"
+    rel = float(np.abs(g - ex).sum() / max(float(np.abs(ex).sum()), 1e-30))
+    assert rel <= ATTN8_MEAN_REL, f"{what}: mean-rel against exact {rel:.4f} > {ATTN8_MEAN_REL}"
 
 
 QUANT_CASES = [  # B, H, Lq, Lk

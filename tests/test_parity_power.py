@@ -55,3 +55,20 @@ def test_cross_inputs_reject_mean_of_v_and_unscaled_softmax():
         assert m["max_abs"] > 3e-2 and m["mean_rel"] > 1e-2, m
         m = metrics(O.multihead(q * np.sqrt(128.0), k, v, H), ref)
         assert m["max_abs"] > 3e-2 and m["mean_rel"] > 1e-2, m
+
+
+def test_attn8_fixed_bar_rejects_mean_of_v_and_passes_the_oracle():
+    """The 8-bit attention tests' fixed bar (mean relative error against exact
+    attention): the oracle's own 8-bit attention passes it on every parity
+    input, and the plain mean of V fails it on each of them."""
+    from tests.test_gpu_attn8 import ATTN8_MEAN_REL, CASES
+    for qk_std in (1.0, 2.0):
+        for B, H, Lq, Lk in CASES:
+            if Lk == 1:   # one key: every attention is V itself
+                continue
+            q, k, v = synth.attention_inputs(12, B, H, Lq, Lk, qk_std=qk_std)
+            ex = np.stack([O.multihead(q[b], k[b], v[b], H) for b in range(B)])
+            o8 = np.stack([O.multihead_8bit(q[b], k[b], v[b], H) for b in range(B)])
+            assert metrics(o8, ex)["mean_rel"] <= ATTN8_MEAN_REL / 2, (B, H, Lq, Lk, qk_std)
+            mean_v = np.broadcast_to(v.astype(np.float64).mean(axis=1, keepdims=True), ex.shape)
+            assert metrics(mean_v, ex)["mean_rel"] > 5 * ATTN8_MEAN_REL, (B, H, Lq, Lk, qk_std)
