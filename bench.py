@@ -323,7 +323,7 @@ def sampler_bench(n_steps: int, warmup: int):
 
     import synth
     import video_diffusion_transformer_block_amd as W
-    work = synth.CONFIGS[3]
+    work = synth.WORKLOADS["wan1.3b-step-480p-cfg2"]
     m = work.model
     B, L = work.batch, work.L
     cfg = W.make_cfg(dim=m.dim, heads=m.heads, ffn=m.ffn, n_blocks=m.n_blocks, in_ch=m.in_ch,
@@ -470,7 +470,7 @@ def fp8_block_bench(steps: int, warmup: int):
 
     import synth
     import video_diffusion_transformer_block_amd as W
-    work = synth.CONFIGS[2]
+    work = synth.WORKLOADS["wan1.3b-block-480p"]
     m = work.model
     B, L, d = work.batch, work.L, m.dim
     cfg = W.make_cfg(dim=d, heads=m.heads, ffn=m.ffn, n_blocks=1, text_len=m.text_len, eps=m.eps,
@@ -601,7 +601,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--config", type=int, default=2, help="block workload id (2: 1.3B, 4: 14B)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="block workload id (2: wan1.3b-block-480p, 4: wan14b-block-720p)")
     ap.add_argument("--sampler", type=int, default=0, metavar="STEPS",
                     help="time STEPS sampler steps of the 1.3B guidance pair with and without the "
                          "cross-attention K/V cache (prints its own JSON line) instead of the block")
@@ -638,7 +639,7 @@ def main():
     import synth
     import video_diffusion_transformer_block_amd as W
 
-    work = synth.CONFIGS[args.config]
+    work = synth.by_id(args.config)
     assert work.kind == "block"
     m = work.model
     B, L, d, H, F = work.batch, work.L, m.dim, m.heads, m.ffn
@@ -779,7 +780,7 @@ def main():
     out["gemm"] = block_gemm_leg(W, B, L, d, F, stream)
     out["ln_modulate"] = ln_leg(W, B, L, d, stream)
     if args.config == 2:
-        out["c3_step"] = step_leg(W, synth.CONFIGS[3])
+        out["c3_step"] = step_leg(W, synth.WORKLOADS["wan1.3b-step-480p-cfg2"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work, inp, tw, bw)
     print(json.dumps(out), flush=True)

@@ -33,7 +33,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "ModelCfg", "Workload", "CONFIGS", "bf16_round", "to_bf16_bits",
+    "ModelCfg", "Workload", "WORKLOADS", "by_id", "bf16_round", "to_bf16_bits",
     "from_bf16_bits", "draw", "block_weights", "model_weights", "tmlp_weights",
     "workload_inputs", "mini",
 ]
@@ -63,7 +63,7 @@ class ModelCfg:
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
-    cid: int                  # configuration id (1..5), part of every seed
+    cid: int                  # workload id, part of every seed
     name: str
     model: ModelCfg
     batch: int
@@ -88,20 +88,30 @@ class Workload:
 _M13 = dict(dim=1536, heads=12, ffn=8960)
 _M14 = dict(dim=5120, heads=40, ffn=13824)
 
-CONFIGS: Dict[int, Workload] = {
-    1: Workload(1, "tiny-block-f32",
-                ModelCfg(dim=128, heads=2, ffn=512, n_blocks=1, text_len=32, dtype="f32"),
-                batch=1, lat_f=2, lat_h=16, lat_w=16, kind="block"),
-    2: Workload(2, "wan1.3b-block-480p",
-                ModelCfg(n_blocks=1, **_M13), batch=1, lat_f=21, lat_h=60, lat_w=104, kind="block"),
-    3: Workload(3, "wan1.3b-step-480p-cfg2",
-                ModelCfg(n_blocks=30, **_M13), batch=2, lat_f=21, lat_h=60, lat_w=104, kind="step"),
-    4: Workload(4, "wan14b-block-720p",
-                ModelCfg(n_blocks=1, **_M14), batch=1, lat_f=21, lat_h=90, lat_w=160, kind="block"),
-    5: Workload(5, "wan14b-i2v-step-480p",
-                ModelCfg(n_blocks=40, in_ch=36, img_len=257, **_M14),
-                batch=1, lat_f=21, lat_h=60, lat_w=104, kind="step"),
-}
+# The full-size workloads, by name.  A workload's integer id seeds its
+# inputs and weights (synth draws every array from it), so it stays fixed.
+WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
+    Workload(1, "tiny-block-f32",
+             ModelCfg(dim=128, heads=2, ffn=512, n_blocks=1, text_len=32, dtype="f32"),
+             batch=1, lat_f=2, lat_h=16, lat_w=16, kind="block"),
+    Workload(2, "wan1.3b-block-480p",
+             ModelCfg(n_blocks=1, **_M13), batch=1, lat_f=21, lat_h=60, lat_w=104, kind="block"),
+    Workload(3, "wan1.3b-step-480p-cfg2",
+             ModelCfg(n_blocks=30, **_M13), batch=2, lat_f=21, lat_h=60, lat_w=104, kind="step"),
+    Workload(4, "wan14b-block-720p",
+             ModelCfg(n_blocks=1, **_M14), batch=1, lat_f=21, lat_h=90, lat_w=160, kind="block"),
+    Workload(5, "wan14b-i2v-step-480p",
+             ModelCfg(n_blocks=40, in_ch=36, img_len=257, **_M14),
+             batch=1, lat_f=21, lat_h=60, lat_w=104, kind="step"),
+)}
+
+
+def by_id(cid: int) -> Workload:
+    """The full-size workload with integer id cid."""
+    for w in WORKLOADS.values():
+        if w.cid == cid:
+            return w
+    raise KeyError(cid)
 
 
 def mini(cid: int, name: str, *, dim: int, heads: int, ffn: int, n_blocks: int,

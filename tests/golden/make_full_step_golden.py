@@ -46,7 +46,7 @@ N_SAMPLED = 4096          # output elements stored per batch sample
 # minutes, so the step can also be compared in float32
 SHORT_I2V = synth.mini(53, "wan14b-i2v-step-short", dim=5120, heads=40, ffn=13824, n_blocks=40,
                        lat_f=21, lat_h=8, lat_w=8, batch=1, text_len=512, in_ch=36, img_len=257)
-WORKLOADS = {3: synth.CONFIGS[3], 5: synth.CONFIGS[5], 53: SHORT_I2V}
+WORKLOADS = {3: synth.by_id(3), 5: synth.by_id(5), 53: SHORT_I2V}
 
 
 def golden_path(cid: int, fp8: bool = False) -> str:

@@ -93,7 +93,7 @@ def test_attn8_block_full_size_sampled_rows():
     self-attention: the whole block on the GPU, sampled token rows in the
     oracle (self-attention reads every key, so the oracle still projects all
     tokens)."""
-    work = synth.CONFIGS[2]
+    work = synth.WORKLOADS["wan1.3b-block-480p"]
     L = work.L
     rng = np.random.default_rng(3)
     rows = np.unique(np.concatenate([[0, 1, 255, 256, L - 1, L - 2], rng.integers(0, L, 18)]))

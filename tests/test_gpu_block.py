@@ -22,7 +22,7 @@ MINI_BLOCKS = {
                                 lat_f=1, lat_h=10, lat_w=10, batch=3, text_len=40, kind="block"),
     "bf16-b5-tiny": synth.mini(14, "bf16-b5-tiny", dim=256, heads=2, ffn=512, n_blocks=1,
                                lat_f=1, lat_h=4, lat_w=6, batch=5, text_len=24, kind="block"),
-    "f32-tiny": synth.CONFIGS[1],
+    "f32-tiny": synth.WORKLOADS["tiny-block-f32"],
 }
 
 
@@ -78,8 +78,8 @@ def test_block_mini(name):
 # image-to-video model at 480P (d = 5120, 40 heads, 257 image tokens beside the
 # 512 text tokens: [Note] I2V 架构扩展, decoupled cross-attention)
 FULL_BLOCKS = {
-    2: synth.CONFIGS[2],
-    4: synth.CONFIGS[4],
+    2: synth.WORKLOADS["wan1.3b-block-480p"],
+    4: synth.WORKLOADS["wan14b-block-720p"],
     "i2v14b": synth.mini(51, "wan14b-i2v-block-480p", dim=5120, heads=40, ffn=13824, n_blocks=1,
                          lat_f=21, lat_h=60, lat_w=104, batch=1, text_len=512, img_len=257,
                          kind="block"),
@@ -128,7 +128,7 @@ def test_block_branches_full_size(branch):
     as the softmax flattens over more keys)."""
     import video_diffusion_transformer_block_amd as W
     from tests.gpu_util import assert_parity, cfg_of, up, up_block, workspace
-    work = synth.CONFIGS[2]
+    work = synth.WORKLOADS["wan1.3b-block-480p"]
     m = work.model
     d, L = m.dim, work.L
     rows = np.unique(np.concatenate([[0, 255, 256, L - 1],

@@ -265,7 +265,7 @@ def test_block_fp8_mini(name):
 def test_block_fp8_full_size_sampled_rows():
     """The 1.3B block at 480P (L = 32760) in FP8: the whole block on the GPU,
     sampled token rows in the oracle."""
-    work = synth.CONFIGS[2]
+    work = synth.WORKLOADS["wan1.3b-block-480p"]
     L = work.L
     rng = np.random.default_rng(2)
     rows = np.unique(np.concatenate([[0, 1, 255, 256, L - 1, L - 2], rng.integers(0, L, 26)]))

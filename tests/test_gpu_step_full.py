@@ -46,7 +46,7 @@ def _inputs(work, B):
 
 
 def test_c3_step_batch_independence_and_determinism():
-    work = synth.CONFIGS[3]
+    work = synth.WORKLOADS["wan1.3b-step-480p-cfg2"]
     print(f"C3 step: B=2, L={work.L}, {work.model.n_blocks} blocks", flush=True)
     mw = synth.device_model_weights(work)
     lat, t, ctx, _ = _inputs(work, 2)
@@ -65,7 +65,7 @@ def test_c3_cached_step_equals_plain_step_bitwise():
     from the cache equals the plain step bit for bit."""
     import video_diffusion_transformer_block_amd as W
     from tests.gpu_util import cfg_of
-    work = synth.CONFIGS[3]
+    work = synth.WORKLOADS["wan1.3b-step-480p-cfg2"]
     print(f"C3 cached step: B=2, L={work.L}, {work.model.n_blocks} blocks", flush=True)
     cfg = cfg_of(work)
     mw = synth.device_model_weights(work)
@@ -83,7 +83,7 @@ def test_c3_cached_step_equals_plain_step_bitwise():
 
 
 def test_c5_step_zero_projection_and_identity():
-    work = synth.CONFIGS[5]
+    work = synth.WORKLOADS["wan14b-i2v-step-480p"]
     m = work.model
     print(f"C5 I2V step: L={work.L}, {m.n_blocks} blocks, {m.in_ch} channels", flush=True)
     mw = synth.device_model_weights(work)

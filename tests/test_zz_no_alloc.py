@@ -62,7 +62,7 @@ def test_noalloc_block_equals_workspace_block_twice():
 
 def test_noalloc_block_rejects_sizes_beyond_scratch():
     import video_diffusion_transformer_block_amd as W
-    work = synth.CONFIGS[2]      # the full 480P latent needs ~1.1 GiB of temporaries
+    work = synth.WORKLOADS["wan1.3b-block-480p"]   # the full latent needs ~1.1 GiB of temporaries
     cfg = W.make_cfg(dim=1536, heads=12, ffn=8960)
     assert W.dit_block_noalloc_bytes(cfg, 1, work.lat_f, work.Hp, work.Wp) > W.NOALLOC_SCRATCH_BYTES
     x = torch.zeros(1, dtype=torch.float32, device="cuda")
