@@ -147,12 +147,24 @@ def test_short_i2v_step_float32():
 def test_full_step_fp8_against_oracle_samples():
     """The 30-block 1.3B guidance pair with every block's Linear layers in FP8
     (wan_quantize_model_fp8, wan_dit_step_fp8_fwd; [Note] Infra / 推理优化: FP8
-    GEMM) against the oracle's FP8 step on the stored elements: the usual bar,
-    and decisively nearer the FP8 oracle than the exact step -- within 0.75 of
-    the distance between the two on the same elements (the exact values are
-    the bf16 golden's: the same seeded indices)."""
+    GEMM) against the oracle's FP8 step on the stored elements (reading R28).
+
+    An E4M3 code is an integer decided from a bf16 activation; where two
+    correct implementations differ in a bf16 activation's last place, codes
+    move by a whole E4M3 step (6 - 12 %), and over 30 full-width blocks those
+    flips compound.  Two FP8 runs of the oracle itself at this width (d = 1536,
+    FFN 8960, a short clip), one with bf16-level noise added after every block,
+    drift apart by 0.67x the FP8 effect after one block and 0.84 - 0.87x from
+    10 to 30 blocks, while each keeps an FP8 effect (distance from the exact
+    step) of the same size (tests/golden/fp8_drift.py, on the CPU).  So the bar, on the stored elements, is:
+    the GPU's FP8 step no farther from the oracle's FP8 step than the exact
+    step is (1.0x the FP8 effect); the GPU's own FP8 effect (its distance from
+    the exact step, the bf16 golden's values at the same seeded indices)
+    between 0.8x and 1.25x the oracle's -- an FP8 switch that does nothing
+    lands near 0.05x (bf16 noise), a wrong scale far above; and the mean
+    magnitude within 1 % of the oracle's."""
     import video_diffusion_transformer_block_amd as W
-    from tests.gpu_util import assert_parity, cfg_of, metrics, up
+    from tests.gpu_util import cfg_of, metrics, up
     cid = 3
     work = WORKLOADS[cid]
     m = work.model
@@ -176,7 +188,10 @@ def test_full_step_fp8_against_oracle_samples():
         idx = np.asarray(s8["flat_index"])
         g = g_all[b].reshape(-1)[idx]
         o8, oe = np.asarray(s8["value"]), np.asarray(se["value"])
-        dev, eff = metrics(g, o8), metrics(oe, o8)
-        print(f"  fp8 sample {b}: {dev}; fp8 effect {eff}", flush=True)
-        assert_parity(g, o8, 3e-2, 1e-2, f"{work.name} FP8 sample {b}")
-        assert dev["mean_rel"] <= 0.75 * eff["mean_rel"], (dev, eff)
+        dev, eff, own = metrics(g, o8), metrics(oe, o8), metrics(g, oe)
+        print(f"  fp8 sample {b}: GPU vs FP8 oracle {dev}; FP8 effect {eff}; GPU vs exact {own}; "
+              f"ratios {dev['mean_rel'] / eff['mean_rel']:.2f}, {own['mean_rel'] / eff['mean_rel']:.2f}",
+              flush=True)
+        assert dev["mean_rel"] <= 1.0 * eff["mean_rel"], (dev, eff)
+        assert 0.8 * eff["mean_rel"] <= own["mean_rel"] <= 1.25 * eff["mean_rel"], (own, eff)
+        assert abs(np.abs(g_all[b]).mean() / s8["abs_mean_all"] - 1) < 1e-2
